@@ -1,0 +1,54 @@
+"""Each mutant is a copy of oracle.c with one plausible mistake planted (a
+dropped term, a wrong sign, index or operand, a rounding slip). Each is
+built on the CPU and run through the pins; every mutant must fail at least
+one pin, which shows the pins can see that kind of mistake. Mutants are
+chosen so that none of them can index outside its buffers."""
+import os
+
+import pytest
+
+import oracle
+from oracle_pins import PINS
+
+MUTANTS = {
+    "eps_dropped": ("1.0 / sqrt(ms + eps)", "1.0 / sqrt(ms)"),
+    "eps_outside_sqrt": ("1.0 / sqrt(ms + eps)", "1.0 / sqrt(ms) + eps"),
+    "sum_not_mean": ("double ms = sum_sq / (double)d;", "double ms = sum_sq;"),
+    "weight_dropped": ("* r * load(w, j, dtype);", "* r;"),
+    "weight_reversed": ("* r * load(w, j, dtype);", "* r * load(w, d - 1 - j, dtype);"),
+    "residual_not_stored": ("            store(x, r * x_stride + j, s, dtype);\n", ""),
+    "rope_sign": ("out[i] = x1 * c - x2 * s;", "out[i] = x1 * c + x2 * s;"),
+    "rope_sin_cos_swapped": ("double c = cos(a), s = sin(a);", "double c = sin(a), s = cos(a);"),
+    "rope_adjacent_pairs": ("double x2 = load(x, x_off + i + half, dtype);",
+                            "double x2 = load(x, x_off + (i ^ 1), dtype);"),
+    "rope_frequency_exponent": ("pow(base, -2.0 * (double)i / (double)d)",
+                                "pow(base, -1.0 * (double)i / (double)d)"),
+    "rope_k_head_stride": ("rope_head(k, t * k_ts + h * k_hs,", "rope_head(k, t * k_ts + 0 * k_hs,"),
+    "kv_halves_swapped": ("(((0 * num_blocks + block)", "(((1 * num_blocks + block)"),
+    "skip_zero_slot": ("if (slot < 0 || slot >= n_slots) continue;",
+                       "if (slot <= 0 || slot >= n_slots) continue;"),
+    "silu_exp_sign": ("1.0 / (1.0 + exp(-g))", "1.0 / (1.0 + exp(g))"),
+    "swiglu_up_dropped": ("out[r * out_stride + c] = g * sigmoid * u;",
+                          "out[r * out_stride + c] = g * sigmoid;"),
+    "bf16_double_rounding": ("double n = rint(a / q);", "double n = rint((double)(float)a / q);"),
+    "bf16_truncation": ("double n = rint(a / q);", "double n = floor(a / q);"),
+    "gqa_modulo": ("return h / (hq / hkv);", "return h % hkv;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    src = open(oracle.SRC).read()
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    path = tmp_path / "mutant.c"
+    path.write_text(src.replace(old, new))
+    so = oracle.build(str(path), str(tmp_path / f"lib{name}.so"))
+    L = oracle.lib(so)
+    failed = []
+    for pin, fn in PINS.items():
+        try:
+            fn(L)
+        except AssertionError:
+            failed.append(pin)
+    assert failed, f"mutant {name} passed every pin"
