@@ -1,0 +1,378 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused per-token decode ops on one MI355X.
+
+Workload (one "step"): the batched decode chain of a Qwen2.5-1.5B-shaped
+model -- 28 layers x [add_rmsnorm, rope_kvstore, add_rmsnorm, swiglu] at
+batch 256, every sequence with 4096 tokens already cached and decoding
+position 4096, random block tables, bf16, hidden 1536, intermediate 8960,
+12 query / 2 KV heads of 128. Inputs are seeded synthetic data, resident in
+HBM before timing starts. The timed step is a captured HIP graph replay.
+
+Prints ONE JSON line:
+  value        algorithmic bytes of a step / step time (GB/s), whole job
+  ms_per_step  decode-step fused-op latency (graph replay)
+  roofline     dominant kernel (swiglu at the chain's shape): algorithmic
+               bytes per launch / its mean duration, measured with events
+               stamped at kernel start and end (hipExtLaunchKernel)
+  cpu_baseline the CPU fp64 oracle on a bounded sample of the same workload
+  kernels      each kernel at its large shape on cold, rotated buffers
+  ceiling      1 GiB device copies: the library's copy kernel and hipMemcpy
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "achieved HBM GB/s (% of peak) per kernel; decode-step fused-op latency"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def events(n):
+    """n timing events, each recorded once so that it exists."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in evs:
+        e.record()
+    return evs
+
+
+def timed_launch(kcr, fn, ev0, ev1):
+    """Run fn (one kcr op) with the kernel's own start/end stamped on ev0/ev1."""
+    kcr.time_next_launch(ev0, ev1)
+    fn()
+
+
+def kernel_stats(ms):
+    ms = sorted(ms)
+    return dict(n=len(ms), median_us=1e3 * statistics.median(ms), min_us=1e3 * ms[0],
+                mean_us=1e3 * statistics.fmean(ms),
+                p20_us=1e3 * ms[int(0.2 * (len(ms) - 1))], p80_us=1e3 * ms[int(0.8 * (len(ms) - 1))])
+
+
+# ------------------------------------------------------------------ chain
+def chain_ops(kcr, chain, L):
+    return [
+        ("add_rmsnorm", lambda: kcr.add_rmsnorm(chain.h, L["d_attn"], L["w_attn"], chain.eps, out=L["y_attn"])),
+        ("rope_kvstore", lambda: kcr.rope_kvstore(L["q"], L["k"], L["v"], chain.positions, chain.cos,
+                                                  chain.sin, L["cache"], chain.slot_mapping, q_out=L["q_out"])),
+        ("add_rmsnorm", lambda: kcr.add_rmsnorm(chain.h, L["d_mlp"], L["w_mlp"], chain.eps, out=L["y_mlp"])),
+        ("swiglu", lambda: kcr.swiglu(L["gate"], L["up"], out=L["act"])),
+    ]
+
+
+def instrumented_steps(kcr, chain, n_steps):
+    """Eager steps with every launch's kernel duration stamped; returns
+    {op: [ms, ...]} and the per-step kernel-time sums."""
+    import torch
+    per_op, sums = {}, []
+    n_launch = 4 * len(chain.layers)
+    ev = events(2 * n_launch)
+    for _ in range(n_steps):
+        names = []
+        i = 0
+        for L in chain.layers:
+            for name, fn in chain_ops(kcr, chain, L):
+                timed_launch(kcr, fn, ev[2 * i], ev[2 * i + 1])
+                names.append(name)
+                i += 1
+        torch.cuda.synchronize()
+        tot = 0.0
+        for j, name in enumerate(names):
+            ms = ev[2 * j].elapsed_time(ev[2 * j + 1])
+            per_op.setdefault(name, []).append(ms)
+            tot += ms
+        sums.append(tot)
+    return per_op, sums
+
+
+# ------------------------------------------------------- large shapes
+def large_shapes(kcr, iters: int):
+    """Each kernel at its large shape, three rotated buffer sets (more than
+    the 256 MB Infinity Cache holds), kernel durations from start/end stamps."""
+    import torch
+    import workloads
+    from kv_cache_rmsnorm_amd.chain import norm_bytes, rope_bytes, swiglu_bytes
+    dev = torch.device("cuda")
+    out = {}
+
+    def run(name, nbytes, fns, shape_desc):
+        ev = events(2 * iters)
+        for i in range(2):  # warm-up
+            fns[i % len(fns)]()
+        torch.cuda.synchronize()
+        for i in range(iters):
+            timed_launch(kcr, fns[i % len(fns)], ev[2 * i], ev[2 * i + 1])
+        torch.cuda.synchronize()
+        st = kernel_stats([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(iters)])
+        gbs = nbytes / (st["median_us"] * 1e-6) / 1e9
+        out[name] = dict(shape=shape_desc, bytes=nbytes, **{k: round(v, 3) for k, v in st.items()},
+                         gbs=round(gbs, 1), frac_of_peak=round(gbs / PEAK_GBS, 4))
+        log(f"{name}: {st['median_us']:.1f} us median, {gbs:.0f} GB/s ({100 * gbs / PEAK_GBS:.1f}% of peak)")
+
+    R = 131072
+    for dt, tag in ((torch.bfloat16, "bf16"), (torch.float32, "f32")):
+        wl = workloads.rmsnorm_rows(rows=R, d=2176, dtype=tag, seed=0)
+        xs = [wl["x"].to(dev)]
+        xs += [xs[0].clone() for _ in range(2)]
+        ys = [torch.empty_like(xs[0]) for _ in range(3)]
+        w = wl["w"].to(dev)
+        fns = [lambda i=i: kcr.rmsnorm(xs[i], w, wl["eps"], out=ys[i]) for i in range(3)]
+        run(f"rmsnorm_{tag}", norm_bytes(R, 2176, xs[0].element_size(), False), fns, f"[{R}, 2176] {tag}")
+        del xs, ys, wl
+    wl = workloads.add_rmsnorm_rows(R, 1536, dtype="bf16", seed=0)
+    xs = [wl["x"].to(dev) for _ in range(3)]
+    ds = [wl["delta"].to(dev) for _ in range(3)]
+    ys = [torch.empty_like(xs[0]) for _ in range(3)]
+    w = wl["w"].to(dev)
+    fns = [lambda i=i: kcr.add_rmsnorm(xs[i], ds[i], w, wl["eps"], out=ys[i]) for i in range(3)]
+    run("add_rmsnorm_bf16", norm_bytes(R, 1536, 2, True), fns, f"[{R}, 1536] bf16")
+    del xs, ds, ys, wl
+    wl = workloads.prefill(n_seqs=64, dtype="bf16", seed=0)
+    T = wl["qkv"].shape[0]
+    cos, sin = kcr.rope_cos_sin(wl["max_pos"], wl["dh"], wl["theta"])
+    qkvs = [wl["qkv"].to(dev)]
+    qkvs += [qkvs[0].clone() for _ in range(2)]
+    views = [workloads.qkv_views(b, wl["hq"], wl["hkv"], wl["dh"]) for b in qkvs]
+    cache = torch.empty(list(wl["cache"].shape), dtype=torch.bfloat16, device=dev)
+    pos, slots = wl["positions"].to(dev), wl["slot_mapping"].to(dev)
+    qo = [torch.empty((T, wl["hq"], wl["dh"]), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    fns = [lambda i=i: kcr.rope_kvstore(*views[i], pos, cos, sin, cache, slots, q_out=qo[i]) for i in range(3)]
+    nb = rope_bytes(T, wl["hq"], wl["hkv"], wl["dh"], 2, int(torch.unique(wl["positions"]).numel()))
+    run("rope_kvstore_bf16", nb, fns, f"64 seqs, T={T}, 12q/2kv x128, bf16")
+    del qkvs, views, cache, qo, wl
+    wl = workloads.swiglu_fused(rows=8192, inter=8960, dtype="bf16", seed=0)
+    gus = [wl["gate_up"].to(dev)]
+    gus += [gus[0].clone() for _ in range(2)]
+    outs = [torch.empty((8192, 8960), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    fns = [lambda i=i: kcr.swiglu(gus[i][:, :8960], gus[i][:, 8960:], out=outs[i]) for i in range(3)]
+    run("swiglu_bf16", swiglu_bytes(8192, 8960, 2), fns, "gate_up [8192, 17920] -> [8192, 8960] bf16")
+    del gus, outs, wl
+    torch.cuda.empty_cache()
+    return out
+
+
+def copy_ceiling(kcr, iters: int):
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.random_(generator=torch.Generator(device="cuda").manual_seed(0))
+    dsts = [torch.empty_like(src) for _ in range(2)]
+    ev = events(2 * iters)
+    kcr.copy_(dsts[0], src)
+    torch.cuda.synchronize()
+    for i in range(iters):
+        timed_launch(kcr, lambda i=i: kcr.copy_(dsts[i % 2], src), ev[2 * i], ev[2 * i + 1])
+    torch.cuda.synchronize()
+    st = kernel_stats([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(iters)])
+    e0, e1 = events(2)
+    e0.record()
+    for i in range(iters):
+        dsts[i % 2].copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    memcpy_ms = e0.elapsed_time(e1) / iters
+    res = dict(bytes_moved=2 * n, copy_kernel_gbs=round(2 * n / (st["median_us"] * 1e-6) / 1e9, 1),
+               copy_kernel_us=round(st["median_us"], 2),
+               hip_memcpy_gbs=round(2 * n / (memcpy_ms * 1e-3) / 1e9, 1))
+    log(f"copy ceiling: kernel {res['copy_kernel_gbs']} GB/s, hipMemcpy {res['hip_memcpy_gbs']} GB/s")
+    del src, dsts
+    return res
+
+
+# --------------------------------------------------------- CPU baseline
+def cpu_baseline_run(wl, bytes_per_step, budget_s: float):
+    import numpy as np
+    import torch
+    import oracle
+
+    def bits(t):
+        t = t.contiguous() if t.dim() == 1 else t
+        return t.view(torch.int16).numpy().view(np.uint16)
+
+    threads = oracle.num_threads()
+    eps = float(np.float32(wl["eps"]))
+    hq, hkv, dh = wl["hq"], wl["hkv"], wl["dh"]
+    layers = [dict(w_attn=bits(L["w_attn"]), w_mlp=bits(L["w_mlp"]), d_attn=bits(L["d_attn"]),
+                   d_mlp=bits(L["d_mlp"]),
+                   q=bits(L["qkv"][:, : hq * dh].unflatten(1, (hq, dh))),
+                   k=bits(L["qkv"][:, hq * dh:(hq + hkv) * dh].unflatten(1, (hkv, dh))),
+                   v=bits(L["qkv"][:, (hq + hkv) * dh:].unflatten(1, (hkv, dh))),
+                   gate=bits(L["gate_up"][:, : wl["inter"]]), up=bits(L["gate_up"][:, wl["inter"]:]))
+              for L in wl["layers"]]
+    cache = np.zeros(wl["cache_shape"], dtype=np.uint16)  # one shared, lazily mapped cache
+    pos, slots = wl["positions"].numpy(), wl["slot_mapping"].numpy()
+    h = bits(wl["h"]).copy()
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        for L in layers:
+            h, _ = oracle.add_rmsnorm(h, L["d_attn"], L["w_attn"], eps)
+            oracle.rope_kvstore(L["q"], L["k"], L["v"], pos, wl["theta"], cache, slots,
+                                block_size=wl["block_size"])
+            h, _ = oracle.add_rmsnorm(h, L["d_mlp"], L["w_mlp"], eps)
+            oracle.swiglu(L["gate"], L["up"])
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or el * (steps + 1) / steps > 3 * budget_s:
+            break
+    gbs = steps * bytes_per_step / el / 1e9
+    return dict(value=round(gbs, 3), unit="GB/s", cores=threads, kind="oracle",
+                sample=f"{steps} full step(s) of the same 28-layer, batch-256 chain "
+                       f"({steps * 112} op calls, {el:.1f} s); one shared cache array stands in "
+                       f"for the 28 per-layer caches (only the 256 named slots are touched)",
+                seconds=round(el, 2), ms_per_step=round(1e3 * el / steps, 1))
+
+
+def counter_traffic(kernel_name: str):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "swiglu_decode_chain_b256_counters.md")
+    if not os.path.exists(path):
+        return None, None
+    text = open(path).read()
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return None, None
+    data = json.loads(m.group(1))
+    if data.get("source_sha256") != kernel_source_sha():
+        return None, "kernel source changed since the counters were taken"
+    return data.get("traffic_bytes_per_launch"), None
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in ("swiglu.hip", "kcr_device.h", "kcr_host.h"):
+        h.update(open(os.path.join(ROOT, "kv_cache_rmsnorm_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--kernel-iters", type=int, default=30)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--skip-large", action="store_true", help="skip the per-kernel large shapes")
+    ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); the ops "
+              "shard by rows and tokens with no exchange, so a multi-GPU run is not part of this "
+              "benchmark", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kv_cache_rmsnorm_amd as kcr
+    import workloads
+    from kv_cache_rmsnorm_amd.chain import DecodeChain, swiglu_bytes
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    t0 = time.perf_counter()
+    wl = workloads.decode_chain()
+    log(f"generated workload in {time.perf_counter() - t0:.1f} s")
+    chain = DecodeChain(wl, "cuda", sentinel_cache=False)
+    nbytes = chain.bytes_per_step()
+    B, inter = chain.h.shape[0], chain.inter
+    log(f"step moves {nbytes['step']} algorithmic bytes over {4 * len(chain.layers)} launches")
+
+    # eager warm-up, then per-kernel durations inside whole steps
+    chain.step_eager()
+    torch.cuda.synchronize()
+    per_op, sums = instrumented_steps(kcr, chain, max(3, args.steps // 10))
+    sw = per_op["swiglu"]
+    sw_us = 1e3 * statistics.fmean(sw)
+    sw_bytes = swiglu_bytes(B, inter, 2)
+    kernel_sum_us = 1e3 * statistics.median(sums)
+
+    # eager steps (one Python launch per op)
+    for _ in range(3):
+        chain.step_eager()
+    torch.cuda.synchronize()
+    e0, e1 = events(2)
+    n_eager = max(5, args.steps // 5)
+    e0.record()
+    for _ in range(n_eager):
+        chain.step_eager()
+    e1.record()
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / n_eager
+
+    # graph replay: the timed region
+    chain.capture()
+    for _ in range(args.warmup):
+        chain.step_graph()
+    torch.cuda.synchronize()
+    e0, e1 = events(2)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        chain.step_graph()
+    e1.record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / args.steps
+    value = nbytes["step"] / (ms * 1e-3) / 1e9
+    log(f"graph step {ms * 1e3:.1f} us = {value:.0f} GB/s; eager {eager_ms * 1e3:.1f} us; "
+        f"kernel sum {kernel_sum_us:.1f} us; swiglu {sw_us:.2f} us")
+
+    ceiling = copy_ceiling(kcr, args.kernel_iters)
+    kernels = {} if args.skip_large else large_shapes(kcr, args.kernel_iters)
+
+    traffic, traffic_note = counter_traffic("swiglu")
+    achieved = sw_bytes / (sw_us * 1e-6) / 1e9
+    roofline = dict(bound="hbm", kernel="swiglu", shape=f"gate_up [{B}, {2 * inter}] -> [{B}, {inter}] bf16",
+                    bytes_per_launch=sw_bytes, mean_us=round(sw_us, 3), launches=len(sw),
+                    achieved=round(achieved, 1), peak=PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / PEAK_GBS, 4), traffic=traffic)
+    if traffic_note:
+        roofline["traffic_note"] = traffic_note
+
+    cpu = None
+    if not args.skip_cpu:
+        cpu = cpu_baseline_run(wl, nbytes["step"], args.cpu_seconds)
+        log(f"cpu oracle: {cpu['value']} GB/s on {cpu['cores']} threads ({cpu['sample']})")
+
+    op_us = {k: round(1e3 * statistics.fmean(v), 3) for k, v in per_op.items()}
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; shapes and distributions of the Qwen2.5-1.5B decode workload)",
+        "config": {"workload": "decode_chain: 28 layers x [add_rmsnorm, rope_kvstore, add_rmsnorm, swiglu], "
+                               "batch 256, ctx 4096 cached, hidden 1536, inter 8960, 12q/2kv heads x128, "
+                               "block 16, bf16",
+                   "launch": "hipgraph replay of 112 kernels", "global_batch": B},
+        "frac_of_peak": round(value / PEAK_GBS, 4),
+        "step_bytes": nbytes["step"],
+        "eager_ms_per_step": round(eager_ms, 5),
+        "kernel_sum_us_per_step": round(kernel_sum_us, 2),
+        "launch_gap_share_graph": round(1.0 - kernel_sum_us / (ms * 1e3), 4),
+        "op_mean_us": op_us,
+        "timed_wall_s": round(wall_s, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "ceiling": ceiling,
+        "kernels": kernels,
+        "device": torch.cuda.get_device_name(0),
+        "cus": kcr.device_cus(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,247 @@
+/*
+ * kcr.h -- C ABI of libkcr: hand-written HIP kernels for AMD MI355X (gfx950)
+ * covering the memory-bound per-token ops of small-LLM decode.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensor arguments are DEVICE pointers into memory the caller allocated on
+ *    the current HIP device; the library never allocates, frees, copies to
+ *    the host or synchronizes. Work is enqueued on `stream` (a hipStream_t
+ *    passed as void*; NULL means the default stream) and the call returns
+ *    as soon as the kernel is queued.
+ *  - Strides are in ELEMENTS, not bytes. The innermost dimension of every
+ *    tensor is contiguous.
+ *  - `dtype` is one of kcr_dtype. Weights, activations and the KV cache of
+ *    one call share that dtype; arithmetic is done in fp32 and every output
+ *    element is rounded once (to nearest, ties to even) into the dtype.
+ *  - Alignment: every pointer must be aligned to its element size
+ *    (KCR_ERR_ALIGN otherwise). Rows whose base address is 16-byte aligned
+ *    move with 16-byte vector loads and stores; other rows (for example the
+ *    rows of a densely packed tensor whose width is not a multiple of 16
+ *    bytes) are accessed element by element, correct but slower.
+ *    kcr_rope_kvstore is stricter, see there.
+ *  - Arguments are validated on the host before anything is launched; a
+ *    negative return code means nothing was enqueued. A call with no work
+ *    (rows == 0, T == 0) returns KCR_OK and launches nothing, and NULL
+ *    pointers are accepted then.
+ *  - Data-dependent indices (positions, slots) are bounds-checked inside the
+ *    kernels: an out-of-range index skips that token's writes instead of
+ *    touching memory outside the caller's buffers.
+ *  - Calls are thread-safe; the only library state is a per-device cache of
+ *    the compute-unit count.
+ *
+ * Citations name the web page and the section that defines each operation.
+ */
+#ifndef KCR_H
+#define KCR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kcr_dtype {
+    KCR_BF16 = 0, /* bfloat16 storage, fp32 arithmetic */
+    KCR_F32 = 1   /* float32 storage and arithmetic */
+} kcr_dtype;
+
+enum kcr_status {
+    KCR_OK = 0,
+    KCR_ERR_NULL = -1,   /* a required pointer is NULL while there is work to do */
+    KCR_ERR_SHAPE = -2,  /* a size is negative, zero where it must not be, or above a limit */
+    KCR_ERR_DTYPE = -3,  /* dtype is not a kcr_dtype */
+    KCR_ERR_ALIGN = -4,  /* a base pointer or a stride breaks 16-byte vector alignment */
+    KCR_ERR_HEADS = -5,  /* n_head is not a multiple of n_kv_head */
+    KCR_ERR_ALIAS = -6,  /* an output overlaps an input in a way the op does not allow */
+    KCR_ERR_LAUNCH = -7, /* the HIP runtime refused the launch (see hipGetLastError) */
+    KCR_ERR_DEVICE = -8  /* no usable HIP device is current */
+};
+
+/* Largest row width of the register-resident RMSNorm: 32768 bf16 or
+ * 16384 fp32 elements (one 256-lane workgroup, 16 x 16 bytes per lane). */
+#define KCR_NORM_MAX_D_BF16 32768
+#define KCR_NORM_MAX_D_F32 16384
+/* Largest head_dim accepted by kcr_rope_kvstore. */
+#define KCR_ROPE_MAX_HEAD_DIM 512
+
+/*
+ * kcr_rmsnorm -- row-wise RMSNorm with fp32 accumulation.
+ *
+ *   for each row r < rows:
+ *     ms   = sum_{j<d} x[r,j]^2 / d          (fp32 sum of the d real columns)
+ *     y[r,j] = x[r,j] * (ms + eps)^(-1/2) * w[j]
+ *
+ * Defined in the koas-w.github.io 2026-03-31 post, section 3 ("Triton
+ * RMSNorm": pow, mean, add eps, rsqrt, mul x, mul weight in one pass, fp32
+ * inside, cast back to the input dtype on write) and in m.lsln.cn/news/61269
+ * section 2.3 (var = sum(x^2)/n_cols, rstd = 1/sqrt(var + eps),
+ * y = x * rstd * w); the one-pass, register-resident form follows the csdn
+ * "Qwen3 from scratch (4-2): RMSNorm in Triton" page.
+ *
+ *   x    [rows, d] at row stride x_stride (>= d)          input
+ *   w    [d]       contiguous                              input
+ *   y    [rows, d] at row stride y_stride (>= d)          output
+ *   eps  added to the mean square before the reciprocal square root
+ *
+ * y may be x itself (same pointer and stride: in-place); any other overlap
+ * of y with x or w is KCR_ERR_ALIAS. 1 <= d <= KCR_NORM_MAX_D_* else
+ * KCR_ERR_SHAPE.
+ */
+int kcr_rmsnorm(const void* x, int64_t x_stride, const void* w, void* y, int64_t y_stride,
+                int64_t rows, int64_t d, float eps, int dtype, void* stream);
+
+/*
+ * kcr_add_rmsnorm -- residual add fused with RMSNorm.
+ *
+ *   x[r,j] <- round(x[r,j] + delta[r,j])            (x is updated in place)
+ *   y[r,:]  = rmsnorm(x[r,:]) * w                   (norm of the rounded sum)
+ *
+ * Defined in the koas-w.github.io 2026-03-31 post, section 4 ("Fused Add
+ * Norm"): x + residual is formed in registers, x is updated in place to the
+ * sum and the normalised sum is returned (one read of each input, two
+ * writes). The stored sum is what the norm sees, so the result equals the
+ * unfused "x = x + delta; y = rmsnorm(x)" and the updated x is bit-exact.
+ *
+ *   x     [rows, d] at x_stride       input and output (the residual stream)
+ *   delta [rows, d] at delta_stride   input (attention or MLP output)
+ *   w, y, eps, rows, d                as for kcr_rmsnorm
+ *
+ * y must not overlap x, delta or w, and delta must not overlap x
+ * (KCR_ERR_ALIAS). Limits as for kcr_rmsnorm.
+ */
+int kcr_add_rmsnorm(void* x, int64_t x_stride, const void* delta, int64_t delta_stride,
+                    const void* w, void* y, int64_t y_stride, int64_t rows, int64_t d,
+                    float eps, int dtype, void* stream);
+
+/*
+ * kcr_rope_kvstore -- rotate-half RoPE of Q and K fused with the paged
+ * KV-cache store of the rotated K and of V.
+ *
+ * For each token t with p = positions[t] and each frequency i < head_dim/2,
+ * with c = cos_tab[p, i] and s = sin_tab[p, i]:
+ *     out[i]              = x[i] * c - x[i + head_dim/2] * s
+ *     out[i + head_dim/2] = x[i + head_dim/2] * c + x[i] * s
+ * for every query head (written to q_out) and every KV head (written to the
+ * cache). Then, if 0 <= slot = slot_mapping[t] < num_blocks * block_size,
+ * with block = slot / block_size and offset = slot % block_size:
+ *     kv_cache[0, block, offset, h, :] = rotated k[t, h, :]
+ *     kv_cache[1, block, offset, h, :] = v[t, h, :]           (bit copy)
+ *
+ * Defined in the koas-w.github.io 2026-03-31 post, section 1 ("Fused RoPE &
+ * Paged KV Cache Store": Q, K, V, cos and sin read once, the rotation done in
+ * registers, Q written back to contiguous memory, rotated K and V written
+ * directly to the cache slots named by slot_mapping; query heads share KV
+ * heads through kv_head = head / (n_head / n_kv_head)); rotate-half pairing
+ * from the same section's description of the unfused version (slice the
+ * halves, negate, concatenate); cache layout from mer.dev "AsyncT vLLM notes
+ * (1)", section 1.1, and slot = block * block_size + offset from its
+ * section 1.4; precomputed cos/sin tables from m.lsln.cn/news/61269
+ * section 2.3.
+ *
+ *   q   [T, n_head, head_dim]     strides (q_tok_stride, q_head_stride)   input
+ *   k   [T, n_kv_head, head_dim]  strides (k_tok_stride, k_head_stride)   input
+ *   v   [T, n_kv_head, head_dim]  strides (v_tok_stride, v_head_stride)   input
+ *       (q, k and v may be narrow views of one fused QKV projection buffer)
+ *   q_out [T, n_head, head_dim] contiguous                                output
+ *       may be q itself only when q is contiguous; no other overlap
+ *   positions [T] int64; tokens with p outside [0, max_pos) are skipped
+ *       entirely (no q_out, no cache write)
+ *   cos_tab, sin_tab [max_pos, head_dim/2] fp32, contiguous (for example
+ *       from kcr_rope_cos_sin)
+ *   kv_cache [2, num_blocks, block_size, n_kv_head, head_dim] contiguous
+ *   slot_mapping [T] int64; a negative slot marks a padding token whose K
+ *       and V are not stored; slots must be distinct (with repeats, which
+ *       token's data lands in the slot is unspecified)
+ *
+ * Alignment: q, k, v, q_out, the tables and the cache must be 16-byte
+ * aligned and every head and token stride a multiple of 16 bytes
+ * (KCR_ERR_ALIGN); positions and slot_mapping 8-byte aligned.
+ *
+ * Errors: KCR_ERR_HEADS when n_head % n_kv_head != 0; KCR_ERR_SHAPE unless
+ * head_dim is even, head_dim/2 is a multiple of 16 bytes' worth of elements
+ * (8 bf16, 4 fp32), head_dim <= KCR_ROPE_MAX_HEAD_DIM, n_kv_head >= 1,
+ * block_size >= 1, num_blocks >= 0, max_pos >= 1; KCR_ERR_ALIAS when q_out
+ * overlaps k, v, the tables or the cache, or the cache overlaps q, k or v.
+ */
+int kcr_rope_kvstore(const void* q, int64_t q_tok_stride, int64_t q_head_stride,
+                     const void* k, int64_t k_tok_stride, int64_t k_head_stride,
+                     const void* v, int64_t v_tok_stride, int64_t v_head_stride,
+                     void* q_out, const int64_t* positions, const float* cos_tab,
+                     const float* sin_tab, int64_t max_pos, void* kv_cache,
+                     const int64_t* slot_mapping, int64_t T, int n_head, int n_kv_head,
+                     int head_dim, int block_size, int64_t num_blocks, int dtype, void* stream);
+
+/*
+ * kcr_rope_cos_sin -- fill the RoPE tables on the device:
+ *     cos_tab[p, i] = cos(p * theta^(-2i/head_dim)),  sin_tab likewise,
+ * for p < max_pos and i < head_dim/2, evaluated in fp64 and rounded once
+ * to fp32. The tables are precomputed once rather than evaluated per token
+ * (m.lsln.cn/news/61269, section 2.3) and kept in fp32 because low-precision
+ * trigonometry loses accuracy as positions grow (same page, section 1.1).
+ * Frequencies are the RoFormer ones.
+ *
+ *   cos_tab, sin_tab [max_pos, head_dim/2] fp32 device outputs, 16-byte
+ *   aligned; head_dim even and >= 2; max_pos >= 0.
+ */
+int kcr_rope_cos_sin(float* cos_tab, float* sin_tab, int64_t max_pos, int head_dim,
+                     double theta, void* stream);
+
+/*
+ * kcr_swiglu -- SwiGLU activation: out = silu(gate) * up, with
+ * silu(g) = g / (1 + exp(-g)), in fp32, rounded once.
+ *
+ * Defined in the koas-w.github.io 2026-03-31 post, section 2 ("Fused
+ * SwiGLU": gate and up loaded together, sigmoid, gate * sigmoid and the
+ * product with up done in registers, one write); the flattened (row x
+ * column) work split follows the same section.
+ *
+ *   gate [rows, cols] at gate_stride   input
+ *   up   [rows, cols] at up_stride     input
+ *   out  [rows, cols] at out_stride    output
+ *
+ * For a fused gate_up [rows, 2*cols] buffer (gate first): up = gate + cols
+ * and gate_stride = up_stride = 2*cols. out may be gate or up itself (same
+ * pointer and stride); any other overlap is KCR_ERR_ALIAS. rows * ceil(cols
+ * / (16 bytes' worth of elements)) must stay below 2^31 (KCR_ERR_SHAPE).
+ */
+int kcr_swiglu(const void* gate, int64_t gate_stride, const void* up, int64_t up_stride,
+               void* out, int64_t out_stride, int64_t rows, int64_t cols, int dtype,
+               void* stream);
+
+/*
+ * kcr_copy -- plain streaming copy of `bytes` bytes (a multiple of 16, both
+ * pointers 16-byte aligned, no overlap). It moves data with the same 16-byte
+ * vector loads and stores as the kernels above and serves as the measured
+ * bandwidth ceiling and as the reference for hardware byte counters.
+ */
+int kcr_copy(void* dst, const void* src, int64_t bytes, void* stream);
+
+/* Measurement hook: the calling thread's next kernel launch through this
+ * library records `start_event` when the kernel begins executing and
+ * `stop_event` when it ends (hipExtLaunchKernel), so their elapsed time is
+ * the kernel's own duration, free of launch gaps. Both are hipEvent_t
+ * handles created by the caller with timing enabled (either may be NULL).
+ * The arming is consumed by that one launch. */
+int kcr_time_next_launch(void* start_event, void* stop_event);
+
+/* Number of compute units of the current device (0 if none is usable). */
+int kcr_device_cus(void);
+
+/* Checks the host-side helper arithmetic (fast integer division constants,
+ * dispatch bucket choice) exhaustively on small ranges and by sampling on
+ * large ones. Needs no GPU. Returns 0 on success, else the number of the
+ * first failing check. */
+int kcr_selftest_host(void);
+
+/* Human-readable message for a kcr_status value. */
+const char* kcr_strerror(int status);
+
+/* Library version string. */
+const char* kcr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KCR_H */

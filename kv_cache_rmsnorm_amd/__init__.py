@@ -1,0 +1,217 @@
+"""kv_cache_rmsnorm_amd -- Python binding of libkcr, the gfx950 HIP library of
+fused per-token decode ops (C ABI in include/kcr.h).
+
+This module only marshals arguments: it reads pointers, strides and the
+current HIP stream off torch tensors and calls the library. Every step of
+the computation runs in the library's kernels; there is no fallback path, and
+importing this module fails if libkcr.so has not been built
+(``python kv_cache_rmsnorm_amd/build.py``).
+
+Ops (names as in the C ABI):
+  rmsnorm(x, w, eps)                       y = x * rsqrt(mean(x^2) + eps) * w
+  add_rmsnorm(x, delta, w, eps)            x <- x + delta (in place); y = rmsnorm(x) * w
+  rope_kvstore(q, k, v, positions, cos, sin, kv_cache, slot_mapping)
+                                           rotate-half RoPE of Q/K; q_out; K_rot, V -> cache
+  swiglu(gate, up)                         silu(gate) * up
+  rope_cos_sin(max_pos, head_dim, theta)   fp32 cos/sin tables built on the device
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkcr.so")
+
+BF16, F32 = 0, 1
+_DTYPE = {torch.bfloat16: BF16, torch.float32: F32}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python kv_cache_rmsnorm_amd/build.py`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P, _I64, _I, _F, _D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_double
+_SIGS = {
+    "kcr_rmsnorm": [_P, _I64, _P, _P, _I64, _I64, _I64, _F, _I, _P],
+    "kcr_add_rmsnorm": [_P, _I64, _P, _I64, _P, _P, _I64, _I64, _I64, _F, _I, _P],
+    "kcr_rope_kvstore": [_P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _P, _P, _P, _P, _I64, _P,
+                         _P, _I64, _I, _I, _I, _I, _I64, _I, _P],
+    "kcr_rope_cos_sin": [_P, _P, _I64, _I, _D, _P],
+    "kcr_swiglu": [_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I, _P],
+    "kcr_copy": [_P, _P, _I64, _P],
+    "kcr_time_next_launch": [_P, _P],
+    "kcr_device_cus": [],
+    "kcr_selftest_host": [],
+}
+for _name, _args in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _I
+_lib.kcr_strerror.argtypes = [_I]
+_lib.kcr_strerror.restype = ctypes.c_char_p
+_lib.kcr_version.argtypes = []
+_lib.kcr_version.restype = ctypes.c_char_p
+
+
+class KcrError(RuntimeError):
+    def __init__(self, op: str, status: int):
+        self.status = status
+        super().__init__(f"{op}: {_lib.kcr_strerror(status).decode()} (status {status})")
+
+
+def _check(op: str, status: int) -> None:
+    if status != 0:
+        raise KcrError(op, status)
+
+
+def _dt(*ts: torch.Tensor) -> int:
+    dt = ts[0].dtype
+    for t in ts:
+        if t.dtype != dt:
+            raise TypeError(f"mixed dtypes {dt} and {t.dtype}")
+        if t.device.type != "cuda":
+            raise ValueError("kcr ops take device tensors")
+    if dt not in _DTYPE:
+        raise TypeError(f"unsupported dtype {dt}")
+    return _DTYPE[dt]
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _rows(t: torch.Tensor):
+    """(rows, cols, row stride) of a tensor viewed as 2-D over its last dim."""
+    if t.stride(-1) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    cols = t.shape[-1]
+    if t.dim() == 1:
+        return 1, cols, cols
+    flat = t.reshape(-1, cols) if t.dim() > 2 else t
+    if flat.data_ptr() != t.data_ptr() or (t.dim() > 2 and not _uniform_rows(t)):
+        raise ValueError("leading dimensions must collapse to one row stride")
+    return flat.shape[0], cols, (flat.stride(0) if flat.shape[0] > 1 else cols)
+
+
+def _uniform_rows(t: torch.Tensor) -> bool:
+    expect = t.stride(-2)
+    for i in range(t.dim() - 2, 0, -1):
+        expect *= t.shape[i]
+        if t.shape[i - 1] > 1 and t.stride(i - 1) != expect:
+            return False
+    return True
+
+
+# ------------------------------------------------------------------- ops
+def rmsnorm(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
+            out: torch.Tensor | None = None) -> torch.Tensor:
+    dt = _dt(x, w)
+    rows, d, xs = _rows(x)
+    y = torch.empty_like(x, memory_format=torch.contiguous_format) if out is None else out
+    _, _, ys = _rows(y)
+    _check("rmsnorm", _lib.kcr_rmsnorm(x.data_ptr(), xs, w.data_ptr(), y.data_ptr(), ys, rows, d,
+                                       float(eps), dt, _stream(x)))
+    return y
+
+
+def add_rmsnorm(x: torch.Tensor, delta: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
+                out: torch.Tensor | None = None) -> torch.Tensor:
+    """x is updated in place to x + delta; returns rmsnorm(x + delta) * w."""
+    dt = _dt(x, delta, w)
+    rows, d, xs = _rows(x)
+    _, _, ds = _rows(delta)
+    y = torch.empty_like(x, memory_format=torch.contiguous_format) if out is None else out
+    _, _, ys = _rows(y)
+    _check("add_rmsnorm", _lib.kcr_add_rmsnorm(x.data_ptr(), xs, delta.data_ptr(), ds, w.data_ptr(),
+                                               y.data_ptr(), ys, rows, d, float(eps), dt, _stream(x)))
+    return y
+
+
+def rope_kvstore(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, positions: torch.Tensor,
+                 cos: torch.Tensor, sin: torch.Tensor, kv_cache: torch.Tensor,
+                 slot_mapping: torch.Tensor, q_out: torch.Tensor | None = None) -> torch.Tensor:
+    """q [T,Hq,D], k/v [T,Hkv,D] (views allowed), positions/slot_mapping [T]
+    int64, cos/sin [max_pos, D/2] fp32, kv_cache [2, blocks, block_size, Hkv, D].
+    Returns q_out [T,Hq,D] (contiguous); K_rot and V land in kv_cache."""
+    dt = _dt(q, k, v, kv_cache)
+    T, hq, hd = q.shape
+    hkv = k.shape[1]
+    if positions.dtype != torch.int64 or slot_mapping.dtype != torch.int64:
+        raise TypeError("positions and slot_mapping must be int64")
+    if cos.dtype != torch.float32 or sin.dtype != torch.float32:
+        raise TypeError("cos/sin tables must be float32")
+    if not (cos.is_contiguous() and sin.is_contiguous() and kv_cache.is_contiguous()
+            and positions.is_contiguous() and slot_mapping.is_contiguous()):
+        raise ValueError("tables, cache, positions and slot_mapping must be contiguous")
+    if kv_cache.dim() != 5 or kv_cache.shape[0] != 2 or tuple(kv_cache.shape[3:]) != (hkv, hd):
+        raise ValueError("kv_cache must be [2, num_blocks, block_size, n_kv_head, head_dim]")
+    if q_out is None:
+        q_out = torch.empty((T, hq, hd), dtype=q.dtype, device=q.device)
+    _check("rope_kvstore", _lib.kcr_rope_kvstore(
+        q.data_ptr(), q.stride(0), q.stride(1), k.data_ptr(), k.stride(0), k.stride(1),
+        v.data_ptr(), v.stride(0), v.stride(1), q_out.data_ptr(), positions.data_ptr(),
+        cos.data_ptr(), sin.data_ptr(), cos.shape[0], kv_cache.data_ptr(), slot_mapping.data_ptr(),
+        T, hq, hkv, hd, kv_cache.shape[2], kv_cache.shape[1], dt, _stream(q)))
+    return q_out
+
+
+def rope_cos_sin(max_pos: int, head_dim: int, theta: float, device="cuda"):
+    cos = torch.empty((max_pos, head_dim // 2), dtype=torch.float32, device=device)
+    sin = torch.empty_like(cos)
+    _check("rope_cos_sin", _lib.kcr_rope_cos_sin(cos.data_ptr(), sin.data_ptr(), max_pos, head_dim,
+                                                 float(theta), _stream(cos)))
+    return cos, sin
+
+
+def swiglu(gate: torch.Tensor, up: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    dt = _dt(gate, up)
+    rows, cols, gs = _rows(gate)
+    _, _, us = _rows(up)
+    if out is None:
+        out = torch.empty(gate.shape, dtype=gate.dtype, device=gate.device)
+    _, _, os_ = _rows(out)
+    _check("swiglu", _lib.kcr_swiglu(gate.data_ptr(), gs, up.data_ptr(), us, out.data_ptr(), os_,
+                                     rows, cols, dt, _stream(gate)))
+    return out
+
+
+def swiglu_fused(gate_up: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """SwiGLU of a fused [..., 2*I] buffer whose first half is the gate."""
+    inter = gate_up.shape[-1] // 2
+    return swiglu(gate_up[..., :inter], gate_up[..., inter:], out=out)
+
+
+def copy_(dst: torch.Tensor, src: torch.Tensor) -> torch.Tensor:
+    """Plain 16-byte streaming copy of src's bytes into dst (bandwidth probe)."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n or not (dst.is_contiguous() and src.is_contiguous()):
+        raise ValueError("copy_ needs contiguous tensors, dst at least as large as src")
+    _check("copy", _lib.kcr_copy(dst.data_ptr(), src.data_ptr(), n, _stream(src)))
+    return dst
+
+
+def time_next_launch(start: torch.cuda.Event, stop: torch.cuda.Event) -> None:
+    """Arm a pair of timing events (already recorded once, so that they
+    exist) to be stamped at the start and end of the calling thread's next
+    kcr kernel; start.elapsed_time(stop) is then that kernel's duration."""
+    _check("time_next_launch", _lib.kcr_time_next_launch(start.cuda_event, stop.cuda_event))
+
+
+def device_cus() -> int:
+    return _lib.kcr_device_cus()
+
+
+def selftest_host() -> int:
+    return _lib.kcr_selftest_host()
+
+
+def version() -> str:
+    return _lib.kcr_version().decode()
+
+
+def raw_lib():
+    """The ctypes handle of libkcr.so, for callers that drive the C ABI directly."""
+    return _lib

@@ -1,0 +1,223 @@
+// kcr_device.h -- device-side building blocks shared by the gfx950 kernels:
+// 16-byte vector loads and stores with an element-wise tail, bf16 <-> fp32
+// conversion, and the wave64 sum reduction.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kcr {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Storage types. kVec is the number of elements in one 16-byte vector, the
+// unit of every global load and store (global_load_dwordx4 /
+// global_store_dwordx4).
+struct Bf16 {
+    using storage = uint16_t;
+    static constexpr int kVec = 8;
+};
+struct F32 {
+    using storage = float;
+    static constexpr int kVec = 4;
+};
+
+// ---------------------------------------------------------------- codec
+// bf16 is the top half of an fp32, so widening is a shift or a mask.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 -> two bf16, round to nearest even, one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2 f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    return (uint16_t)(pack_bf16x2(f, 0.0f) & 0xffffu);
+}
+
+// Unpack a 16-byte vector into kVec floats, and pack back.
+template <typename T>
+__device__ __forceinline__ void unpack(const u32x4& v, float* f);
+template <>
+__device__ __forceinline__ void unpack<Bf16>(const u32x4& v, float* f) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f[2 * j] = bf16_lo(v[j]);
+        f[2 * j + 1] = bf16_hi(v[j]);
+    }
+}
+template <>
+__device__ __forceinline__ void unpack<F32>(const u32x4& v, float* f) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f[j] = __uint_as_float(v[j]);
+}
+
+template <typename T>
+__device__ __forceinline__ u32x4 pack(const float* f);
+template <>
+__device__ __forceinline__ u32x4 pack<Bf16>(const float* f) {
+    u32x4 v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = pack_bf16x2(f[2 * j], f[2 * j + 1]);
+    return v;
+}
+template <>
+__device__ __forceinline__ u32x4 pack<F32>(const float* f) {
+    u32x4 v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = __float_as_uint(f[j]);
+    return v;
+}
+
+// Single elements, for the ragged tail of a row.
+template <typename T>
+__device__ __forceinline__ float load_one(const void* base, int64_t i);
+template <>
+__device__ __forceinline__ float load_one<Bf16>(const void* base, int64_t i) {
+    return bf16_to_f32(static_cast<const uint16_t*>(base)[i]);
+}
+template <>
+__device__ __forceinline__ float load_one<F32>(const void* base, int64_t i) {
+    return static_cast<const float*>(base)[i];
+}
+template <typename T>
+__device__ __forceinline__ void store_one(void* base, int64_t i, float v);
+template <>
+__device__ __forceinline__ void store_one<Bf16>(void* base, int64_t i, float v) {
+    static_cast<uint16_t*>(base)[i] = f32_to_bf16(v);
+}
+template <>
+__device__ __forceinline__ void store_one<F32>(void* base, int64_t i, float v) {
+    static_cast<float*>(base)[i] = v;
+}
+
+// ------------------------------------------------------------ vector I/O
+// `elem` is an element offset that is a multiple of kVec, so the address is
+// 16-byte aligned whenever the base and the row stride are.
+template <typename T>
+__device__ __forceinline__ u32x4 ld16(const void* base, int64_t elem) {
+    return *reinterpret_cast<const u32x4*>(static_cast<const typename T::storage*>(base) + elem);
+}
+template <typename T>
+__device__ __forceinline__ u32x4 ld16_nt(const void* base, int64_t elem) {
+    return __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(static_cast<const typename T::storage*>(base) + elem));
+}
+template <typename T>
+__device__ __forceinline__ void st16(void* base, int64_t elem, const u32x4& v) {
+    *reinterpret_cast<u32x4*>(static_cast<typename T::storage*>(base) + elem) = v;
+}
+template <typename T>
+__device__ __forceinline__ void st16_nt(void* base, int64_t elem, const u32x4& v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(static_cast<typename T::storage*>(base) + elem));
+}
+
+// Loads the vector that starts at element `elem` of a row of `n` elements:
+// a full 16-byte load when the whole vector is inside the row, element loads
+// for the `n - elem` (< kVec) valid elements of a ragged tail, zeros past the
+// end. Returns the floats in f[0..kVec).
+template <typename T, bool NT>
+__device__ __forceinline__ void load_vec(const void* base, int64_t elem, int64_t n, float* f) {
+    if (elem + T::kVec <= n) {
+        u32x4 v = NT ? ld16_nt<T>(base, elem) : ld16<T>(base, elem);
+        unpack<T>(v, f);
+    } else {
+#pragma unroll
+        for (int e = 0; e < T::kVec; ++e) f[e] = (elem + e < n) ? load_one<T>(base, elem + e) : 0.0f;
+    }
+}
+
+template <typename T, bool NT>
+__device__ __forceinline__ void store_vec(void* base, int64_t elem, int64_t n, const float* f) {
+    if (elem + T::kVec <= n) {
+        u32x4 v = pack<T>(f);
+        if (NT) st16_nt<T>(base, elem, v); else st16<T>(base, elem, v);
+    } else {
+#pragma unroll
+        for (int e = 0; e < T::kVec; ++e)
+            if (elem + e < n) store_one<T>(base, elem + e, f[e]);
+    }
+}
+
+// Raw-bit variants: the vector starting at element `elem` of a row of `n`
+// elements, as it sits in memory. `vec` says whether the row's base address
+// is 16-byte aligned; when it is, every vector wholly inside the row moves
+// with one 16-byte access, and otherwise (and for the vector that straddles
+// the end of the row) element by element. Elements past the end of the row
+// read as zero bits (+0.0 in both dtypes) and are never written.
+__host__ __device__ __forceinline__ bool aligned16(const void* p) {
+    return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+template <typename T, bool NT>
+__device__ __forceinline__ u32x4 load_raw(const void* base, int64_t elem, int64_t n, bool vec = true) {
+    if (vec && elem + T::kVec <= n) return NT ? ld16_nt<T>(base, elem) : ld16<T>(base, elem);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    const typename T::storage* p = static_cast<const typename T::storage*>(base) + elem;
+#pragma unroll
+    for (int e = 0; e < T::kVec; ++e) {
+        if (elem + e < n) {
+            if constexpr (T::kVec == 8) v[e >> 1] |= (uint32_t)p[e] << (16 * (e & 1));
+            else v[e] = __float_as_uint(p[e]);
+        }
+    }
+    return v;
+}
+
+template <typename T, bool NT>
+__device__ __forceinline__ void store_raw(void* base, int64_t elem, int64_t n, const u32x4& v,
+                                          bool vec = true) {
+    if (vec && elem + T::kVec <= n) {
+        if (NT) st16_nt<T>(base, elem, v); else st16<T>(base, elem, v);
+        return;
+    }
+    typename T::storage* p = static_cast<typename T::storage*>(base) + elem;
+#pragma unroll
+    for (int e = 0; e < T::kVec; ++e) {
+        if (elem + e < n) {
+            if constexpr (T::kVec == 8) p[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+            else p[e] = __uint_as_float(v[e]);
+        }
+    }
+}
+
+// ------------------------------------------------------------ reductions
+// DPP lane permutations within rows of 16 lanes (gfx9 encodings).
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm:[1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm:[2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141; // lane i <- lane 7-i within each half row
+constexpr int kDppRowMirror = 0x140;    // lane i <- lane 15-i within each row
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over all 64 lanes of a wave; every lane must be active. The result is
+// wave-uniform (the same value, bit for bit, in every lane): four DPP steps
+// leave each 16-lane row's sum in all its lanes, and the four row sums are
+// read out with v_readlane and added in a fixed order.
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp<kDppQuadXor1>(v);
+    v += dpp<kDppQuadXor2>(v);
+    v += dpp<kDppRowHalfMirror>(v);
+    v += dpp<kDppRowMirror>(v);
+    float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+// Wave index made explicitly uniform, so that row and unit indices derived
+// from it live in scalar registers.
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
+}  // namespace kcr

@@ -1,0 +1,248 @@
+// rope_kvstore.hip -- rotate-half RoPE of Q and K fused with the paged
+// KV-cache store of rotated K and V (kcr_rope_kvstore), and the device-side
+// cos/sin table build (kcr_rope_cos_sin).
+//
+// The op is the fused kernel of the koas-w.github.io 2026-03-31 post,
+// section 1 ("Fused RoPE & Paged KV Cache Store"): Q, K, V, cos and sin are
+// read once, rotated in registers, Q goes back to contiguous memory and the
+// rotated K and V go straight to the cache slots named by slot_mapping.
+// Cache layout [2, num_blocks, block_size, kv_heads, head_dim] as in mer.dev
+// "AsyncT vLLM notes (1)", section 1.1.
+//
+// gfx950 design
+//  * Work unit = (token t, KV group g). Following the GQA mapping of the
+//    same section, kv_head = head / (n_head / n_kv_head), group g holds the
+//    query heads g*G .. g*G+G-1 (G = n_head / n_kv_head) -- contiguous in
+//    memory -- plus K head g and V head g: G + 2 "virtual heads" of equal
+//    cost, so every unit does the same work and no lane idles on K/V.
+//  * LPU lanes per unit (the next power of two at or above the number of
+//    16-byte chunks in half a head: 8 for bf16 head_dim 128). Lane c owns
+//    chunk c of the first half AND chunk c of the second half, so each
+//    rotation pair (i, i + d/2) sits in one lane and needs no shuffle.
+//  * cos/sin for the lane's frequencies are loaded once per unit (fp32
+//    table rows) and reused for all G + 2 virtual heads; HU heads are loaded
+//    before any is stored, so a lane keeps 2*HU 16-byte loads in flight.
+//  * K_rot and V are written with 16-byte stores at
+//    ((which * n_slots + slot) * n_kv_head + g) * head_dim: the cache's
+//    (block, offset) pair flattens to the slot, so no division is needed.
+//    V is moved as raw bits (bit-exact); Q and K go through fp32.
+#include "kcr_device.h"
+#include "kcr_host.h"
+
+namespace kcr {
+
+struct RopeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* q_out;
+    void* cache;
+    const int64_t* pos;
+    const int64_t* slots;
+    const float* cos_t;
+    const float* sin_t;
+    int64_t q_ts, q_hs, k_ts, k_hs, v_ts, v_hs;  // elements
+    int64_t max_pos, n_slots;
+    uint32_t units;  // T * n_kv_head
+    FastDiv hkv;     // division by n_kv_head
+    int32_t hq, group, dh;
+};
+
+template <typename T, int LPU, int HU>
+__global__ __launch_bounds__(256) void rope_kvstore_kernel(const RopeArgs a) {
+    using S = typename T::storage;
+    constexpr int kVec = T::kVec;
+    constexpr int UPW = 256 / LPU;  // units per workgroup
+    const int c = threadIdx.x % LPU;
+    const int half = a.dh >> 1;
+    const bool lane_on = c * kVec < half;
+    const int nvh = a.group + 2;
+    const int64_t c0 = (int64_t)c * kVec;
+
+    for (uint32_t u = blockIdx.x * UPW + threadIdx.x / LPU; u < a.units; u += gridDim.x * UPW) {
+        const uint32_t t = fastdiv(u, a.hkv);
+        const int g = (int)(u - t * a.hkv.d);
+        const int64_t p = a.pos[t];
+        if (!lane_on || p < 0 || p >= a.max_pos) continue;
+        const int64_t slot = a.slots[t];
+        const bool store_kv = slot >= 0 && slot < a.n_slots;
+
+        float cs[kVec], sn[kVec];
+        {
+            const float* cr = a.cos_t + p * half + c0;
+            const float* sr = a.sin_t + p * half + c0;
+#pragma unroll
+            for (int i = 0; i < kVec; i += 4) {
+                u32x4 cv = *reinterpret_cast<const u32x4*>(cr + i);
+                u32x4 sv = *reinterpret_cast<const u32x4*>(sr + i);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    cs[i + e] = __uint_as_float(cv[e]);
+                    sn[i + e] = __uint_as_float(sv[e]);
+                }
+            }
+        }
+
+        for (int j0 = 0; j0 < nvh; j0 += HU) {
+            u32x4 x1[HU], x2[HU];
+#pragma unroll
+            for (int h = 0; h < HU; ++h) {
+                const int j = j0 + h;
+                if (j >= nvh) break;
+                const S* src;
+                if (j < a.group) src = static_cast<const S*>(a.q) + t * a.q_ts + (int64_t)(g * a.group + j) * a.q_hs;
+                else if (j == a.group) src = static_cast<const S*>(a.k) + t * a.k_ts + (int64_t)g * a.k_hs;
+                else src = static_cast<const S*>(a.v) + t * a.v_ts + (int64_t)g * a.v_hs;
+                x1[h] = *reinterpret_cast<const u32x4*>(src + c0);
+                x2[h] = *reinterpret_cast<const u32x4*>(src + half + c0);
+            }
+#pragma unroll
+            for (int h = 0; h < HU; ++h) {
+                const int j = j0 + h;
+                if (j >= nvh) break;
+                S* dst;
+                if (j < a.group) {
+                    dst = static_cast<S*>(a.q_out) + ((int64_t)t * a.hq + g * a.group + j) * a.dh;
+                } else {
+                    if (!store_kv) continue;
+                    const int64_t which = j == a.group ? 0 : 1;
+                    dst = static_cast<S*>(a.cache) +
+                          ((which * a.n_slots + slot) * a.hkv.d + g) * (int64_t)a.dh;
+                }
+                u32x4 o1 = x1[h], o2 = x2[h];
+                if (j <= a.group) {  // Q or K: rotate; V is copied as is
+                    float f1[kVec], f2[kVec], r1[kVec], r2[kVec];
+                    unpack<T>(x1[h], f1);
+                    unpack<T>(x2[h], f2);
+#pragma unroll
+                    for (int e = 0; e < kVec; ++e) {
+                        r1[e] = f1[e] * cs[e] - f2[e] * sn[e];
+                        r2[e] = f2[e] * cs[e] + f1[e] * sn[e];
+                    }
+                    o1 = pack<T>(r1);
+                    o2 = pack<T>(r2);
+                }
+                *reinterpret_cast<u32x4*>(dst + c0) = o1;
+                *reinterpret_cast<u32x4*>(dst + half + c0) = o2;
+            }
+        }
+    }
+}
+
+constexpr int kRopeHU = 8;
+constexpr int kRopeWgsPerCu = 8;
+
+template <typename T, int LPU>
+static int launch_rope(const RopeArgs& a, void* stream) {
+    constexpr int UPW = 256 / LPU;
+    const dim3 grid(grid_for(a.units, UPW, device_cus(), kRopeWgsPerCu));
+    return launch(rope_kvstore_kernel<T, LPU, kRopeHU>, grid, dim3(256), stream, a);
+}
+
+template <typename T>
+static int dispatch_rope(const RopeArgs& a, void* stream) {
+    const int chunks = (a.dh / 2) / T::kVec;
+    if (chunks <= 1) return launch_rope<T, 1>(a, stream);
+    if (chunks <= 2) return launch_rope<T, 2>(a, stream);
+    if (chunks <= 4) return launch_rope<T, 4>(a, stream);
+    if (chunks <= 8) return launch_rope<T, 8>(a, stream);
+    if (chunks <= 16) return launch_rope<T, 16>(a, stream);
+    if (chunks <= 32) return launch_rope<T, 32>(a, stream);
+    if (chunks <= 64) return launch_rope<T, 64>(a, stream);
+    return KCR_ERR_SHAPE;
+}
+
+// ---------------------------------------------------------- cos/sin tables
+struct TableArgs {
+    float* cos_t;
+    float* sin_t;
+    int64_t n;  // max_pos * half
+    int32_t half, head_dim;
+    double theta;
+};
+
+// cos/sin(p * theta^(-2i/d)) in fp64, rounded once to fp32.
+__global__ __launch_bounds__(256) void rope_table_kernel(const TableArgs a) {
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < a.n;
+         idx += (int64_t)gridDim.x * 256) {
+        const int64_t p = idx / a.half;
+        const int i = (int)(idx - p * a.half);
+        const double ang = (double)p * pow(a.theta, -2.0 * (double)i / (double)a.head_dim);
+        a.cos_t[idx] = (float)cos(ang);
+        a.sin_t[idx] = (float)sin(ang);
+    }
+}
+
+}  // namespace kcr
+
+using namespace kcr;
+
+extern "C" int kcr_rope_kvstore(const void* q, int64_t q_tok_stride, int64_t q_head_stride,
+                                const void* k, int64_t k_tok_stride, int64_t k_head_stride,
+                                const void* v, int64_t v_tok_stride, int64_t v_head_stride,
+                                void* q_out, const int64_t* positions, const float* cos_tab,
+                                const float* sin_tab, int64_t max_pos, void* kv_cache,
+                                const int64_t* slot_mapping, int64_t T, int n_head, int n_kv_head,
+                                int head_dim, int block_size, int64_t num_blocks, int dtype,
+                                void* stream) {
+    if (!dtype_ok(dtype)) return KCR_ERR_DTYPE;
+    if (n_kv_head < 1 || n_head < 1) return KCR_ERR_SHAPE;
+    if (n_head % n_kv_head != 0) return KCR_ERR_HEADS;
+    const size_t es = dtype_size(dtype);
+    const int vec = (int)(16 / es);
+    if (head_dim < 2 || head_dim % 2 != 0 || (head_dim / 2) % vec != 0 ||
+        head_dim > KCR_ROPE_MAX_HEAD_DIM)
+        return KCR_ERR_SHAPE;
+    if (T < 0 || block_size < 1 || num_blocks < 0 || max_pos < 1) return KCR_ERR_SHAPE;
+    if (T * (int64_t)n_kv_head >= (int64_t(1) << 31)) return KCR_ERR_SHAPE;
+    if (T == 0) return KCR_OK;
+    if (!q || !k || !v || !q_out || !positions || !cos_tab || !sin_tab || !slot_mapping)
+        return KCR_ERR_NULL;
+    if (!kv_cache && num_blocks > 0) return KCR_ERR_NULL;
+    if (q_head_stride < head_dim || k_head_stride < head_dim || v_head_stride < head_dim ||
+        q_tok_stride < 0 || k_tok_stride < 0 || v_tok_stride < 0)
+        return KCR_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q_out) ||
+        !aligned16(cos_tab) || !aligned16(sin_tab) || (kv_cache && !aligned16(kv_cache)) ||
+        !stride_ok(q_tok_stride, es) || !stride_ok(q_head_stride, es) ||
+        !stride_ok(k_tok_stride, es) || !stride_ok(k_head_stride, es) ||
+        !stride_ok(v_tok_stride, es) || !stride_ok(v_head_stride, es) ||
+        (reinterpret_cast<uintptr_t>(positions) & 7u) || (reinterpret_cast<uintptr_t>(slot_mapping) & 7u))
+        return KCR_ERR_ALIGN;
+
+    const int64_t n_slots = num_blocks * (int64_t)block_size;
+    const Span sq = span3d(q, T, q_tok_stride, n_head, q_head_stride, head_dim, es);
+    const Span sk = span3d(k, T, k_tok_stride, n_kv_head, k_head_stride, head_dim, es);
+    const Span sv = span3d(v, T, v_tok_stride, n_kv_head, v_head_stride, head_dim, es);
+    const Span so = span2d(q_out, 1, 0, T * n_head * (int64_t)head_dim, es);
+    const Span sc = span2d(kv_cache, 1, 0, 2 * n_slots * n_kv_head * (int64_t)head_dim, es);
+    const Span st = span2d(cos_tab, 1, 0, max_pos * (head_dim / 2), 4);
+    const Span ss = span2d(sin_tab, 1, 0, max_pos * (head_dim / 2), 4);
+    const bool q_contig = q_head_stride == head_dim && q_tok_stride == (int64_t)n_head * head_dim;
+    const bool in_place = q == q_out && q_contig;
+    if ((!in_place && overlap(so, sq)) || overlap(so, sk) || overlap(so, sv) || overlap(so, sc) ||
+        overlap(so, st) || overlap(so, ss) || overlap(sc, sq) || overlap(sc, sk) || overlap(sc, sv) ||
+        overlap(sc, st) || overlap(sc, ss))
+        return KCR_ERR_ALIAS;
+    if (device_cus() <= 0) return KCR_ERR_DEVICE;
+
+    RopeArgs a{q, k, v, q_out, kv_cache, positions, slot_mapping, cos_tab, sin_tab,
+               q_tok_stride, q_head_stride, k_tok_stride, k_head_stride, v_tok_stride, v_head_stride,
+               max_pos, n_slots, (uint32_t)(T * n_kv_head), make_fastdiv((uint32_t)n_kv_head),
+               n_head, n_head / n_kv_head, head_dim};
+    return dtype == KCR_BF16 ? dispatch_rope<Bf16>(a, stream) : dispatch_rope<F32>(a, stream);
+}
+
+extern "C" int kcr_rope_cos_sin(float* cos_tab, float* sin_tab, int64_t max_pos, int head_dim,
+                                double theta, void* stream) {
+    if (max_pos < 0 || head_dim < 2 || head_dim % 2 != 0) return KCR_ERR_SHAPE;
+    if (max_pos == 0) return KCR_OK;
+    if (!cos_tab || !sin_tab) return KCR_ERR_NULL;
+    if (!aligned16(cos_tab) || !aligned16(sin_tab)) return KCR_ERR_ALIGN;
+    const int half = head_dim / 2;
+    const int64_t n = max_pos * half;
+    if (overlap(span2d(cos_tab, 1, 0, n, 4), span2d(sin_tab, 1, 0, n, 4))) return KCR_ERR_ALIAS;
+    if (device_cus() <= 0) return KCR_ERR_DEVICE;
+    const TableArgs a{cos_tab, sin_tab, n, half, head_dim, theta};
+    return launch(rope_table_kernel, dim3(grid_for(n, 256, device_cus(), 8)), dim3(256), stream, a);
+}

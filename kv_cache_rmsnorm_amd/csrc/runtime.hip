@@ -1,0 +1,121 @@
+// runtime.hip -- library-wide pieces of the C ABI: device query, the plain
+// copy kernel used as the bandwidth ceiling, status strings and the host
+// self-test.
+#include <atomic>
+
+#include "kcr_device.h"
+#include "kcr_host.h"
+
+int kcr_norm_shape_selftest();  // rmsnorm.hip
+
+namespace kcr {
+
+static std::atomic<int> g_cus[kMaxDevices];
+
+TimingEvents& next_launch_events() {
+    static thread_local TimingEvents ev;
+    return ev;
+}
+
+int device_cus() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int n = g_cus[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        return 0;
+    g_cus[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+struct CopyArgs {
+    u32x4* dst;
+    const u32x4* src;
+    int64_t n;  // 16-byte vectors
+};
+
+// Grid-stride copy, four 16-byte loads in flight per lane before the stores.
+__global__ __launch_bounds__(256) void copy_kernel(const CopyArgs a) {
+    constexpr int U = 4;
+    const int64_t step = (int64_t)gridDim.x * 256 * U;
+    for (int64_t base = (int64_t)blockIdx.x * 256 * U + threadIdx.x; base < a.n; base += step) {
+        u32x4 v[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+            if (base + k * 256 < a.n) v[k] = a.src[base + k * 256];
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+            if (base + k * 256 < a.n) a.dst[base + k * 256] = v[k];
+    }
+}
+
+}  // namespace kcr
+
+using namespace kcr;
+
+extern "C" int kcr_copy(void* dst, const void* src, int64_t bytes, void* stream) {
+    if (bytes < 0 || bytes % 16 != 0) return KCR_ERR_SHAPE;
+    if (bytes == 0) return KCR_OK;
+    if (!dst || !src) return KCR_ERR_NULL;
+    if (!aligned16(dst) || !aligned16(src)) return KCR_ERR_ALIGN;
+    if (overlap(span2d(dst, 1, 0, bytes, 1), span2d(src, 1, 0, bytes, 1))) return KCR_ERR_ALIAS;
+    const int cus = device_cus();
+    if (cus <= 0) return KCR_ERR_DEVICE;
+    CopyArgs a{static_cast<u32x4*>(dst), static_cast<const u32x4*>(src), bytes / 16};
+    return launch(copy_kernel, dim3(grid_for(a.n, 256 * 4, cus, 8)), dim3(256), stream, a);
+}
+
+extern "C" int kcr_device_cus(void) { return device_cus(); }
+
+extern "C" int kcr_time_next_launch(void* start_event, void* stop_event) {
+    TimingEvents& ev = next_launch_events();
+    ev.start = static_cast<hipEvent_t>(start_event);
+    ev.stop = static_cast<hipEvent_t>(stop_event);
+    return KCR_OK;
+}
+
+extern "C" const char* kcr_strerror(int status) {
+    switch (status) {
+        case KCR_OK: return "ok";
+        case KCR_ERR_NULL: return "a required pointer is NULL";
+        case KCR_ERR_SHAPE: return "a size is out of range";
+        case KCR_ERR_DTYPE: return "unknown dtype";
+        case KCR_ERR_ALIGN: return "pointer or stride breaks 16-byte alignment";
+        case KCR_ERR_HEADS: return "n_head is not a multiple of n_kv_head";
+        case KCR_ERR_ALIAS: return "an output overlaps an input";
+        case KCR_ERR_LAUNCH: return "kernel launch failed";
+        case KCR_ERR_DEVICE: return "no usable HIP device";
+        default: return "unknown status";
+    }
+}
+
+extern "C" const char* kcr_version(void) { return "kcr 0.1.0 (gfx950)"; }
+
+extern "C" int kcr_selftest_host(void) {
+    // 1: fast division, exhaustive over small divisors and numerators.
+    for (uint32_t d = 1; d <= 2048; ++d) {
+        const FastDiv f = make_fastdiv(d);
+        for (uint32_t n = 0; n < 8192; ++n)
+            if (fastdiv(n, f) != n / d) return 1;
+    }
+    // 2: fast division, sampled over the whole range n < 2^31 (a 64-bit LCG).
+    uint64_t s = 0x9E3779B97F4A7C15ull;
+    for (int i = 0; i < 200000; ++i) {
+        s = s * 6364136223846793005ull + 1442695040888963407ull;
+        const uint32_t d = (uint32_t)(s >> 40) % 0x7FFFFFFFu + 1u;
+        s = s * 6364136223846793005ull + 1442695040888963407ull;
+        const uint32_t n = (uint32_t)(s >> 33);
+        const FastDiv f = make_fastdiv(d);
+        if (fastdiv(n, f) != n / d) return 2;
+        const uint32_t near = (n / d) * d;  // a multiple of d and its neighbour
+        if (fastdiv(near, f) != near / d || (near > 0 && fastdiv(near - 1, f) != (near - 1) / d)) return 2;
+    }
+    // 3: every RMSNorm width maps to a register shape that covers it.
+    if (kcr_norm_shape_selftest() != 0) return 3;
+    // 4: interleaved halves of a fused buffer are element-disjoint; a shifted
+    //    copy of the same rows is not.
+    alignas(16) static char buf[64];
+    if (!rows_disjoint(buf, 8, buf + 8, 8, 4, 4, 2)) return 4;
+    if (rows_disjoint(buf, 8, buf + 2, 8, 4, 4, 2)) return 4;
+    return 0;
+}

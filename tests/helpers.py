@@ -15,6 +15,9 @@ from __future__ import annotations
 import numpy as np
 import torch
 
+import oracle
+import workloads
+
 BF16_ATOL = 1e-2
 BF16_ULPS = 2.0
 F32_RTOL = 1e-5
@@ -75,3 +78,60 @@ def assert_bits_equal(a: torch.Tensor, b: torch.Tensor, what: str = ""):
     if bool(ne.any()):
         idx = ne.nonzero()[:5].tolist()
         raise AssertionError(f"{what}: {int(ne.sum())} elements differ bitwise, first at {idx}")
+
+
+# ------------------------------------------------------- RoPE + KV store
+def dev(t):
+    return t.to("cuda")
+
+
+def gpu_qkv(wl):
+    """Device q/k/v: narrow views of one fused device QKV buffer when the
+    workload has one, else contiguous copies."""
+    if "qkv" in wl:
+        return workloads.qkv_views(dev(wl["qkv"]), wl["hq"], wl["hkv"], wl["dh"])
+    return dev(wl["q"]), dev(wl["k"]), dev(wl["v"])
+
+
+def assert_rope_close(got, ref, dt, what):
+    """bf16: the common rule. fp32: |got - ref| <= 1e-5 * the norm of the
+    rotation pair (i, i + d/2), which the rotation preserves; a relative
+    bound per element would be meaningless where x_i c - x_{i+d/2} s
+    cancels."""
+    if dt == torch.bfloat16:
+        assert_close(got, ref, dt, what)
+        return
+    half = ref.shape[-1] // 2
+    pn = np.sqrt(ref[..., :half] ** 2 + ref[..., half:] ** 2)
+    scale = np.concatenate([pn, pn], axis=-1)
+    err = np.abs(got - ref)
+    bad = err > np.maximum(1e-5 * scale, 1.2e-38)
+    assert not bad.any(), f"{what}: {int(bad.sum())} outside 1e-5 of the pair norm, max {err.max()}"
+
+
+def check_rope(q, k, v, positions, cache0, slots, theta, q_gpu, cache_gpu, dt, what):
+    """q_out within tolerance; cache: V rows and untouched bytes bit-exact,
+    K rows within tolerance."""
+    cache_ref = np_bits(cache0).copy()
+    q_rot, k_rot = oracle.rope_kvstore(np_bits(q), np_bits(k), np_bits(v), positions.numpy(), theta,
+                                       cache_ref, slots.numpy(), block_size=cache0.shape[2])
+    assert_rope_close(q_gpu.double().numpy(), q_rot, dt, f"{what}: q_out")
+    got = np_bits(cache_gpu)
+    nb, bs, hkv, d = cache0.shape[1:]
+    live = slots.numpy()
+    live = live[(live >= 0) & (live < nb * bs)]
+    g_flat, r_flat = got.reshape(2, nb * bs, hkv, d), cache_ref.reshape(2, nb * bs, hkv, d)
+    # everything except the K rows of live slots: bit-exact (V rows, untouched sentinel)
+    mask = np.ones((nb * bs,), dtype=bool)
+    mask[live] = False
+    assert np.array_equal(g_flat[1].view(np.uint8), r_flat[1].view(np.uint8)), f"{what}: V half"
+    assert np.array_equal(g_flat[0][mask].view(np.uint8), r_flat[0][mask].view(np.uint8)), \
+        f"{what}: untouched K slots"
+    # K rows of live slots against the fp64 rotation
+    tok = {int(s): t for t, s in enumerate(slots.numpy()) if 0 <= s < nb * bs}
+    order = np.array([tok[int(s)] for s in live], dtype=np.int64)
+    kg = torch.from_numpy(g_flat[0][live].view(np.int16 if dt == torch.bfloat16 else np.int32).copy())
+    kg = kg.view(dt).double().numpy()
+    assert_rope_close(kg, k_rot[order], dt, f"{what}: K rows")
+
+

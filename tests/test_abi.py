@@ -1,0 +1,159 @@
+"""C ABI of libkcr.so on the CPU: the library loads, exports every entry
+point include/kcr.h declares, passes its host self-test, and rejects bad
+arguments with the documented status before touching any device. No kernel
+is launched here (fake, never-dereferenced addresses are used where the
+validation only inspects pointer values)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kcr.h")
+LIB = os.path.join(ROOT, "kv_cache_rmsnorm_amd", "libkcr.so")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, HEADS, ALIAS, LAUNCH, DEVICE = 0, -1, -2, -3, -4, -5, -6, -7, -8
+BF16, F32 = 0, 1
+A = 1 << 20  # fake 16-byte-aligned device addresses, never dereferenced
+
+
+def declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(kcr_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libkcr.so is not built (python kv_cache_rmsnorm_amd/build.py)")
+    L = ctypes.CDLL(LIB)
+    P, I64, I, F, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_double
+    L.kcr_rmsnorm.argtypes = [P, I64, P, P, I64, I64, I64, F, I, P]
+    L.kcr_add_rmsnorm.argtypes = [P, I64, P, I64, P, P, I64, I64, I64, F, I, P]
+    L.kcr_rope_kvstore.argtypes = [P, I64, I64, P, I64, I64, P, I64, I64, P, P, P, P, I64, P, P,
+                                   I64, I, I, I, I, I64, I, P]
+    L.kcr_rope_cos_sin.argtypes = [P, P, I64, I, D, P]
+    L.kcr_swiglu.argtypes = [P, I64, P, I64, P, I64, I64, I64, I, P]
+    L.kcr_copy.argtypes = [P, P, I64, P]
+    L.kcr_strerror.argtypes = [I]
+    L.kcr_strerror.restype = ctypes.c_char_p
+    L.kcr_version.restype = ctypes.c_char_p
+    return L
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared()
+    assert {"kcr_rmsnorm", "kcr_add_rmsnorm", "kcr_rope_kvstore", "kcr_swiglu"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_host_selftest(lib):
+    assert lib.kcr_selftest_host() == 0
+
+
+def test_strings(lib):
+    assert lib.kcr_version().startswith(b"kcr")
+    for code in (OK, NULL, SHAPE, DTYPE, ALIGN, HEADS, ALIAS, LAUNCH, DEVICE):
+        assert lib.kcr_strerror(code) and lib.kcr_strerror(code) != b"unknown status"
+
+
+def test_rmsnorm_validation(lib):
+    f = lib.kcr_rmsnorm
+    assert f(A, 1536, A * 2, A * 3, 1536, 4, 1536, 1e-6, 7, None) == DTYPE
+    assert f(A, 1536, A * 2, A * 3, 1536, -1, 1536, 1e-6, BF16, None) == SHAPE
+    assert f(A, 1536, A * 2, A * 3, 1536, 4, 0, 1e-6, BF16, None) == SHAPE
+    assert f(A, 40000, A * 2, A * 3, 40000, 4, 40000, 1e-6, BF16, None) == SHAPE
+    assert f(A, 20000, A * 2, A * 3, 20000, 4, 20000, 1e-6, F32, None) == SHAPE
+    assert f(None, 1536, None, None, 1536, 0, 1536, 1e-6, BF16, None) == OK  # no work, no launch
+    assert f(None, 1536, A * 2, A * 3, 1536, 4, 1536, 1e-6, BF16, None) == NULL
+    assert f(A + 1, 1536, A * 2, A * 3, 1536, 4, 1536, 1e-6, BF16, None) == ALIGN
+    assert f(A + 2, 1536, A * 2, A * 3, 1536, 4, 1536, 1e-6, F32, None) == ALIGN
+    # 2-byte aligned bf16 rows with an odd stride are accepted (element access)
+    assert f(A + 2, 1537, A * 2, A * 3, 1536, 4, 1536, 1e-6, BF16, None) in (DEVICE, OK)
+    assert f(A, 1000, A * 2, A * 3, 1536, 4, 1536, 1e-6, BF16, None) == SHAPE  # stride < d
+    # y overlapping x (not exactly in place) is refused; exactly in place is allowed
+    assert f(A, 1536, A * 64, A + 3072, 1536, 4, 1536, 1e-6, BF16, None) == ALIAS
+    assert f(A, 1536, A * 64, A, 1536, 4, 1536, 1e-6, BF16, None) in (DEVICE, OK)
+
+
+def test_add_rmsnorm_validation(lib):
+    f = lib.kcr_add_rmsnorm
+    assert f(A, 1536, A * 2, 1536, A * 3, A * 4, 1536, 4, 1536, 1e-6, 9, None) == DTYPE
+    assert f(None, 1536, A * 2, 1536, A * 3, A * 4, 1536, 4, 1536, 1e-6, BF16, None) == NULL
+    assert f(A, 1536, None, 1536, A * 3, A * 4, 1536, 4, 1536, 1e-6, BF16, None) == NULL
+    assert f(A, 1536, A * 2 + 1, 1536, A * 3, A * 4, 1536, 4, 1536, 1e-6, BF16, None) == ALIGN
+    assert f(A, 1536, A * 2, 1536, A * 3, A, 1536, 4, 1536, 1e-6, BF16, None) == ALIAS  # y == x
+    assert f(A, 1536, A, 1536, A * 3, A * 4, 1536, 4, 1536, 1e-6, BF16, None) == ALIAS  # delta == x
+
+
+def _rope(lib, **kw):
+    args = dict(q=A, qts=16 * 128, qhs=128, k=A + 12 * 128 * 2, kts=16 * 128, khs=128,
+                v=A + 14 * 128 * 2, vts=16 * 128, vhs=128, qo=A * 8, pos=A * 9, cos=A * 10,
+                sin=A * 11, max_pos=4096, cache=A * 16, slots=A * 12, T=4, hq=12, hkv=2, hd=128,
+                bs=16, nb=64, dt=BF16)
+    args.update(kw)
+    a = args
+    return lib.kcr_rope_kvstore(a["q"], a["qts"], a["qhs"], a["k"], a["kts"], a["khs"], a["v"],
+                                a["vts"], a["vhs"], a["qo"], a["pos"], a["cos"], a["sin"],
+                                a["max_pos"], a["cache"], a["slots"], a["T"], a["hq"], a["hkv"],
+                                a["hd"], a["bs"], a["nb"], a["dt"], None)
+
+
+def test_rope_validation(lib):
+    assert _rope(lib, dt=5) == DTYPE
+    assert _rope(lib, hq=12, hkv=5) == HEADS
+    assert _rope(lib, hd=127) == SHAPE
+    assert _rope(lib, hd=24) == SHAPE            # half head (12) not a multiple of 8 bf16
+    assert _rope(lib, hd=24, dt=F32) in (DEVICE, OK)  # 12 is a multiple of 4 fp32
+    assert _rope(lib, hd=1024) == SHAPE
+    assert _rope(lib, bs=0) == SHAPE
+    assert _rope(lib, max_pos=0) == SHAPE
+    assert _rope(lib, T=0, q=None, k=None, v=None) == OK
+    assert _rope(lib, slots=None) == NULL
+    assert _rope(lib, cos=A * 10 + 4) == ALIGN
+    assert _rope(lib, qhs=129) == ALIGN
+    assert _rope(lib, pos=A * 9 + 4) == ALIGN
+    assert _rope(lib, qo=A + 64) == ALIAS        # q_out inside q's fused buffer
+    assert _rope(lib, cache=A) == ALIAS          # cache over the inputs
+    # contiguous q may be rotated in place
+    assert _rope(lib, qts=12 * 128, k=A * 3, kts=2 * 128, v=A * 4, vts=2 * 128,
+                 qo=A) in (DEVICE, OK)
+
+
+def test_swiglu_validation(lib):
+    f = lib.kcr_swiglu
+    I = 8960
+    assert f(A, 2 * I, A + 2 * I, 2 * I, A * 64, I, 4, I, 3, None) == DTYPE
+    assert f(A, 2 * I, A + 2 * I, 2 * I, A * 64, I, 4, 0, BF16, None) == SHAPE
+    assert f(A, 2 * I, A + 2 * I, 2 * I, A * 64, I, 1 << 30, I, BF16, None) == SHAPE  # > 2^31 vectors
+    assert f(A, 2 * I, A + 2 * I, 2 * I, None, I, 4, I, BF16, None) == NULL
+    assert f(A, 2 * I, A + 2 * I + 1, 2 * I, A * 64, I, 4, I, BF16, None) == ALIGN
+    # output into the gate half of the fused buffer: exact, allowed
+    assert f(A, 2 * I, A + 2 * I, 2 * I, A, 2 * I, 4, I, BF16, None) in (DEVICE, OK)
+    # output overlapping the up half with a shifted row: refused
+    assert f(A, 2 * I, A + 2 * I, 2 * I, A + 16, 2 * I, 4, I, BF16, None) == ALIAS
+    # fused halves as inputs, separate output: fine
+    assert f(A, 2 * I, A + 2 * I, 2 * I, A * 64, I, 4, I, BF16, None) in (DEVICE, OK)
+
+
+def test_copy_validation(lib):
+    assert lib.kcr_copy(A * 2, A, 17, None) == SHAPE
+    assert lib.kcr_copy(A * 2, A + 8, 32, None) == ALIGN
+    assert lib.kcr_copy(A + 16, A, 64, None) == ALIAS
+    assert lib.kcr_copy(None, None, 0, None) == OK
+
+
+def test_binding_refuses_missing_library(tmp_path):
+    # The binding must fail loudly rather than fall back when the HIP library
+    # is absent: load its source against an empty directory.
+    import importlib.util
+    src = os.path.join(ROOT, "kv_cache_rmsnorm_amd", "__init__.py")
+    fake_pkg = tmp_path / "kcr_missing"
+    fake_pkg.mkdir()
+    (fake_pkg / "__init__.py").write_text(open(src).read())
+    spec = importlib.util.spec_from_file_location("kcr_missing", fake_pkg / "__init__.py")
+    mod = importlib.util.module_from_spec(spec)
+    with pytest.raises(ImportError):
+        spec.loader.exec_module(mod)

@@ -1,0 +1,189 @@
+"""GPU parity on the five workloads at their full sizes, and at the large
+per-kernel shapes the benchmark times (same entry points, same launch
+configuration), against the CPU fp64 oracle:
+
+  1 batch-1 Qwen2.5-1.5B decode token (rmsnorm, rope_kvstore, swiglu)
+  2 RMSNorm 512 x 2176, fp32 and bf16, 1% outlier rows x100
+  3 prefill RoPE + paged store, 8 sequences of 128..2048 tokens
+  4 SwiGLU of a fused gate_up [8192, 2 x 8960]
+  5 the 28-layer batch-256 decode chain, replayed from a captured HIP graph
+
+At the large shapes the oracle checks sampled rows/tokens one by one and
+whole-tensor properties cover the rest (residual and V bit-exact, untouched
+cache slots still hold the sentinel)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from helpers import assert_close, assert_rope_close, check_rope, gpu_qkv, np_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kcr():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import kv_cache_rmsnorm_amd as k
+    return k
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def f32eps(e):
+    return float(np.float32(e))
+
+
+def test_config1_decode_token(kcr):
+    say("config 1: batch-1 decode token")
+    wl = workloads.decode_token(seed=0)
+    dev = torch.device("cuda")
+    y = kcr.rmsnorm(wl["x"].to(dev), wl["w"].to(dev), wl["eps"])
+    assert_close(y.cpu().double().numpy(),
+                 oracle.rmsnorm(np_bits(wl["x"]), np_bits(wl["w"]), f32eps(wl["eps"])),
+                 torch.bfloat16, "rmsnorm [1,1536]")
+    cos, sin = kcr.rope_cos_sin(wl["max_pos"], 128, wl["theta"])
+    cache = wl["cache"].to(dev)
+    qo = kcr.rope_kvstore(*gpu_qkv(wl), wl["positions"].to(dev), cos, sin, cache,
+                          wl["slot_mapping"].to(dev))
+    check_rope(wl["q"], wl["k"], wl["v"], wl["positions"], wl["cache"], wl["slot_mapping"],
+               wl["theta"], qo.cpu(), cache.cpu(), torch.bfloat16, "config 1 rope")
+    act = kcr.swiglu(wl["gate"].to(dev), wl["up"].to(dev))
+    assert_close(act.cpu().double().numpy(), oracle.swiglu(np_bits(wl["gate"]), np_bits(wl["up"])),
+                 torch.bfloat16, "swiglu [1,8960]")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_config2_rmsnorm(kcr, dt):
+    say(f"config 2: rmsnorm 512x2176 {dt}")
+    wl = workloads.rmsnorm_rows(rows=512, d=2176, dtype=dt, seed=0)
+    y = kcr.rmsnorm(wl["x"].cuda(), wl["w"].cuda(), wl["eps"])
+    ref = oracle.rmsnorm(np_bits(wl["x"]), np_bits(wl["w"]), f32eps(wl["eps"]))
+    assert_close(y.cpu().double().numpy(), ref, workloads.as_dtype(dt), "config 2")
+
+
+def test_config3_prefill(kcr):
+    say("config 3: prefill rope + paged store, 8 seqs")
+    wl = workloads.prefill(n_seqs=8, dtype="bf16", seed=0)
+    assert 8 * 128 <= wl["qkv"].shape[0] <= 8 * 2048
+    cos, sin = kcr.rope_cos_sin(wl["max_pos"], wl["dh"], wl["theta"])
+    cache = wl["cache"].cuda()
+    qo = kcr.rope_kvstore(*gpu_qkv(wl), wl["positions"].cuda(), cos, sin, cache,
+                          wl["slot_mapping"].cuda())
+    check_rope(wl["q"], wl["k"], wl["v"], wl["positions"], wl["cache"], wl["slot_mapping"],
+               wl["theta"], qo.cpu(), cache.cpu(), torch.bfloat16, "config 3")
+    # round trip: gathering each sequence through its block table returns V
+    c = cache.cpu()
+    off = 0
+    for L, bt in zip(wl["layout"].lens, wl["layout"].block_tables):
+        got = oracle.paged_gather(np_bits(c), 1, bt.numpy(), L)
+        assert np.array_equal(got, np.ascontiguousarray(np_bits(wl["v"][off:off + L])))
+        off += L
+
+
+def test_config4_swiglu(kcr):
+    say("config 4: swiglu gate_up [8192, 17920]")
+    wl = workloads.swiglu_fused(rows=8192, inter=8960, dtype="bf16", seed=0)
+    out = kcr.swiglu_fused(wl["gate_up"].cuda())
+    ref = oracle.swiglu(np_bits(wl["gate"]), np_bits(wl["up"]))
+    assert_close(out.cpu().double().numpy(), ref, torch.bfloat16, "config 4")
+
+
+def test_config5_decode_chain_graph(kcr):
+    """The benchmark's own step (DecodeChain, HIP graph replay), all 28
+    layers at batch 256, against the oracle run layer by layer."""
+    from kv_cache_rmsnorm_amd.chain import DecodeChain
+    say("config 5: 28-layer decode chain, graph replay")
+    wl = workloads.decode_chain(seed=0)
+    chain = DecodeChain(wl, "cuda", sentinel_cache=True)
+    chain.capture()           # runs one eager warm-up step, then captures
+    for L in chain.layers:    # reset the state the warm-up step changed
+        L["cache"].view(torch.int16).fill_(-1)
+    chain.reset_residual()
+    torch.cuda.synchronize()
+    chain.step_graph()
+    torch.cuda.synchronize()
+
+    eps = f32eps(wl["eps"])
+    hq, hkv, dh, inter = wl["hq"], wl["hkv"], wl["dh"], wl["inter"]
+    h = np_bits(wl["h"]).copy()
+    pos, slots = wl["positions"].numpy(), wl["slot_mapping"].numpy()
+    n_slots = wl["num_blocks"] * wl["block_size"]
+    for i, (lw, L) in enumerate(zip(wl["layers"], chain.layers)):
+        h, y_attn = oracle.add_rmsnorm(h, np_bits(lw["d_attn"]), np_bits(lw["w_attn"]), eps)
+        q, k, v = workloads.qkv_views(lw["qkv"], hq, hkv, dh)
+        q_rot, k_rot = oracle.rope_kvstore(np_bits(q), np_bits(k), np_bits(v), pos, wl["theta"],
+                                           None, None)
+        h, y_mlp = oracle.add_rmsnorm(h, np_bits(lw["d_mlp"]), np_bits(lw["w_mlp"]), eps)
+        act = oracle.swiglu(np_bits(lw["gate_up"][:, :inter]), np_bits(lw["gate_up"][:, inter:]))
+        assert_close(L["y_attn"].cpu().double().numpy(), y_attn, torch.bfloat16, f"layer {i} y_attn")
+        assert_close(L["y_mlp"].cpu().double().numpy(), y_mlp, torch.bfloat16, f"layer {i} y_mlp")
+        assert_rope_close(L["q_out"].cpu().double().numpy(), q_rot, torch.bfloat16, f"layer {i} q_out")
+        assert_close(L["act"].cpu().double().numpy(), act, torch.bfloat16, f"layer {i} act")
+        # cache: the 256 named slots hold K_rot and V; every other slot the sentinel
+        flat = L["cache"].view(2, n_slots, hkv, dh)
+        s_dev = chain.slot_mapping
+        k_got = flat[0][s_dev].cpu().double().numpy()
+        assert_rope_close(k_got, k_rot, torch.bfloat16, f"layer {i} K slots")
+        assert torch.equal(flat[1][s_dev].view(torch.int16).cpu(), v.contiguous().view(torch.int16))
+        untouched = int((L["cache"].view(torch.int16) == -1).sum())
+        assert untouched == L["cache"].numel() - 2 * len(slots) * hkv * dh, f"layer {i} stray writes"
+    # the residual after 56 fused adds is bit-exact
+    assert np.array_equal(np_bits(chain.h.cpu()), h), "residual stream after the step"
+
+
+def test_large_rmsnorm_sampled(kcr):
+    R, d = 131072, 2176
+    for dt in ("bf16", "f32"):
+        say(f"large rmsnorm [{R}, {d}] {dt}, sampled rows")
+        wl = workloads.rmsnorm_rows(rows=R, d=d, dtype=dt, seed=0)
+        y = kcr.rmsnorm(wl["x"].cuda(), wl["w"].cuda(), wl["eps"]).cpu()
+        rng = np.random.default_rng(1)
+        rows = np.unique(np.concatenate([[0, 1, R - 1], wl["outlier_rows"].numpy()[:50],
+                                         rng.choice(R, 400, replace=False)]))
+        ref = oracle.rmsnorm(np_bits(wl["x"][rows]), np_bits(wl["w"]), f32eps(wl["eps"]))
+        assert_close(y[rows].double().numpy(), ref, workloads.as_dtype(dt), f"rows of {dt}")
+        assert bool(torch.isfinite(y).all())
+
+
+def test_large_add_rmsnorm_sampled(kcr):
+    R, d = 131072, 1536
+    say(f"large add_rmsnorm [{R}, {d}] bf16")
+    wl = workloads.add_rmsnorm_rows(R, d, dtype="bf16", seed=0)
+    x = wl["x"].cuda()
+    delta = wl["delta"].cuda()
+    y = kcr.add_rmsnorm(x, delta, wl["w"].cuda(), wl["eps"]).cpu()
+    # every row's residual: bit-exact against torch's fp32 add rounded to bf16
+    want = (wl["x"].cuda().float() + delta.float()).to(torch.bfloat16)
+    assert torch.equal(x.view(torch.int16), want.view(torch.int16))
+    rows = np.unique(np.concatenate([[0, R - 1], np.random.default_rng(2).choice(R, 400, replace=False)]))
+    x_ref, y_ref = oracle.add_rmsnorm(np_bits(wl["x"][rows]), np_bits(wl["delta"][rows]),
+                                      np_bits(wl["w"]), f32eps(wl["eps"]))
+    assert np.array_equal(np_bits(x[rows].cpu()), x_ref)
+    assert_close(y[rows].double().numpy(), y_ref, torch.bfloat16, "sampled rows")
+
+
+def test_large_rope_sampled(kcr):
+    say("large prefill rope + store, 64 seqs, sampled tokens")
+    wl = workloads.prefill(n_seqs=64, dtype="bf16", seed=0)
+    T = wl["qkv"].shape[0]
+    cos, sin = kcr.rope_cos_sin(wl["max_pos"], wl["dh"], wl["theta"])
+    cache = wl["cache"].cuda()
+    q, k, v = gpu_qkv(wl)
+    slots = wl["slot_mapping"].cuda()
+    qo = kcr.rope_kvstore(q, k, v, wl["positions"].cuda(), cos, sin, cache, slots)
+    hkv, dh = wl["hkv"], wl["dh"]
+    flat = cache.view(2, -1, hkv, dh)
+    # V of every token bit-exact at its slot; all other slots untouched
+    assert torch.equal(flat[1][slots].view(torch.int16), v.view(torch.int16))
+    assert int((cache.view(torch.int16) == -1).sum()) == cache.numel() - 2 * T * hkv * dh
+    toks = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(3).choice(T, 500, replace=False)]))
+    q_rot, k_rot = oracle.rope_kvstore(np_bits(wl["q"][toks]), np_bits(wl["k"][toks]),
+                                       np_bits(wl["v"][toks]), wl["positions"].numpy()[toks],
+                                       wl["theta"], None, None)
+    assert_rope_close(qo.cpu()[toks].double().numpy(), q_rot, torch.bfloat16, "sampled q_out")
+    k_got = flat[0][slots[torch.from_numpy(toks).cuda()]].cpu().double().numpy()
+    assert_rope_close(k_got, k_rot, torch.bfloat16, "sampled K slots")

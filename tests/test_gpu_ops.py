@@ -1,0 +1,270 @@
+"""GPU parity of each op against the CPU fp64 oracle, element by element, on
+seeded inputs sized to span several workgroups and ragged tails, plus the
+edge cases: widths 1..32768 including primes and 16-byte-misaligned tails,
+strided views, in-place forms, padding slots, out-of-range indices, empty
+calls and non-default streams.
+
+Tolerances (written out in helpers.py): bf16 within 2 ulp or 1e-2, fp32
+within 1e-5 relative; the updated residual, V and every untouched cache byte
+bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from helpers import (assert_bits_equal, assert_close, check_rope, gpu_qkv, np_bits,
+                     tol_violations)
+
+pytestmark = pytest.mark.gpu
+
+DTS = [torch.bfloat16, torch.float32]
+DT_ID = {torch.bfloat16: "bf16", torch.float32: "f32"}
+
+
+@pytest.fixture(scope="module")
+def kcr():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import kv_cache_rmsnorm_amd as k
+    return k
+
+
+from helpers import dev
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------------ RMSNorm
+NORM_WIDTHS = [1, 7, 8, 9, 63, 64, 65, 127, 511, 512, 513, 1000, 1536, 2048, 2176, 3001, 4095,
+               4096, 4097, 8191, 8192, 8193, 12289, 16384]
+
+
+@pytest.mark.parametrize("dt", DTS, ids=DT_ID.get)
+@pytest.mark.parametrize("d", NORM_WIDTHS)
+def test_rmsnorm_widths(kcr, dt, d):
+    rows = 37
+    say(f"rmsnorm dt={dt} d={d} rows={rows}")
+    wl = workloads.rmsnorm_rows(rows=rows, d=d, dtype=dt, seed=d)
+    y = kcr.rmsnorm(dev(wl["x"]), dev(wl["w"]), wl["eps"])
+    ref = oracle.rmsnorm(np_bits(wl["x"]), np_bits(wl["w"]), float(np.float32(wl["eps"])))
+    assert_close(y.cpu().double().numpy(), ref, dt, f"rmsnorm d={d}")
+
+
+@pytest.mark.parametrize("d", [20000, 24577, 32768])
+def test_rmsnorm_widest_bf16(kcr, d):
+    say(f"rmsnorm bf16 wide d={d}")
+    wl = workloads.rmsnorm_rows(rows=9, d=d, dtype="bf16", seed=d)
+    y = kcr.rmsnorm(dev(wl["x"]), dev(wl["w"]), wl["eps"])
+    ref = oracle.rmsnorm(np_bits(wl["x"]), np_bits(wl["w"]), float(np.float32(wl["eps"])))
+    assert_close(y.cpu().double().numpy(), ref, torch.bfloat16, f"rmsnorm d={d}")
+
+
+@pytest.mark.parametrize("dt", DTS, ids=DT_ID.get)
+def test_rmsnorm_many_rows_grid_stride(kcr, dt):
+    # more rows than the resident grid holds: every workgroup loops
+    rows, d = 40000, 200
+    say(f"rmsnorm grid-stride rows={rows} dt={dt}")
+    wl = workloads.rmsnorm_rows(rows=rows, d=d, dtype=dt, seed=5)
+    y = kcr.rmsnorm(dev(wl["x"]), dev(wl["w"]), wl["eps"])
+    ref = oracle.rmsnorm(np_bits(wl["x"]), np_bits(wl["w"]), float(np.float32(wl["eps"])))
+    assert_close(y.cpu().double().numpy(), ref, dt, "rmsnorm many rows")
+
+
+def test_rmsnorm_strided_and_in_place(kcr):
+    say("rmsnorm strided + in place")
+    wl = workloads.rmsnorm_rows(rows=50, d=1536 + 64, dtype="bf16", seed=7)
+    big = dev(wl["x"])
+    x = big[:, :1528]  # row stride 1600, width 1528 (ragged: 1528 = 191 vectors)
+    w = dev(wl["w"][:1528].contiguous())
+    ref = oracle.rmsnorm(np_bits(wl["x"][:, :1528]), np_bits(wl["w"][:1528].contiguous()), 1e-6)
+    y = kcr.rmsnorm(x, w, 1e-6)
+    assert_close(y.cpu().double().numpy(), ref, torch.bfloat16, "strided")
+    before = big[:, 1528:].clone()
+    kcr.rmsnorm(x, w, 1e-6, out=x)  # in place
+    assert_close(x.cpu().double().numpy(), ref, torch.bfloat16, "in place")
+    assert_bits_equal(big[:, 1528:], before, "columns past the view")
+
+
+def test_rmsnorm_outlier_rows_fp32(kcr):
+    # the 1% x100 outlier rows keep full fp32 accuracy
+    wl = workloads.rmsnorm_rows(rows=512, d=2176, dtype="f32", seed=0)
+    y = kcr.rmsnorm(dev(wl["x"]), dev(wl["w"]), wl["eps"]).cpu().double().numpy()
+    ref = oracle.rmsnorm(np_bits(wl["x"]), np_bits(wl["w"]), float(np.float32(wl["eps"])))
+    rows = wl["outlier_rows"].numpy()
+    assert len(rows) == 5
+    assert_close(y[rows], ref[rows], torch.float32, "outlier rows")
+
+
+def test_rmsnorm_empty_and_stream(kcr):
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    w = torch.ones(64, dtype=torch.bfloat16, device="cuda")
+    assert kcr.rmsnorm(x, w).shape == (0, 64)
+    wl = workloads.rmsnorm_rows(rows=300, d=1536, dtype="bf16", seed=9)
+    s = torch.cuda.Stream()
+    xs, ws = dev(wl["x"]), dev(wl["w"])
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        y = kcr.rmsnorm(xs, ws, 1e-6)
+    s.synchronize()
+    ref = oracle.rmsnorm(np_bits(wl["x"]), np_bits(wl["w"]), 1e-6)
+    assert_close(y.cpu().double().numpy(), ref, torch.bfloat16, "side stream")
+
+
+# ------------------------------------------------------------- add + RMSNorm
+@pytest.mark.parametrize("dt", DTS, ids=DT_ID.get)
+@pytest.mark.parametrize("d", [1, 9, 1536, 2176, 4097, 8960, 16384])
+def test_add_rmsnorm(kcr, dt, d):
+    rows = 33
+    say(f"add_rmsnorm dt={dt} d={d}")
+    wl = workloads.add_rmsnorm_rows(rows, d, dtype=dt, seed=d)
+    x = dev(wl["x"])
+    y = kcr.add_rmsnorm(x, dev(wl["delta"]), dev(wl["w"]), wl["eps"])
+    x_ref, y_ref = oracle.add_rmsnorm(np_bits(wl["x"]), np_bits(wl["delta"]), np_bits(wl["w"]),
+                                      float(np.float32(wl["eps"])))
+    got = np_bits(x.cpu())
+    assert np.array_equal(got.view(np.uint8), x_ref.view(np.uint8)), "residual not bit-exact"
+    assert_close(y.cpu().double().numpy(), y_ref, dt, f"add_rmsnorm y d={d}")
+
+
+def test_add_rmsnorm_strided_delta(kcr):
+    wl = workloads.add_rmsnorm_rows(300, 2048, dtype="bf16", seed=11)
+    x = dev(wl["x"][:, :1536].contiguous())
+    delta = dev(wl["delta"])[:, 256:1792]  # strided view, stride 2048
+    w = dev(wl["w"][:1536].contiguous())
+    y = kcr.add_rmsnorm(x, delta, w, 1e-6)
+    x_ref, y_ref = oracle.add_rmsnorm(np_bits(wl["x"][:, :1536].contiguous()),
+                                      np_bits(wl["delta"][:, 256:1792]),
+                                      np_bits(wl["w"][:1536].contiguous()), 1e-6)
+    assert np.array_equal(np_bits(x.cpu()), x_ref)
+    assert_close(y.cpu().double().numpy(), y_ref, torch.bfloat16, "strided delta")
+
+
+# ---------------------------------------------------------- RoPE + KV store
+def rope_case(kcr, q, k, v, positions, cache, slots, theta, max_pos, q_out=None):
+    """q, k, v on the device; runs the op and returns (q_out, cache) on the CPU."""
+    cos, sin = kcr.rope_cos_sin(max_pos, q.shape[-1], theta)
+    c = dev(cache)
+    qo = kcr.rope_kvstore(q, k, v, dev(positions), cos, sin, c, dev(slots), q_out=q_out)
+    return qo.cpu(), c.cpu()
+
+
+@pytest.mark.parametrize("dt", DTS, ids=DT_ID.get)
+def test_rope_decode_token(kcr, dt):
+    say(f"rope decode token dt={dt}")
+    wl = workloads.decode_token(dtype=dt)
+    qg, cg = rope_case(kcr, *gpu_qkv(wl), wl["positions"], wl["cache"], wl["slot_mapping"],
+                       wl["theta"], wl["max_pos"])
+    check_rope(wl["q"], wl["k"], wl["v"], wl["positions"], wl["cache"], wl["slot_mapping"],
+               wl["theta"], qg, cg, dt, "decode token")
+    # the written slot is 597 = block 37, offset 5, and nothing else changed
+    changed = (cg.view(torch.int16 if dt == torch.bfloat16 else torch.int32) != -1)
+    assert changed.any(dim=(3, 4)).nonzero().tolist() == [[0, 37, 5], [1, 37, 5]]
+
+
+@pytest.mark.parametrize("hq,hkv,dh", [(12, 2, 128), (8, 8, 64), (32, 8, 128), (16, 1, 256),
+                                       (4, 2, 16), (2, 1, 512)])
+@pytest.mark.parametrize("dt", DTS, ids=DT_ID.get)
+def test_rope_shapes(kcr, hq, hkv, dh, dt):
+    say(f"rope shapes hq={hq} hkv={hkv} dh={dh} dt={dt}")
+    wl = workloads.prefill(n_seqs=3, len_lo=1, len_hi=70, dtype=dt, seed=hq * dh, hq=hq, hkv=hkv,
+                           dh=dh, block_size=16)
+    slots = wl["slot_mapping"].clone()
+    slots[::5] = -1  # padding tokens
+    qg, cg = rope_case(kcr, *gpu_qkv(wl), wl["positions"], wl["cache"], slots, wl["theta"],
+                       wl["max_pos"])
+    check_rope(wl["q"], wl["k"], wl["v"], wl["positions"], wl["cache"], slots, wl["theta"], qg, cg,
+               dt, f"hq={hq} hkv={hkv} dh={dh}")
+
+
+def test_rope_prefill_block_size_and_in_place(kcr):
+    say("rope block_size 7, contiguous q rotated in place")
+    wl = workloads.prefill(n_seqs=4, len_lo=3, len_hi=300, dtype="bf16", seed=3, block_size=7)
+    _, k, v = gpu_qkv(wl)
+    q = dev(wl["q"].contiguous())
+    qg, cg = rope_case(kcr, q, k, v, wl["positions"], wl["cache"], wl["slot_mapping"],
+                       wl["theta"], wl["max_pos"], q_out=q)
+    check_rope(wl["q"], wl["k"], wl["v"], wl["positions"], wl["cache"], wl["slot_mapping"],
+               wl["theta"], qg, cg, torch.bfloat16, "in place, block size 7")
+
+
+def test_rope_position_zero_and_out_of_range(kcr):
+    say("rope position 0 identity; out-of-range positions and slots skipped")
+    g = workloads.gen(17)
+    T, hq, hkv, dh = 6, 12, 2, 128
+    q = workloads.randn([T, hq, dh], g).to(torch.bfloat16)
+    k = workloads.randn([T, hkv, dh], g).to(torch.bfloat16)
+    v = workloads.randn([T, hkv, dh], g).to(torch.bfloat16)
+    cache = workloads.sentinel_cache([2, 4, 16, hkv, dh], torch.bfloat16)
+    positions = torch.tensor([0, 0, 5, 99, -1, 3], dtype=torch.int64)   # max_pos 64: 99, -1 invalid
+    slots = torch.tensor([1, 63, 64, 2, 3, -7], dtype=torch.int64)      # 64 slots: 64 invalid
+    q_out = torch.full((T, hq, dh), 7.0, dtype=torch.bfloat16, device="cuda")
+    qg, cg = rope_case(kcr, dev(q), dev(k), dev(v), positions, cache, slots, 1e6, 64, q_out=q_out)
+    # position 0 is the identity (values; +0 and -0 compare equal)
+    assert torch.equal(qg[:2].float(), q[:2].float())
+    # tokens with invalid positions are skipped entirely
+    assert bool((qg[3:5] == 7.0).all())
+    cb = cg.view(torch.int16)
+    written = sorted({(b * 16 + o) for _, b, o in (cb != -1).any(dim=(3, 4)).nonzero().tolist()})
+    assert written == [1, 63]  # token 2's slot 64 is out of range, tokens 3/4 skipped, 5 padding
+    assert torch.equal(cg[0, 0, 1].float(), k[0].float()) and torch.equal(cg[1, 3, 15], v[1])
+
+
+def test_rope_table(kcr):
+    say("rope cos/sin table")
+    for max_pos, dh, theta in ((4097, 128, 1e6), (70000, 64, 1e4), (3, 2, 10.0)):
+        cos, sin = kcr.rope_cos_sin(max_pos, dh, theta)
+        c_ref, s_ref = oracle.rope_angles(max_pos, dh, theta)
+        for got, ref in ((cos, c_ref), (sin, s_ref)):
+            err = np.abs(got.cpu().double().numpy() - ref)
+            # one fp32 rounding of an fp64 value (2^-24 relative) plus fp64 angle error
+            assert np.all(err <= np.abs(ref) * 2.0 ** -24 + 1e-10), float(err.max())
+
+
+# ------------------------------------------------------------------ SwiGLU
+@pytest.mark.parametrize("dt", DTS, ids=DT_ID.get)
+@pytest.mark.parametrize("rows,cols", [(1, 1), (3, 7), (1, 8960), (5, 8961), (300, 100),
+                                       (64, 1023), (257, 4096), (1000, 17)])
+def test_swiglu(kcr, dt, rows, cols):
+    say(f"swiglu dt={dt} rows={rows} cols={cols}")
+    wl = workloads.swiglu_fused(rows=rows, inter=cols, dtype=dt, seed=rows + cols)
+    out = kcr.swiglu(dev(wl["gate"].contiguous()), dev(wl["up"].contiguous()))
+    ref = oracle.swiglu(np_bits(wl["gate"]), np_bits(wl["up"]))
+    assert_close(out.cpu().double().numpy(), ref, dt, f"swiglu {rows}x{cols}")
+
+
+@pytest.mark.parametrize("dt", DTS, ids=DT_ID.get)
+def test_swiglu_fused_halves_and_in_place(kcr, dt):
+    wl = workloads.swiglu_fused(rows=123, inter=8960, dtype=dt, seed=4)
+    gu = dev(wl["gate_up"])
+    ref = oracle.swiglu(np_bits(wl["gate"]), np_bits(wl["up"]))
+    out = kcr.swiglu_fused(gu)
+    assert_close(out.cpu().double().numpy(), ref, dt, "fused halves")
+    up_before = gu[:, 8960:].clone()
+    kcr.swiglu(gu[:, :8960], gu[:, 8960:], out=gu[:, :8960])  # into the gate half
+    assert_close(gu[:, :8960].cpu().double().numpy(), ref, dt, "in place")
+    assert_bits_equal(gu[:, 8960:], up_before, "up half untouched")
+
+
+def test_swiglu_extremes(kcr):
+    # Inside |g| <= 87 every fp32 intermediate stays normal and the relative
+    # bound holds; past the overflow of exp(-g) the result is +-0 or g * u.
+    g = torch.tensor([[-200.0, -87.0, -20.0, -1.0, -1e-30, 0.0, 1e-30, 1.0, 20.0, 87.0, 200.0,
+                       3e38, -3e38]], dtype=torch.float32)
+    u = torch.full_like(g, 0.5)
+    out = kcr.swiglu(dev(g), dev(u)).cpu().double().numpy()
+    ref = oracle.swiglu(np_bits(g), np_bits(u))
+    assert not tol_violations(out, ref, torch.float32).any(), (out, ref)
+    # between -104 and -88 the exact result is below 2e-36 and may flush to zero
+    g2 = torch.linspace(-104, -88, 64, dtype=torch.float32).reshape(1, -1)
+    out2 = kcr.swiglu(dev(g2), dev(torch.ones_like(g2))).cpu().double().numpy()
+    assert np.all(np.abs(out2) <= 2e-36) and np.all(out2 <= 0)
+
+
+# ------------------------------------------------------------------ copy
+def test_copy(kcr):
+    src = torch.randint(-2**31, 2**31 - 1, (1 << 20,), dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    kcr.copy_(dst, src)
+    assert torch.equal(dst, src)
