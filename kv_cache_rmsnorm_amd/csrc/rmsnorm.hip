@@ -12,20 +12,17 @@
 //    row, so each load instruction of a wave reads 1 KiB of consecutive
 //    bytes, and the row is read from HBM exactly once into registers (the
 //    one-pass form of the csdn "Qwen3 from scratch (4-2)" page).
-//  * WPR = 1 (one wave per row, four rows per 256-lane workgroup) up to
-//    16 vectors per lane: 8192 bf16 or 4096 fp32 columns. Wider rows use a
-//    256-lane workgroup per row (WPR = 4) and a two-slot LDS exchange of the
-//    four wave partial sums.
+//  * WPR waves share a row (1..8, chosen per width, see norm_shape), with a
+//    two-slot LDS exchange of the wave partial sums when WPR > 1.
 //  * The sum of squares is reduced in-wave with DPP and v_readlane (no LDS,
 //    no barrier when WPR = 1).
 //  * Ragged widths (1536, 2176, primes) need no power-of-two padding: only
 //    the vector that straddles the end of a row is read element by element.
 //    A row whose base is not 16-byte aligned (odd widths packed densely) is
 //    accessed element by element; the choice is uniform per row.
-//  * Grid-stride over rows with the weight held in registers for every row
-//    a group processes; the grid is capped at a few resident workgroups per
-//    CU, so large batches run as a persistent grid and batch-1 decode as a
-//    single workgroup.
+//  * One-pass grid (a workgroup per GROUPS rows) with nontemporal loads and
+//    stores: on MI355X this streams HBM 10-20% faster than a persistent
+//    grid-stride loop; the weight is read once per workgroup (from L2).
 #include "kcr_device.h"
 #include "kcr_host.h"
 
@@ -52,143 +49,188 @@ __device__ __forceinline__ void* row_ptr(void* base, int64_t row, int64_t stride
     return static_cast<typename T::storage*>(base) + row * stride;
 }
 
-template <typename T, int VPT, int WPR, bool ADD>
-__global__ __launch_bounds__(WPR == 1 ? 256 : 64 * WPR) void row_norm_kernel(const NormArgs a) {
-    constexpr int kVec = T::kVec;
+// Launch shape of the row engine: VPT 16-byte vectors per lane, WPR waves
+// per row, GROUPS rows per workgroup, nontemporal loads (NTL) and stores
+// (NTS) for the streamed rows.
+template <int VPT_, int WPR_, int GROUPS_, bool NTL_, bool NTS_>
+struct NormCfg {
+    static constexpr int VPT = VPT_, WPR = WPR_, GROUPS = GROUPS_;
+    static constexpr bool NTL = NTL_, NTS = NTS_;
+    static constexpr int BLOCK = 64 * WPR * GROUPS;
+};
+
+template <typename T, typename C, bool ADD>
+__global__ __launch_bounds__(C::BLOCK) void row_norm_kernel(const NormArgs a) {
+    constexpr int kVec = T::kVec, VPT = C::VPT, WPR = C::WPR, GROUPS = C::GROUPS;
     constexpr int LANES = 64 * WPR;
-    constexpr int GROUPS = WPR == 1 ? 4 : 1;  // row groups per workgroup
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
-    const int grp = WPR == 1 ? wave : 0;
-    const int rl = (WPR == 1 ? 0 : wave) * 64 + lane;  // lane within the row group
+    const int grp = wave / WPR;                    // row group within the workgroup
+    const int rl = (wave % WPR) * 64 + lane;       // lane within the row group
     const int64_t d = a.d;
 
-    // The weight, once per row group, in registers.
+    // The weight, once per workgroup, in registers.
     const bool vw = aligned16(a.w);
     u32x4 wr[VPT];
 #pragma unroll
     for (int j = 0; j < VPT; ++j) wr[j] = load_raw<T, false>(a.w, (int64_t)(j * LANES + rl) * kVec, d, vw);
 
-    __shared__ float part[2][WPR];
+    __shared__ float part[2][GROUPS][WPR];
     int it = 0;
-    for (int64_t row = (int64_t)blockIdx.x * GROUPS + grp; row < a.rows;
-         row += (int64_t)gridDim.x * GROUPS, ++it) {
+    // The loop bound depends only on the workgroup, so every wave reaches
+    // every barrier; `live` is uniform per row group.
+    for (int64_t base = (int64_t)blockIdx.x * GROUPS; base < a.rows;
+         base += (int64_t)gridDim.x * GROUPS, ++it) {
+        const int64_t row = base + grp;
+        const bool live = row < a.rows;
         u32x4 xr[VPT];
-        const void* xrow = row_ptr<T>(a.x, row, a.x_stride);
-        const bool vx = aligned16(xrow);  // row-uniform: vector or element access
-#pragma unroll
-        for (int j = 0; j < VPT; ++j) xr[j] = load_raw<T, false>(xrow, (int64_t)(j * LANES + rl) * kVec, d, vx);
-
-        if constexpr (ADD) {
-            const void* drow = row_ptr<T>(a.delta, row, a.delta_stride);
-            const bool vd = aligned16(drow);
-            u32x4 dr[VPT];
+        float ss = 0.0f;
+        bool vx = false;
+        if (live) {
+            const void* xrow = row_ptr<T>(a.x, row, a.x_stride);
+            vx = aligned16(xrow);  // row-uniform: vector or element access
 #pragma unroll
             for (int j = 0; j < VPT; ++j)
-                dr[j] = load_raw<T, false>(drow, (int64_t)(j * LANES + rl) * kVec, d, vd);
-            void* orow = row_ptr<T>(a.x_out, row, a.x_stride);
+                xr[j] = load_raw<T, C::NTL>(xrow, (int64_t)(j * LANES + rl) * kVec, d, vx);
+            if constexpr (ADD) {
+                const void* drow = row_ptr<T>(a.delta, row, a.delta_stride);
+                const bool vd = aligned16(drow);
+                u32x4 dr[VPT];
+#pragma unroll
+                for (int j = 0; j < VPT; ++j)
+                    dr[j] = load_raw<T, C::NTL>(drow, (int64_t)(j * LANES + rl) * kVec, d, vd);
+                void* orow = row_ptr<T>(a.x_out, row, a.x_stride);
+#pragma unroll
+                for (int j = 0; j < VPT; ++j) {
+                    float xf[kVec], df[kVec];
+                    unpack<T>(xr[j], xf);
+                    unpack<T>(dr[j], df);
+#pragma unroll
+                    for (int e = 0; e < kVec; ++e) xf[e] += df[e];
+                    xr[j] = pack<T>(xf);  // the rounded sum: stored, and normalised below
+                    store_raw<T, C::NTS>(orow, (int64_t)(j * LANES + rl) * kVec, d, xr[j], vx);
+                }
+            }
 #pragma unroll
             for (int j = 0; j < VPT; ++j) {
-                float xf[kVec], df[kVec];
+                float xf[kVec];
                 unpack<T>(xr[j], xf);
-                unpack<T>(dr[j], df);
 #pragma unroll
-                for (int e = 0; e < kVec; ++e) xf[e] += df[e];
-                xr[j] = pack<T>(xf);  // the rounded sum: stored, and normalised below
-                store_raw<T, false>(orow, (int64_t)(j * LANES + rl) * kVec, d, xr[j], vx);
+                for (int e = 0; e < kVec; ++e) ss += xf[e] * xf[e];
             }
-        }
-
-        float ss = 0.0f;
-#pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            float xf[kVec];
-            unpack<T>(xr[j], xf);
-#pragma unroll
-            for (int e = 0; e < kVec; ++e) ss += xf[e] * xf[e];
         }
         ss = wave_sum(ss);
         if constexpr (WPR > 1) {
-            float* slot = part[it & 1];
-            if (lane == 0) slot[wave] = ss;
+            float* slot = part[it & 1][grp];
+            if (lane == 0) slot[wave % WPR] = ss;
             __syncthreads();
             ss = 0.0f;
 #pragma unroll
             for (int i = 0; i < WPR; ++i) ss += slot[i];
         }
-        const float r = __builtin_amdgcn_rsqf(ss / (float)a.d + a.eps);
-
-        void* yrow = row_ptr<T>(a.y, row, a.y_stride);
-        const bool vy = aligned16(yrow);
+        if (live) {
+            const float r = __builtin_amdgcn_rsqf(ss / (float)a.d + a.eps);
+            void* yrow = row_ptr<T>(a.y, row, a.y_stride);
+            const bool vy = aligned16(yrow);
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            float xf[kVec], wf[kVec], yf[kVec];
-            unpack<T>(xr[j], xf);
-            unpack<T>(wr[j], wf);
+            for (int j = 0; j < VPT; ++j) {
+                float xf[kVec], wf[kVec], yf[kVec];
+                unpack<T>(xr[j], xf);
+                unpack<T>(wr[j], wf);
 #pragma unroll
-            for (int e = 0; e < kVec; ++e) yf[e] = xf[e] * r * wf[e];
-            store_raw<T, false>(yrow, (int64_t)(j * LANES + rl) * kVec, d, pack<T>(yf), vy);
+                for (int e = 0; e < kVec; ++e) yf[e] = xf[e] * r * wf[e];
+                store_raw<T, C::NTS>(yrow, (int64_t)(j * LANES + rl) * kVec, d, pack<T>(yf), vy);
+            }
         }
     }
 }
 
-// Resident workgroups per CU that the grid-stride launch aims for.
-constexpr int kNormWgsPerCu = 8;
-
-template <typename T, int VPT, int WPR, bool ADD>
-static int launch_norm(const NormArgs& a, void* stream) {
-    constexpr int GROUPS = WPR == 1 ? 4 : 1;
-    const dim3 block(WPR == 1 ? 256 : 64 * WPR);
-    const dim3 grid(grid_for(a.rows, GROUPS, device_cus(), kNormWgsPerCu));
-    return launch(row_norm_kernel<T, VPT, WPR, ADD>, grid, block, stream, a);
+// Launches with a grid of ceil(rows / GROUPS) workgroups, capped at
+// `wgs_per_cu` resident rounds per CU (a large cap gives a one-pass grid).
+template <typename T, typename C, bool ADD>
+static int launch_norm(const NormArgs& a, void* stream, int wgs_per_cu) {
+    const dim3 grid(grid_for(a.rows, C::GROUPS, device_cus(), wgs_per_cu));
+    return launch(row_norm_kernel<T, C, ADD>, grid, dim3(C::BLOCK), stream, a);
 }
 
-// Vectors per lane for one wave per row (WPR = 1) and for a 4-wave row
-// group (WPR = 4); the 4-wave buckets are coarser.
-constexpr int kWaveMaxVpt = 16;
-constexpr int kWgBuckets[] = {6, 8, 10, 12, 16};
-
-// (VPT, WPR) for a row of `nvec` 16-byte vectors; VPT = 0 if too wide.
+// ------------------------------------------------------------ dispatch
+// The launch shape for a row of `nvec` 16-byte vectors, chosen from sweeps
+// of every (VPT, WPR, GROUPS) on MI355X at widths 512..8192 in bf16 and
+// fp32 (one-pass grids, nontemporal loads and stores):
+//  * HBM streams best when each lane holds only a few vectors of each
+//    stream: one wave per row while a plain row needs at most 5 vectors per
+//    lane, otherwise 2 or 3 vectors per lane over up to 8 waves, whichever
+//    leaves fewer lanes idle; the add variant reads two streams and takes 1
+//    or 2 vectors per lane;
+//  * rows of up to 3 waves go two to a workgroup (four for single-wave rows
+//    of 3 or more vectors per lane).
 struct NormShape {
-    int vpt, wpr;
+    int vpt, wpr, groups;
 };
-inline NormShape norm_shape(int64_t nvec) {
-    if (nvec <= (int64_t)kWaveMaxVpt * 64) return {(int)((nvec + 63) / 64), 1};
-    for (int b : kWgBuckets)
-        if (nvec <= (int64_t)b * 256) return {b, 4};
-    return {0, 0};
+
+inline NormShape norm_shape(int64_t nvec, bool add) {
+    if (nvec <= 0) return {0, 0, 0};
+    if (!add && nvec <= 5 * 64) {
+        const int vpt = (int)((nvec + 63) / 64);
+        return {vpt, 1, vpt >= 3 ? 4 : 2};
+    }
+    if (add && nvec <= 64) return {1, 1, 2};
+    const int lo = add ? 1 : 2, hi = add ? 2 : 3;
+    int best_v = 0, best_w = 0;
+    double best_util = -1.0;
+    for (int v = lo; v <= hi; ++v) {
+        const int64_t w = (nvec + 64 * v - 1) / (64 * v);
+        if (w > 8) continue;
+        const double util = (double)nvec / (double)(64 * v * w);
+        if (util > best_util + 1e-9) {
+            best_util = util;
+            best_v = v;
+            best_w = (int)w;
+        }
+    }
+    if (best_v == 0) {  // wider than 8 waves at hi vectors per lane
+        best_w = 8;
+        best_v = (int)((nvec + 511) / 512);
+        if (best_v > 8) return {0, 0, 0};
+    }
+    return {best_v, best_w, best_w <= 3 ? 2 : 1};
+}
+
+template <typename T, bool ADD, int VPT, int WPR>
+static int launch_g(const NormArgs& a, void* stream, int groups) {
+    constexpr int kOnePass = 1 << 20;  // grid cap per CU: effectively one pass
+    if (groups == 4) return launch_norm<T, NormCfg<VPT, WPR, 4, true, true>, ADD>(a, stream, kOnePass);
+    if (groups == 2) return launch_norm<T, NormCfg<VPT, WPR, 2, true, true>, ADD>(a, stream, kOnePass);
+    return launch_norm<T, NormCfg<VPT, WPR, 1, true, true>, ADD>(a, stream, kOnePass);
+}
+
+template <typename T, bool ADD, int WPR>
+static int launch_w(const NormArgs& a, void* stream, int vpt, int groups) {
+    switch (vpt) {
+        case 1: return launch_g<T, ADD, 1, WPR>(a, stream, groups);
+        case 2: return launch_g<T, ADD, 2, WPR>(a, stream, groups);
+        case 3: return launch_g<T, ADD, 3, WPR>(a, stream, groups);
+        case 4: return launch_g<T, ADD, 4, WPR>(a, stream, groups);
+        case 5: return launch_g<T, ADD, 5, WPR>(a, stream, groups);
+        case 6: return WPR == 8 ? launch_g<T, ADD, 6, WPR>(a, stream, groups) : KCR_ERR_SHAPE;
+        case 7: return WPR == 8 ? launch_g<T, ADD, 7, WPR>(a, stream, groups) : KCR_ERR_SHAPE;
+        case 8: return WPR == 8 ? launch_g<T, ADD, 8, WPR>(a, stream, groups) : KCR_ERR_SHAPE;
+    }
+    return KCR_ERR_SHAPE;
 }
 
 template <typename T, bool ADD>
 static int dispatch_norm(const NormArgs& a, void* stream) {
-    const NormShape s = norm_shape((a.d + T::kVec - 1) / T::kVec);
-    if (s.wpr == 1) {
-        switch (s.vpt) {
-            case 1: return launch_norm<T, 1, 1, ADD>(a, stream);
-            case 2: return launch_norm<T, 2, 1, ADD>(a, stream);
-            case 3: return launch_norm<T, 3, 1, ADD>(a, stream);
-            case 4: return launch_norm<T, 4, 1, ADD>(a, stream);
-            case 5: return launch_norm<T, 5, 1, ADD>(a, stream);
-            case 6: return launch_norm<T, 6, 1, ADD>(a, stream);
-            case 7: return launch_norm<T, 7, 1, ADD>(a, stream);
-            case 8: return launch_norm<T, 8, 1, ADD>(a, stream);
-            case 9: return launch_norm<T, 9, 1, ADD>(a, stream);
-            case 10: return launch_norm<T, 10, 1, ADD>(a, stream);
-            case 11: return launch_norm<T, 11, 1, ADD>(a, stream);
-            case 12: return launch_norm<T, 12, 1, ADD>(a, stream);
-            case 13: return launch_norm<T, 13, 1, ADD>(a, stream);
-            case 14: return launch_norm<T, 14, 1, ADD>(a, stream);
-            case 15: return launch_norm<T, 15, 1, ADD>(a, stream);
-            case 16: return launch_norm<T, 16, 1, ADD>(a, stream);
-        }
-    } else if (s.wpr == 4) {
-        switch (s.vpt) {
-            case 6: return launch_norm<T, 6, 4, ADD>(a, stream);
-            case 8: return launch_norm<T, 8, 4, ADD>(a, stream);
-            case 10: return launch_norm<T, 10, 4, ADD>(a, stream);
-            case 12: return launch_norm<T, 12, 4, ADD>(a, stream);
-            case 16: return launch_norm<T, 16, 4, ADD>(a, stream);
-        }
+    const NormShape s = norm_shape((a.d + T::kVec - 1) / T::kVec, ADD);
+    switch (s.wpr) {
+        case 1: return launch_w<T, ADD, 1>(a, stream, s.vpt, s.groups);
+        case 2: return launch_w<T, ADD, 2>(a, stream, s.vpt, s.groups);
+        case 3: return launch_w<T, ADD, 3>(a, stream, s.vpt, s.groups);
+        case 4: return launch_w<T, ADD, 4>(a, stream, s.vpt, s.groups);
+        case 5: return launch_w<T, ADD, 5>(a, stream, s.vpt, s.groups);
+        case 6: return launch_w<T, ADD, 6>(a, stream, s.vpt, s.groups);
+        case 7: return launch_w<T, ADD, 7>(a, stream, s.vpt, s.groups);
+        case 8: return launch_w<T, ADD, 8>(a, stream, s.vpt, s.groups);
     }
     return KCR_ERR_SHAPE;
 }
@@ -249,17 +291,20 @@ extern "C" int kcr_add_rmsnorm(void* x, int64_t x_stride, const void* delta, int
 }
 
 // Host self-test hook: every width up to the limit maps to a shape that
-// covers it. Returns 0 when all widths pass.
+// covers it, within the instantiated range. Returns 0 when all widths pass.
 int kcr_norm_shape_selftest() {
     for (int dt = 0; dt < 2; ++dt) {
         const int vec = dt == 0 ? Bf16::kVec : F32::kVec;
         const int64_t maxd = dt == 0 ? KCR_NORM_MAX_D_BF16 : KCR_NORM_MAX_D_F32;
-        for (int64_t d = 1; d <= maxd; ++d) {
-            const int64_t nvec = (d + vec - 1) / vec;
-            const NormShape s = norm_shape(nvec);
-            if (s.vpt < 1 || s.vpt > 16) return 1;
-            if ((int64_t)s.vpt * 64 * s.wpr < nvec) return 2;
-        }
+        for (int add = 0; add < 2; ++add)
+            for (int64_t d = 1; d <= maxd; ++d) {
+                const int64_t nvec = (d + vec - 1) / vec;
+                const NormShape s = norm_shape(nvec, add != 0);
+                if (s.vpt < 1 || s.wpr < 1 || s.wpr > 8 || s.vpt > 8) return 1;
+                if (s.vpt > 5 && s.wpr != 8) return 1;
+                if ((int64_t)s.vpt * 64 * s.wpr < nvec) return 2;
+                if (64 * s.wpr * s.groups > 1024) return 3;
+            }
     }
     return 0;
 }

@@ -10,18 +10,21 @@
 // "AsyncT vLLM notes (1)", section 1.1.
 //
 // gfx950 design
-//  * Work unit = (token t, KV group g). Following the GQA mapping of the
-//    same section, kv_head = head / (n_head / n_kv_head), group g holds the
-//    query heads g*G .. g*G+G-1 (G = n_head / n_kv_head) -- contiguous in
-//    memory -- plus K head g and V head g: G + 2 "virtual heads" of equal
-//    cost, so every unit does the same work and no lane idles on K/V.
+//  * Virtual heads: following the GQA mapping of the same section,
+//    kv_head = head / (n_head / n_kv_head), KV group g is the query heads
+//    g*G .. g*G+G-1 (G = n_head / n_kv_head, contiguous in memory), then K
+//    head g, then V head g -- G + 2 heads of equal cost. A work unit is a run
+//    of HPU consecutive virtual heads of one token (1 for decode batches, 2
+//    for prefill), so every unit does the same work and no lane idles on
+//    K/V.
 //  * LPU lanes per unit (the next power of two at or above the number of
 //    16-byte chunks in half a head: 8 for bf16 head_dim 128). Lane c owns
 //    chunk c of the first half AND chunk c of the second half, so each
 //    rotation pair (i, i + d/2) sits in one lane and needs no shuffle.
 //  * cos/sin for the lane's frequencies are loaded once per unit (fp32
-//    table rows) and reused for all G + 2 virtual heads; HU heads are loaded
-//    before any is stored, so a lane keeps 2*HU 16-byte loads in flight.
+//    table rows, L2-resident across tokens) and reused for its HPU heads;
+//    all heads of a unit are loaded before any is stored. One-pass grid,
+//    nontemporal loads and stores of the streamed heads.
 //  * K_rot and V are written with 16-byte stores at
 //    ((which * n_slots + slot) * n_kv_head + g) * head_dim: the cache's
 //    (block, offset) pair flattens to the slot, so no division is needed.
@@ -43,25 +46,38 @@ struct RopeArgs {
     const float* sin_t;
     int64_t q_ts, q_hs, k_ts, k_hs, v_ts, v_hs;  // elements
     int64_t max_pos, n_slots;
-    uint32_t units;  // T * n_kv_head
-    FastDiv hkv;     // division by n_kv_head
-    int32_t hq, group, dh;
+    uint32_t units;   // T * units per token
+    FastDiv upt;      // units per token: ceil(n_virtual_heads / HPU)
+    FastDiv gsize;    // virtual heads per KV group: G + 2
+    int32_t nvh;      // virtual heads per token: n_kv_head * (G + 2)
+    int32_t hq, hkv, group, dh;
 };
 
-template <typename T, int LPU, int HU>
+// Launch shape: LPU lanes per unit (one 16-byte chunk of each half head per
+// lane), HPU virtual heads per unit, nontemporal loads (NTL) and stores (NTS)
+// for the streamed heads.
+template <int LPU_, int HPU_, bool NTL_, bool NTS_>
+struct RopeCfg {
+    static constexpr int LPU = LPU_, HPU = HPU_;
+    static constexpr bool NTL = NTL_, NTS = NTS_;
+};
+
+// Virtual heads of a token, in KV-group order: for group g (kv_head g), the
+// query heads g*G .. g*G+G-1 (exactly those with head / G == g), then K head
+// g, then V head g.
+template <typename T, typename C>
 __global__ __launch_bounds__(256) void rope_kvstore_kernel(const RopeArgs a) {
     using S = typename T::storage;
-    constexpr int kVec = T::kVec;
+    constexpr int kVec = T::kVec, LPU = C::LPU, HPU = C::HPU;
     constexpr int UPW = 256 / LPU;  // units per workgroup
     const int c = threadIdx.x % LPU;
     const int half = a.dh >> 1;
     const bool lane_on = c * kVec < half;
-    const int nvh = a.group + 2;
     const int64_t c0 = (int64_t)c * kVec;
 
     for (uint32_t u = blockIdx.x * UPW + threadIdx.x / LPU; u < a.units; u += gridDim.x * UPW) {
-        const uint32_t t = fastdiv(u, a.hkv);
-        const int g = (int)(u - t * a.hkv.d);
+        const uint32_t t = fastdiv(u, a.upt);
+        const int j0 = (int)(u - t * a.upt.d) * HPU;
         const int64_t p = a.pos[t];
         if (!lane_on || p < 0 || p >= a.max_pos) continue;
         const int64_t slot = a.slots[t];
@@ -83,73 +99,101 @@ __global__ __launch_bounds__(256) void rope_kvstore_kernel(const RopeArgs a) {
             }
         }
 
-        for (int j0 = 0; j0 < nvh; j0 += HU) {
-            u32x4 x1[HU], x2[HU];
+        // Load every head of the unit before storing any.
+        u32x4 x1[HPU], x2[HPU];
+        int kind[HPU];  // 0: query head, 1: K, 2: V, -1: past the token's heads
+        int gg[HPU], hh[HPU];
 #pragma unroll
-            for (int h = 0; h < HU; ++h) {
-                const int j = j0 + h;
-                if (j >= nvh) break;
-                const S* src;
-                if (j < a.group) src = static_cast<const S*>(a.q) + t * a.q_ts + (int64_t)(g * a.group + j) * a.q_hs;
-                else if (j == a.group) src = static_cast<const S*>(a.k) + t * a.k_ts + (int64_t)g * a.k_hs;
-                else src = static_cast<const S*>(a.v) + t * a.v_ts + (int64_t)g * a.v_hs;
-                x1[h] = *reinterpret_cast<const u32x4*>(src + c0);
-                x2[h] = *reinterpret_cast<const u32x4*>(src + half + c0);
+        for (int h = 0; h < HPU; ++h) {
+            const int j = j0 + h;
+            kind[h] = -1;
+            if (j >= a.nvh) continue;
+            const int g = (int)fastdiv((uint32_t)j, a.gsize);
+            const int r = j - g * (int)a.gsize.d;
+            const S* src;
+            if (r < a.group) {
+                kind[h] = 0;
+                hh[h] = g * a.group + r;
+                src = static_cast<const S*>(a.q) + t * a.q_ts + (int64_t)hh[h] * a.q_hs;
+            } else if (r == a.group) {
+                kind[h] = 1;
+                src = static_cast<const S*>(a.k) + t * a.k_ts + (int64_t)g * a.k_hs;
+            } else {
+                kind[h] = 2;
+                src = static_cast<const S*>(a.v) + t * a.v_ts + (int64_t)g * a.v_hs;
             }
+            gg[h] = g;
+            x1[h] = C::NTL ? ld16_nt<T>(src, c0) : ld16<T>(src, c0);
+            x2[h] = C::NTL ? ld16_nt<T>(src, half + c0) : ld16<T>(src, half + c0);
+        }
 #pragma unroll
-            for (int h = 0; h < HU; ++h) {
-                const int j = j0 + h;
-                if (j >= nvh) break;
-                S* dst;
-                if (j < a.group) {
-                    dst = static_cast<S*>(a.q_out) + ((int64_t)t * a.hq + g * a.group + j) * a.dh;
-                } else {
-                    if (!store_kv) continue;
-                    const int64_t which = j == a.group ? 0 : 1;
-                    dst = static_cast<S*>(a.cache) +
-                          ((which * a.n_slots + slot) * a.hkv.d + g) * (int64_t)a.dh;
-                }
-                u32x4 o1 = x1[h], o2 = x2[h];
-                if (j <= a.group) {  // Q or K: rotate; V is copied as is
-                    float f1[kVec], f2[kVec], r1[kVec], r2[kVec];
-                    unpack<T>(x1[h], f1);
-                    unpack<T>(x2[h], f2);
+        for (int h = 0; h < HPU; ++h) {
+            if (kind[h] < 0) continue;
+            S* dst;
+            if (kind[h] == 0) {
+                dst = static_cast<S*>(a.q_out) + ((int64_t)t * a.hq + hh[h]) * a.dh;
+            } else {
+                if (!store_kv) continue;
+                dst = static_cast<S*>(a.cache) +
+                      (((int64_t)(kind[h] - 1) * a.n_slots + slot) * a.hkv + gg[h]) * (int64_t)a.dh;
+            }
+            u32x4 o1 = x1[h], o2 = x2[h];
+            if (kind[h] < 2) {  // Q or K: rotate; V is copied as is
+                float f1[kVec], f2[kVec], r1[kVec], r2[kVec];
+                unpack<T>(x1[h], f1);
+                unpack<T>(x2[h], f2);
 #pragma unroll
-                    for (int e = 0; e < kVec; ++e) {
-                        r1[e] = f1[e] * cs[e] - f2[e] * sn[e];
-                        r2[e] = f2[e] * cs[e] + f1[e] * sn[e];
-                    }
-                    o1 = pack<T>(r1);
-                    o2 = pack<T>(r2);
+                for (int e = 0; e < kVec; ++e) {
+                    r1[e] = f1[e] * cs[e] - f2[e] * sn[e];
+                    r2[e] = f2[e] * cs[e] + f1[e] * sn[e];
                 }
-                *reinterpret_cast<u32x4*>(dst + c0) = o1;
-                *reinterpret_cast<u32x4*>(dst + half + c0) = o2;
+                o1 = pack<T>(r1);
+                o2 = pack<T>(r2);
+            }
+            if (C::NTS) {
+                st16_nt<T>(dst, c0, o1);
+                st16_nt<T>(dst, half + c0, o2);
+            } else {
+                st16<T>(dst, c0, o1);
+                st16<T>(dst, half + c0, o2);
             }
         }
     }
 }
 
-constexpr int kRopeHU = 8;
-constexpr int kRopeWgsPerCu = 8;
-
-template <typename T, int LPU>
-static int launch_rope(const RopeArgs& a, void* stream) {
-    constexpr int UPW = 256 / LPU;
-    const dim3 grid(grid_for(a.units, UPW, device_cus(), kRopeWgsPerCu));
-    return launch(rope_kvstore_kernel<T, LPU, kRopeHU>, grid, dim3(256), stream, a);
+template <typename T, typename C>
+static int launch_rope(RopeArgs a, int64_t T_tokens, void* stream, int wgs_per_cu) {
+    constexpr int UPW = 256 / C::LPU;
+    const int upt = (a.nvh + C::HPU - 1) / C::HPU;
+    a.upt = make_fastdiv((uint32_t)upt);
+    a.units = (uint32_t)(T_tokens * upt);
+    const dim3 grid(grid_for(a.units, UPW, device_cus(), wgs_per_cu));
+    return launch(rope_kvstore_kernel<T, C>, grid, dim3(256), stream, a);
 }
 
-template <typename T>
-static int dispatch_rope(const RopeArgs& a, void* stream) {
+template <typename T, int HPU>
+static int dispatch_rope_lpu(const RopeArgs& a, int64_t T_tokens, void* stream) {
+    constexpr int kOnePass = 1 << 20;
     const int chunks = (a.dh / 2) / T::kVec;
-    if (chunks <= 1) return launch_rope<T, 1>(a, stream);
-    if (chunks <= 2) return launch_rope<T, 2>(a, stream);
-    if (chunks <= 4) return launch_rope<T, 4>(a, stream);
-    if (chunks <= 8) return launch_rope<T, 8>(a, stream);
-    if (chunks <= 16) return launch_rope<T, 16>(a, stream);
-    if (chunks <= 32) return launch_rope<T, 32>(a, stream);
-    if (chunks <= 64) return launch_rope<T, 64>(a, stream);
+    if (chunks <= 1) return launch_rope<T, RopeCfg<1, HPU, true, true>>(a, T_tokens, stream, kOnePass);
+    if (chunks <= 2) return launch_rope<T, RopeCfg<2, HPU, true, true>>(a, T_tokens, stream, kOnePass);
+    if (chunks <= 4) return launch_rope<T, RopeCfg<4, HPU, true, true>>(a, T_tokens, stream, kOnePass);
+    if (chunks <= 8) return launch_rope<T, RopeCfg<8, HPU, true, true>>(a, T_tokens, stream, kOnePass);
+    if (chunks <= 16) return launch_rope<T, RopeCfg<16, HPU, true, true>>(a, T_tokens, stream, kOnePass);
+    if (chunks <= 32) return launch_rope<T, RopeCfg<32, HPU, true, true>>(a, T_tokens, stream, kOnePass);
+    if (chunks <= 64) return launch_rope<T, RopeCfg<64, HPU, true, true>>(a, T_tokens, stream, kOnePass);
     return KCR_ERR_SHAPE;
+}
+
+// One virtual head per unit spreads small batches over the most
+// workgroups; prefill-sized batches take two per unit, which reuses each
+// cos/sin load once and measured fastest there.
+constexpr int64_t kRopeSmallBatch = 4096;
+
+template <typename T>
+static int dispatch_rope(const RopeArgs& a, int64_t T_tokens, void* stream) {
+    return T_tokens <= kRopeSmallBatch ? dispatch_rope_lpu<T, 1>(a, T_tokens, stream)
+                                       : dispatch_rope_lpu<T, 2>(a, T_tokens, stream);
 }
 
 // ---------------------------------------------------------- cos/sin tables
@@ -194,7 +238,7 @@ extern "C" int kcr_rope_kvstore(const void* q, int64_t q_tok_stride, int64_t q_h
         head_dim > KCR_ROPE_MAX_HEAD_DIM)
         return KCR_ERR_SHAPE;
     if (T < 0 || block_size < 1 || num_blocks < 0 || max_pos < 1) return KCR_ERR_SHAPE;
-    if (T * (int64_t)n_kv_head >= (int64_t(1) << 31)) return KCR_ERR_SHAPE;
+    if (T * (int64_t)n_kv_head * (n_head / n_kv_head + 2) >= (int64_t(1) << 31)) return KCR_ERR_SHAPE;
     if (T == 0) return KCR_OK;
     if (!q || !k || !v || !q_out || !positions || !cos_tab || !sin_tab || !slot_mapping)
         return KCR_ERR_NULL;
@@ -226,11 +270,12 @@ extern "C" int kcr_rope_kvstore(const void* q, int64_t q_tok_stride, int64_t q_h
         return KCR_ERR_ALIAS;
     if (device_cus() <= 0) return KCR_ERR_DEVICE;
 
+    const int group = n_head / n_kv_head;
     RopeArgs a{q, k, v, q_out, kv_cache, positions, slot_mapping, cos_tab, sin_tab,
                q_tok_stride, q_head_stride, k_tok_stride, k_head_stride, v_tok_stride, v_head_stride,
-               max_pos, n_slots, (uint32_t)(T * n_kv_head), make_fastdiv((uint32_t)n_kv_head),
-               n_head, n_head / n_kv_head, head_dim};
-    return dtype == KCR_BF16 ? dispatch_rope<Bf16>(a, stream) : dispatch_rope<F32>(a, stream);
+               max_pos, n_slots, 0u, make_fastdiv(1u), make_fastdiv((uint32_t)(group + 2)),
+               n_kv_head * (group + 2), n_head, n_kv_head, group, head_dim};
+    return dtype == KCR_BF16 ? dispatch_rope<Bf16>(a, T, stream) : dispatch_rope<F32>(a, T, stream);
 }
 
 extern "C" int kcr_rope_cos_sin(float* cos_tab, float* sin_tab, int64_t max_pos, int head_dim,

@@ -34,19 +34,13 @@ struct CopyArgs {
     int64_t n;  // 16-byte vectors
 };
 
-// Grid-stride copy, four 16-byte loads in flight per lane before the stores.
-__global__ __launch_bounds__(256) void copy_kernel(const CopyArgs a) {
-    constexpr int U = 4;
-    const int64_t step = (int64_t)gridDim.x * 256 * U;
-    for (int64_t base = (int64_t)blockIdx.x * 256 * U + threadIdx.x; base < a.n; base += step) {
-        u32x4 v[U];
-#pragma unroll
-        for (int k = 0; k < U; ++k)
-            if (base + k * 256 < a.n) v[k] = a.src[base + k * 256];
-#pragma unroll
-        for (int k = 0; k < U; ++k)
-            if (base + k * 256 < a.n) a.dst[base + k * 256] = v[k];
-    }
+// One 16-byte vector per lane, 64-lane workgroups, a one-pass grid and
+// nontemporal loads and stores: the fastest copy shape measured on MI355X
+// (sweeps over unroll, block size, grid-stride vs one-pass and cache
+// hints), so it stands for the attainable read+write bandwidth.
+__global__ __launch_bounds__(64) void copy_kernel(const CopyArgs a) {
+    const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
+    if (i < a.n) __builtin_nontemporal_store(__builtin_nontemporal_load(a.src + i), a.dst + i);
 }
 
 }  // namespace kcr
@@ -62,7 +56,8 @@ extern "C" int kcr_copy(void* dst, const void* src, int64_t bytes, void* stream)
     const int cus = device_cus();
     if (cus <= 0) return KCR_ERR_DEVICE;
     CopyArgs a{static_cast<u32x4*>(dst), static_cast<const u32x4*>(src), bytes / 16};
-    return launch(copy_kernel, dim3(grid_for(a.n, 256 * 4, cus, 8)), dim3(256), stream, a);
+    if (a.n > (int64_t)0x7FFFFFFF * 64) return KCR_ERR_SHAPE;
+    return launch(copy_kernel, dim3((uint32_t)((a.n + 63) / 64)), dim3(64), stream, a);
 }
 
 extern "C" int kcr_device_cus(void) { return device_cus(); }

@@ -13,9 +13,9 @@
 //    vector) split uses a precomputed multiply-shift division, so strided
 //    gate/up halves of a fused gate_up buffer need no copy. Rows whose base
 //    is not 16-byte aligned are accessed element by element.
-//  * UNROLL vectors of gate and up are loaded before any math, so each lane
-//    keeps 2 * UNROLL 16-byte loads in flight; the grid is capped at a few
-//    resident workgroups per CU and strides over the rest (persistent).
+//  * One vector of gate and of up per lane, 64-lane workgroups, a one-pass
+//    grid and nontemporal loads and stores: on MI355X many small waves
+//    stream HBM faster than fewer waves with more loads each.
 //  * sigmoid(g) = 1 / (1 + 2^(-g log2 e)) on the hardware v_exp_f32 and
 //    v_rcp_f32 (no IEEE divide): two quarter-rate transcendentals per
 //    element, well under the VALU budget at HBM speed.
@@ -39,49 +39,54 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
     return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
-template <typename T, int UNROLL>
-__global__ __launch_bounds__(256) void swiglu_kernel(const SwigluArgs a) {
+// Launch shape: BLOCK threads, UNROLL vectors of each stream per lane before
+// any math, nontemporal loads (NTL) and stores (NTS).
+template <int BLOCK_, int UNROLL_, bool NTL_, bool NTS_>
+struct SwigluCfg {
+    static constexpr int BLOCK = BLOCK_, UNROLL = UNROLL_;
+    static constexpr bool NTL = NTL_, NTS = NTS_;
+};
+
+template <typename T, typename C>
+__global__ __launch_bounds__(C::BLOCK) void swiglu_kernel(const SwigluArgs a) {
     using S = typename T::storage;
-    constexpr int kVec = T::kVec;
-    const uint32_t step = gridDim.x * (256u * UNROLL);
-    for (uint32_t base = blockIdx.x * (256u * UNROLL) + threadIdx.x; base < a.total; base += step) {
-        u32x4 gr[UNROLL], ur[UNROLL];
-        int64_t row[UNROLL], col[UNROLL];
+    constexpr int kVec = T::kVec, B = C::BLOCK, U = C::UNROLL;
+    const uint32_t step = gridDim.x * (uint32_t)(B * U);
+    for (uint32_t base = blockIdx.x * (uint32_t)(B * U) + threadIdx.x; base < a.total; base += step) {
+        u32x4 gr[U], ur[U];
+        int64_t row[U], col[U];
 #pragma unroll
-        for (int k = 0; k < UNROLL; ++k) {
-            const uint32_t idx = base + k * 256u;
+        for (int k = 0; k < U; ++k) {
+            const uint32_t idx = base + k * (uint32_t)B;
             if (idx < a.total) {
                 const uint32_t r = fastdiv(idx, a.vpr);
                 row[k] = r;
                 col[k] = (int64_t)(idx - r * a.vpr.d) * kVec;
                 const S* gp = static_cast<const S*>(a.g) + row[k] * a.g_stride;
                 const S* up = static_cast<const S*>(a.u) + row[k] * a.u_stride;
-                gr[k] = load_raw<T, false>(gp, col[k], a.cols, aligned16(gp));
-                ur[k] = load_raw<T, false>(up, col[k], a.cols, aligned16(up));
+                gr[k] = load_raw<T, C::NTL>(gp, col[k], a.cols, aligned16(gp));
+                ur[k] = load_raw<T, C::NTL>(up, col[k], a.cols, aligned16(up));
             }
         }
 #pragma unroll
-        for (int k = 0; k < UNROLL; ++k) {
-            if (base + k * 256u < a.total) {
+        for (int k = 0; k < U; ++k) {
+            if (base + k * (uint32_t)B < a.total) {
                 float gf[kVec], uf[kVec], of[kVec];
                 unpack<T>(gr[k], gf);
                 unpack<T>(ur[k], uf);
 #pragma unroll
                 for (int e = 0; e < kVec; ++e) of[e] = silu_mul(gf[e], uf[e]);
                 S* op = static_cast<S*>(a.out) + row[k] * a.out_stride;
-                store_raw<T, false>(op, col[k], a.cols, pack<T>(of), aligned16(op));
+                store_raw<T, C::NTS>(op, col[k], a.cols, pack<T>(of), aligned16(op));
             }
         }
     }
 }
 
-constexpr int kSwigluUnroll = 2;
-constexpr int kSwigluWgsPerCu = 8;
-
-template <typename T>
-static int launch_swiglu(const SwigluArgs& a, void* stream) {
-    const dim3 grid(grid_for(a.total, 256 * kSwigluUnroll, device_cus(), kSwigluWgsPerCu));
-    return launch(swiglu_kernel<T, kSwigluUnroll>, grid, dim3(256), stream, a);
+template <typename T, typename C>
+static int launch_swiglu(const SwigluArgs& a, void* stream, int wgs_per_cu) {
+    const dim3 grid(grid_for(a.total, C::BLOCK * C::UNROLL, device_cus(), wgs_per_cu));
+    return launch(swiglu_kernel<T, C>, grid, dim3(C::BLOCK), stream, a);
 }
 
 }  // namespace kcr
@@ -112,5 +117,10 @@ extern "C" int kcr_swiglu(const void* gate, int64_t gate_stride, const void* up,
     if (device_cus() <= 0) return KCR_ERR_DEVICE;
     SwigluArgs a{gate, up, out, gate_stride, up_stride, out_stride, cols,
                  (uint32_t)(rows * vpr), make_fastdiv((uint32_t)vpr)};
-    return dtype == KCR_BF16 ? launch_swiglu<Bf16>(a, stream) : launch_swiglu<F32>(a, stream);
+    // 64-lane workgroups, one vector of each stream per lane, one-pass grid,
+    // nontemporal loads and stores: the fastest shape in sweeps on MI355X.
+    using Cfg = SwigluCfg<64, 1, true, true>;
+    constexpr int kOnePass = 1 << 20;
+    return dtype == KCR_BF16 ? launch_swiglu<Bf16, Cfg>(a, stream, kOnePass)
+                             : launch_swiglu<F32, Cfg>(a, stream, kOnePass);
 }
