@@ -164,6 +164,34 @@ def large_shapes(kcr, iters: int):
     return out
 
 
+def launch_floor(kcr, n_launch: int, reps: int):
+    """Per-node time of a captured graph of n_launch minimal launches (a
+    16-byte copy): what one graph node costs with (almost) no work."""
+    import torch
+    a = torch.zeros(4, dtype=torch.int32, device="cuda")
+    b = torch.empty_like(a)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        kcr.copy_(b, a)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n_launch):
+            kcr.copy_(b, a)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = events(2)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * n_launch)
+
+
 def copy_ceiling(kcr, iters: int):
     import torch
     n = 1 << 30
@@ -235,6 +263,36 @@ def cpu_baseline_run(wl, bytes_per_step, budget_s: float):
                 seconds=round(el, 2), ms_per_step=round(1e3 * el / steps, 1))
 
 
+def pmc_pass():
+    """Eager launches only (no graphs), for hardware counter runs: the copy
+    kernel on 1 GiB (the byte-counter reference), every op at the decode
+    chain's shape over its 28 layers, and each kernel once at its large
+    shape."""
+    import torch
+    import kv_cache_rmsnorm_amd as kcr
+    import workloads
+    from kv_cache_rmsnorm_amd.chain import DecodeChain
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.random_(generator=torch.Generator(device="cuda").manual_seed(0))
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        kcr.copy_(dst, src)
+    torch.cuda.synchronize()
+    del src, dst
+    chain = DecodeChain(workloads.decode_chain(), "cuda", sentinel_cache=False)
+    for _ in range(2):
+        chain.step_eager()
+    torch.cuda.synchronize()
+    log(f"pmc pass: copy x3, chain steps x2 ({2 * 4 * len(chain.layers)} launches)")
+    del chain
+    torch.cuda.empty_cache()
+    large_shapes(kcr, 3)
+    torch.cuda.synchronize()
+    log("pmc pass done")
+
+
 def counter_traffic(kernel_name: str):
     """HBM bytes per launch of the dominant kernel from the committed
     rocprofv3 counter summary, if it was taken on the current kernel source."""
@@ -267,6 +325,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--skip-large", action="store_true", help="skip the per-kernel large shapes")
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="only launch each kernel eagerly (for rocprofv3 --pmc runs); no JSON line")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -281,6 +341,9 @@ def main():
     from kv_cache_rmsnorm_amd.chain import DecodeChain, swiglu_bytes
 
     assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    if args.pmc_pass:
+        pmc_pass()
+        return
     t0 = time.perf_counter()
     wl = workloads.decode_chain()
     log(f"generated workload in {time.perf_counter() - t0:.1f} s")
@@ -330,6 +393,8 @@ def main():
     log(f"graph step {ms * 1e3:.1f} us = {value:.0f} GB/s; eager {eager_ms * 1e3:.1f} us; "
         f"kernel sum {kernel_sum_us:.1f} us; swiglu {sw_us:.2f} us")
 
+    floor_us = launch_floor(kcr, 4 * len(chain.layers), max(10, args.steps // 2))
+    log(f"launch floor: {floor_us:.2f} us per graph node of a 16-byte copy")
     ceiling = copy_ceiling(kcr, args.kernel_iters)
     kernels = {} if args.skip_large else large_shapes(kcr, args.kernel_iters)
 
@@ -360,8 +425,9 @@ def main():
         "frac_of_peak": round(value / PEAK_GBS, 4),
         "step_bytes": nbytes["step"],
         "eager_ms_per_step": round(eager_ms, 5),
-        "kernel_sum_us_per_step": round(kernel_sum_us, 2),
-        "launch_gap_share_graph": round(1.0 - kernel_sum_us / (ms * 1e3), 4),
+        "event_stamped_kernel_sum_us_per_step": round(kernel_sum_us, 2),
+        "launch_floor_us_per_node": round(floor_us, 3),
+        "launch_floor_share_of_step": round(4 * len(chain.layers) * floor_us / (ms * 1e3), 4),
         "op_mean_us": op_us,
         "timed_wall_s": round(wall_s, 4),
         "roofline": roofline,

@@ -145,8 +145,8 @@ int kcr_add_rmsnorm(void* x, int64_t x_stride, const void* delta, int64_t delta_
  *       (q, k and v may be narrow views of one fused QKV projection buffer)
  *   q_out [T, n_head, head_dim] contiguous                                output
  *       may be q itself only when q is contiguous; no other overlap
- *   positions [T] int64; tokens with p outside [0, max_pos) are skipped
- *       entirely (no q_out, no cache write)
+ *   positions [T] int64; a token with p outside [0, max_pos) gets its
+ *       query heads copied to q_out unrotated and writes nothing to the cache
  *   cos_tab, sin_tab [max_pos, head_dim/2] fp32, contiguous (for example
  *       from kcr_rope_cos_sin)
  *   kv_cache [2, num_blocks, block_size, n_kv_head, head_dim] contiguous

@@ -75,18 +75,54 @@ __global__ __launch_bounds__(256) void rope_kvstore_kernel(const RopeArgs a) {
     const bool lane_on = c * kVec < half;
     const int64_t c0 = (int64_t)c * kVec;
 
+    if (!lane_on) return;
     for (uint32_t u = blockIdx.x * UPW + threadIdx.x / LPU; u < a.units; u += gridDim.x * UPW) {
         const uint32_t t = fastdiv(u, a.upt);
         const int j0 = (int)(u - t * a.upt.d) * HPU;
+        // Position and slot first, then every head of the unit: the head
+        // loads do not depend on the position, so they are in flight while
+        // the position arrives and only the (L2-resident) cos/sin rows wait
+        // for it.
         const int64_t p = a.pos[t];
-        if (!lane_on || p < 0 || p >= a.max_pos) continue;
         const int64_t slot = a.slots[t];
-        const bool store_kv = slot >= 0 && slot < a.n_slots;
+        // Loads are unconditional (a head index past the token's last head
+        // is clamped to it and its result discarded), and the q/k/v choice is
+        // made with selects, so no branch merge forces an early wait.
+        u32x4 x1[HPU], x2[HPU];
+        int kind[HPU];  // 0: query head, 1: K, 2: V, -1: past the token's heads
+        int gg[HPU], hh[HPU];
+#pragma unroll
+        for (int h = 0; h < HPU; ++h) {
+            const int j = j0 + h;
+            const int jc = j < a.nvh ? j : a.nvh - 1;
+            const int g = (int)fastdiv((uint32_t)jc, a.gsize);
+            const int r = jc - g * (int)a.gsize.d;
+            const bool isq = r < a.group, isk = r == a.group;
+            kind[h] = j < a.nvh ? (isq ? 0 : (isk ? 1 : 2)) : -1;
+            hh[h] = g * a.group + r;
+            gg[h] = g;
+            const S* base = static_cast<const S*>(isq ? a.q : (isk ? a.k : a.v));
+            const int64_t ts = isq ? a.q_ts : (isk ? a.k_ts : a.v_ts);
+            const int64_t hs = isq ? a.q_hs : (isk ? a.k_hs : a.v_hs);
+            const S* src = base + t * ts + (int64_t)(isq ? hh[h] : g) * hs;
+            x1[h] = C::NTL ? ld16_nt<T>(src, c0) : ld16<T>(src, c0);
+            x2[h] = C::NTL ? ld16_nt<T>(src, half + c0) : ld16<T>(src, half + c0);
+        }
+        // Compiler-only barrier: keeps the head loads issued here, ahead of
+        // the position-dependent branches below (emits no instruction).
+        asm volatile("" ::: "memory");
+        // A token whose position is out of range writes its query heads
+        // unrotated and nothing to the cache; its table row is clamped to
+        // row 0 and never used. Keeping the query store unconditional also
+        // keeps the head loads ahead of the wait for the position.
+        const bool p_ok = p >= 0 && p < a.max_pos;
+        const int64_t pc = p_ok ? p : 0;
+        const bool store_kv = p_ok && slot >= 0 && slot < a.n_slots;
 
         float cs[kVec], sn[kVec];
         {
-            const float* cr = a.cos_t + p * half + c0;
-            const float* sr = a.sin_t + p * half + c0;
+            const float* cr = a.cos_t + pc * half + c0;
+            const float* sr = a.sin_t + pc * half + c0;
 #pragma unroll
             for (int i = 0; i < kVec; i += 4) {
                 u32x4 cv = *reinterpret_cast<const u32x4*>(cr + i);
@@ -99,33 +135,6 @@ __global__ __launch_bounds__(256) void rope_kvstore_kernel(const RopeArgs a) {
             }
         }
 
-        // Load every head of the unit before storing any.
-        u32x4 x1[HPU], x2[HPU];
-        int kind[HPU];  // 0: query head, 1: K, 2: V, -1: past the token's heads
-        int gg[HPU], hh[HPU];
-#pragma unroll
-        for (int h = 0; h < HPU; ++h) {
-            const int j = j0 + h;
-            kind[h] = -1;
-            if (j >= a.nvh) continue;
-            const int g = (int)fastdiv((uint32_t)j, a.gsize);
-            const int r = j - g * (int)a.gsize.d;
-            const S* src;
-            if (r < a.group) {
-                kind[h] = 0;
-                hh[h] = g * a.group + r;
-                src = static_cast<const S*>(a.q) + t * a.q_ts + (int64_t)hh[h] * a.q_hs;
-            } else if (r == a.group) {
-                kind[h] = 1;
-                src = static_cast<const S*>(a.k) + t * a.k_ts + (int64_t)g * a.k_hs;
-            } else {
-                kind[h] = 2;
-                src = static_cast<const S*>(a.v) + t * a.v_ts + (int64_t)g * a.v_hs;
-            }
-            gg[h] = g;
-            x1[h] = C::NTL ? ld16_nt<T>(src, c0) : ld16<T>(src, c0);
-            x2[h] = C::NTL ? ld16_nt<T>(src, half + c0) : ld16<T>(src, half + c0);
-        }
 #pragma unroll
         for (int h = 0; h < HPU; ++h) {
             if (kind[h] < 0) continue;
@@ -137,19 +146,19 @@ __global__ __launch_bounds__(256) void rope_kvstore_kernel(const RopeArgs a) {
                 dst = static_cast<S*>(a.cache) +
                       (((int64_t)(kind[h] - 1) * a.n_slots + slot) * a.hkv + gg[h]) * (int64_t)a.dh;
             }
-            u32x4 o1 = x1[h], o2 = x2[h];
-            if (kind[h] < 2) {  // Q or K: rotate; V is copied as is
-                float f1[kVec], f2[kVec], r1[kVec], r2[kVec];
-                unpack<T>(x1[h], f1);
-                unpack<T>(x2[h], f2);
+            // Q and K rotate; V (and Q at an out-of-range position) is copied
+            // as is, selected so that its bits pass through untouched.
+            float f1[kVec], f2[kVec], r1[kVec], r2[kVec];
+            unpack<T>(x1[h], f1);
+            unpack<T>(x2[h], f2);
 #pragma unroll
-                for (int e = 0; e < kVec; ++e) {
-                    r1[e] = f1[e] * cs[e] - f2[e] * sn[e];
-                    r2[e] = f2[e] * cs[e] + f1[e] * sn[e];
-                }
-                o1 = pack<T>(r1);
-                o2 = pack<T>(r2);
+            for (int e = 0; e < kVec; ++e) {
+                r1[e] = f1[e] * cs[e] - f2[e] * sn[e];
+                r2[e] = f2[e] * cs[e] + f1[e] * sn[e];
             }
+            const u32x4 p1 = pack<T>(r1), p2 = pack<T>(r2);
+            const bool rot = kind[h] < 2 && p_ok;
+            const u32x4 o1 = rot ? p1 : x1[h], o2 = rot ? p2 : x2[h];
             if (C::NTS) {
                 st16_nt<T>(dst, c0, o1);
                 st16_nt<T>(dst, half + c0, o2);

@@ -203,11 +203,12 @@ def test_rope_position_zero_and_out_of_range(kcr):
     qg, cg = rope_case(kcr, dev(q), dev(k), dev(v), positions, cache, slots, 1e6, 64, q_out=q_out)
     # position 0 is the identity (values; +0 and -0 compare equal)
     assert torch.equal(qg[:2].float(), q[:2].float())
-    # tokens with invalid positions are skipped entirely
-    assert bool((qg[3:5] == 7.0).all())
+    # tokens with invalid positions copy their query heads unrotated (bit for
+    # bit) and write nothing to the cache
+    assert torch.equal(qg[3:5].view(torch.int16), q[3:5].view(torch.int16))
     cb = cg.view(torch.int16)
     written = sorted({(b * 16 + o) for _, b, o in (cb != -1).any(dim=(3, 4)).nonzero().tolist()})
-    assert written == [1, 63]  # token 2's slot 64 is out of range, tokens 3/4 skipped, 5 padding
+    assert written == [1, 63]  # token 2's slot 64 is out of range, tokens 3/4 invalid, 5 padding
     assert torch.equal(cg[0, 0, 1].float(), k[0].float()) and torch.equal(cg[1, 3, 15], v[1])
 
 
