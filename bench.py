@@ -110,8 +110,14 @@ def large_shapes(kcr, iters: int):
 
     def run(name, nbytes, fns, shape_desc):
         ev = events(2 * iters)
-        for i in range(2):  # warm-up
+        # warm-up: about 150 ms of the same launches, so clocks have settled
+        t0 = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t0 < 0.15 or i < 4:
             fns[i % len(fns)]()
+            i += 1
+            if i % 16 == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
         for i in range(iters):
             timed_launch(kcr, fns[i % len(fns)], ev[2 * i], ev[2 * i + 1])
@@ -161,6 +167,38 @@ def large_shapes(kcr, iters: int):
     run("swiglu_bf16", swiglu_bytes(8192, 8960, 2), fns, "gate_up [8192, 17920] -> [8192, 8960] bf16")
     del gus, outs, wl
     torch.cuda.empty_cache()
+    return out
+
+
+def graph_op_us(kcr, chain, reps: int):
+    """Per-launch time of each op inside a captured graph of its 28 launches
+    (one per layer, the chain's shapes and buffers), unprofiled."""
+    import torch
+    out = {}
+    for k, name in enumerate(("add_rmsnorm", "rope_kvstore", "add_rmsnorm_2", "swiglu")):
+        fns = [chain_ops(kcr, chain, L)[k][1] for L in chain.layers]
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for f in fns:
+                f()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for f in fns:
+                f()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = events(2)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = e0.elapsed_time(e1) * 1e3 / (reps * len(fns))
+        del g
     return out
 
 
@@ -395,6 +433,9 @@ def main():
 
     floor_us = launch_floor(kcr, 4 * len(chain.layers), max(10, args.steps // 2))
     log(f"launch floor: {floor_us:.2f} us per graph node of a 16-byte copy")
+    op_graph = graph_op_us(kcr, chain, max(10, args.steps // 2))
+    chain.reset_residual()
+    log("in-graph per-launch us: " + ", ".join(f"{k} {v:.2f}" for k, v in op_graph.items()))
     ceiling = copy_ceiling(kcr, args.kernel_iters)
     kernels = {} if args.skip_large else large_shapes(kcr, args.kernel_iters)
 
@@ -428,7 +469,8 @@ def main():
         "event_stamped_kernel_sum_us_per_step": round(kernel_sum_us, 2),
         "launch_floor_us_per_node": round(floor_us, 3),
         "launch_floor_share_of_step": round(4 * len(chain.layers) * floor_us / (ms * 1e3), 4),
-        "op_mean_us": op_us,
+        "op_event_stamped_mean_us": op_us,
+        "op_in_graph_us": {k: round(v, 3) for k, v in op_graph.items()},
         "timed_wall_s": round(wall_s, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,

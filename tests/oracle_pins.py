@@ -337,6 +337,27 @@ def pin_scatter_round_trip(L):
         off += L_seq
 
 
+def pin_gather_golden(L):
+    # Reading back the golden scatter image through a hand block table: the
+    # sequence that owns block 2 then block 0 (block size 2) sees the rows
+    # written at slots 5 and 0 at its positions 1 and 2, and the sentinel at
+    # its never-written positions 0 and 3.
+    c = golden("scatter_hand.json")["cases"][0]
+    for dt in (F32, BF16):
+        cache = _sentinel([2, c["num_blocks"], c["block_size"], c["hkv"], c["d"]], dt)
+        oracle.rope_kvstore(enc(c["k"], dt), enc(c["k"], dt), enc(c["v"], dt),
+                            np.array(c["positions"]), 1e6, cache, np.array(c["slots"]),
+                            block_size=c["block_size"], L=L)
+        def same(a, b):  # bit patterns: the sentinel is a NaN
+            return np.array_equal(np.ascontiguousarray(a).view(np.uint8), np.ascontiguousarray(b).view(np.uint8))
+        sentinel = _sentinel([1, 1, c["d"]], dt)[0]
+        k = oracle.paged_gather(cache, 0, np.array([2, 0]), 4, L=L)
+        v = oracle.paged_gather(cache, 1, np.array([2, 0]), 4, L=L)
+        assert same(k[0], sentinel) and same(k[3], sentinel) and same(v[0], sentinel)
+        assert same(k[1], enc(c["k"][0], dt)) and same(k[2], enc(c["k"][1], dt))
+        assert same(v[1], enc(c["v"][0], dt)) and same(v[2], enc(c["v"][1], dt))
+
+
 def pin_gqa_map(L):
     for c in golden("gqa_map.json")["cases"]:
         got = [oracle.gqa_kv_head(h, c["hq"], c["hkv"], L=L) for h in range(c["hq"])]

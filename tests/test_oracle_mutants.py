@@ -33,6 +33,8 @@ MUTANTS = {
     "bf16_double_rounding": ("double n = rint(a / q);", "double n = rint((double)(float)a / q);"),
     "bf16_truncation": ("double n = rint(a / q);", "double n = floor(a / q);"),
     "gqa_modulo": ("return h / (hq / hkv);", "return h % hkv;"),
+    "gather_offset_from_block": ("int64_t block = block_table[t / block_size], offset = t % block_size;",
+                                 "int64_t block = block_table[t / block_size], offset = (t + 1) % block_size;"),
 }
 
 
