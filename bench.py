@@ -159,6 +159,21 @@ def large_shapes(kcr, iters: int):
     nb = rope_bytes(T, wl["hq"], wl["hkv"], wl["dh"], 2, int(torch.unique(wl["positions"]).numel()))
     run("rope_kvstore_bf16", nb, fns, f"64 seqs, T={T}, 12q/2kv x128, bf16")
     del qkvs, views, cache, qo, wl
+    # paged gather: one decode-chain layer cache read back for 256 sequences x 4096 positions
+    B, L, bs, hkv, dh = 256, 4096, 16, 2, 128
+    g = workloads.gen(0)
+    nbps = L // bs
+    N = B * (nbps + 1) + 64
+    bt = torch.randperm(N, generator=g)[:B * nbps].view(B, nbps).to(dev)
+    lens = torch.full((B,), L, dtype=torch.int64, device=dev)
+    cache = torch.empty((2, N, bs, hkv, dh), dtype=torch.bfloat16, device=dev)
+    outs = [(torch.empty((B, L, hkv, dh), dtype=torch.bfloat16, device=dev),
+             torch.empty((B, L, hkv, dh), dtype=torch.bfloat16, device=dev)) for _ in range(3)]
+    fns = [lambda i=i: kcr.paged_kv_gather(cache, bt, lens, L, k_out=outs[i][0], v_out=outs[i][1])
+           for i in range(3)]
+    run("paged_kv_gather_bf16", 2 * 2 * B * L * hkv * dh * 2 + B * nbps * 8 + B * 8, fns,
+        f"{B} seqs x {L} positions, 2 kv heads x128, bf16")
+    del cache, outs, bt, lens
     wl = workloads.swiglu_fused(rows=8192, inter=8960, dtype="bf16", seed=0)
     gus = [wl["gate_up"].to(dev)]
     gus += [gus[0].clone() for _ in range(2)]

@@ -210,6 +210,36 @@ int kcr_swiglu(const void* gate, int64_t gate_stride, const void* up, int64_t up
                void* stream);
 
 /*
+ * kcr_paged_kv_gather -- read the paged KV cache back into contiguous
+ * per-sequence K and V:
+ *     for b < n_seqs, t < min(seq_lens[b], max_len), with
+ *     slot = block_tables[b, t / block_size] * block_size + t % block_size:
+ *       k_out[b, t, :, :] = kv_cache[0, slot / block_size, slot % block_size, :, :]
+ *       v_out[b, t, :, :] = kv_cache[1, ...]                        (bit copies)
+ *
+ * The read side of the cache: op 19 (cache_kv_read) of the op list in
+ * m.lsln.cn/news/61269 section 2.1, and the vectorized gather of mer.dev
+ * "AsyncT vLLM notes (1)" section 1.4 (token index = block_table *
+ * block_size + offset).
+ *
+ *   kv_cache [2, num_blocks, block_size, n_kv_head, head_dim] contiguous   input
+ *   block_tables [n_seqs, max_blocks_per_seq] int64, row-major             input
+ *   seq_lens [n_seqs] int64                                                input
+ *   k_out, v_out [n_seqs, max_len, n_kv_head, head_dim] contiguous         outputs
+ *
+ * Rows at t >= seq_lens[b], and rows whose block id is outside
+ * [0, num_blocks), are left untouched. n_kv_head * head_dim must be a
+ * multiple of 16 bytes' worth of elements and max_len <= max_blocks_per_seq
+ * * block_size (KCR_ERR_SHAPE); kv_cache, k_out and v_out 16-byte aligned
+ * (KCR_ERR_ALIGN); outputs may not overlap each other or any input
+ * (KCR_ERR_ALIAS).
+ */
+int kcr_paged_kv_gather(const void* kv_cache, int64_t num_blocks, int block_size, int n_kv_head,
+                        int head_dim, const int64_t* block_tables, int64_t max_blocks_per_seq,
+                        const int64_t* seq_lens, int64_t n_seqs, int64_t max_len, void* k_out,
+                        void* v_out, int dtype, void* stream);
+
+/*
  * kcr_copy -- plain streaming copy of `bytes` bytes (a multiple of 16, both
  * pointers 16-byte aligned, no overlap). It moves data with the same 16-byte
  * vector loads and stores as the kernels above and serves as the measured

@@ -41,6 +41,7 @@ _SIGS = {
                          _P, _I64, _I, _I, _I, _I, _I64, _I, _P],
     "kcr_rope_cos_sin": [_P, _P, _I64, _I, _D, _P],
     "kcr_swiglu": [_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I, _P],
+    "kcr_paged_kv_gather": [_P, _I64, _I, _I, _I, _P, _I64, _P, _I64, _I64, _P, _P, _I, _P],
     "kcr_copy": [_P, _P, _I64, _P],
     "kcr_time_next_launch": [_P, _P],
     "kcr_device_cus": [],
@@ -182,6 +183,29 @@ def swiglu_fused(gate_up: torch.Tensor, out: torch.Tensor | None = None) -> torc
     """SwiGLU of a fused [..., 2*I] buffer whose first half is the gate."""
     inter = gate_up.shape[-1] // 2
     return swiglu(gate_up[..., :inter], gate_up[..., inter:], out=out)
+
+
+def paged_kv_gather(kv_cache: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                    max_len: int, k_out: torch.Tensor | None = None,
+                    v_out: torch.Tensor | None = None):
+    """K and V of each sequence, gathered from the paged cache through its
+    block table: returns (k, v), each [n_seqs, max_len, n_kv_head, head_dim].
+    Rows past a sequence's length are left as allocated (uninitialized when
+    the outputs are created here)."""
+    dt = _dt(kv_cache)
+    _, nb, bs, hkv, hd = kv_cache.shape
+    n = block_tables.shape[0]
+    if block_tables.dtype != torch.int64 or seq_lens.dtype != torch.int64:
+        raise TypeError("block_tables and seq_lens must be int64")
+    if not (kv_cache.is_contiguous() and block_tables.is_contiguous() and seq_lens.is_contiguous()):
+        raise ValueError("kv_cache, block_tables and seq_lens must be contiguous")
+    shape = (n, max_len, hkv, hd)
+    k_out = torch.empty(shape, dtype=kv_cache.dtype, device=kv_cache.device) if k_out is None else k_out
+    v_out = torch.empty(shape, dtype=kv_cache.dtype, device=kv_cache.device) if v_out is None else v_out
+    _check("paged_kv_gather", _lib.kcr_paged_kv_gather(
+        kv_cache.data_ptr(), nb, bs, hkv, hd, block_tables.data_ptr(), block_tables.shape[1],
+        seq_lens.data_ptr(), n, max_len, k_out.data_ptr(), v_out.data_ptr(), dt, _stream(kv_cache)))
+    return k_out, v_out
 
 
 def copy_(dst: torch.Tensor, src: torch.Tensor) -> torch.Tensor:

@@ -36,6 +36,7 @@ def lib():
     L.kcr_rope_cos_sin.argtypes = [P, P, I64, I, D, P]
     L.kcr_swiglu.argtypes = [P, I64, P, I64, P, I64, I64, I64, I, P]
     L.kcr_copy.argtypes = [P, P, I64, P]
+    L.kcr_paged_kv_gather.argtypes = [P, I64, I, I, I, P, I64, P, I64, I64, P, P, I, P]
     L.kcr_strerror.argtypes = [I]
     L.kcr_strerror.restype = ctypes.c_char_p
     L.kcr_version.restype = ctypes.c_char_p
@@ -136,6 +137,28 @@ def test_swiglu_validation(lib):
     assert f(A, 2 * I, A + 2 * I, 2 * I, A + 16, 2 * I, 4, I, BF16, None) == ALIAS
     # fused halves as inputs, separate output: fine
     assert f(A, 2 * I, A + 2 * I, 2 * I, A * 64, I, 4, I, BF16, None) in (DEVICE, OK)
+
+
+def test_gather_validation(lib):
+    f = lib.kcr_paged_kv_gather
+    # cache, blocks, bs, hkv, hd, tables, max blocks/seq, lens, seqs, max_len, k_out, v_out, dtype
+    ok = dict(c=A, nb=64, bs=16, hkv=2, hd=128, bt=A * 2, mb=8, ln=A * 3, n=4, ml=128, k=A * 4,
+              v=A * 5, dt=BF16)
+
+    def g(**kw):
+        a = dict(ok, **kw)
+        return f(a["c"], a["nb"], a["bs"], a["hkv"], a["hd"], a["bt"], a["mb"], a["ln"], a["n"],
+                 a["ml"], a["k"], a["v"], a["dt"], None)
+    assert g() in (DEVICE, OK)
+    assert g(dt=2) == DTYPE
+    assert g(hkv=1, hd=4) == SHAPE             # 4 bf16 per row: not a 16-byte multiple
+    assert g(ml=129) == SHAPE                  # more positions than the table can name
+    assert g(n=0, c=None, bt=None) == OK
+    assert g(ln=None) == NULL
+    assert g(k=A * 4 + 8) == ALIGN
+    assert g(bt=A * 2 + 4) == ALIGN
+    assert g(v=A * 4) == ALIAS
+    assert g(k=A + 64) == ALIAS                # output over the cache
 
 
 def test_copy_validation(lib):

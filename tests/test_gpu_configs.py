@@ -187,3 +187,28 @@ def test_large_rope_sampled(kcr):
     assert_rope_close(qo.cpu()[toks].double().numpy(), q_rot, torch.bfloat16, "sampled q_out")
     k_got = flat[0][slots[torch.from_numpy(toks).cuda()]].cpu().double().numpy()
     assert_rope_close(k_got, k_rot, torch.bfloat16, "sampled K slots")
+
+
+def test_large_paged_gather_sampled(kcr):
+    """The benchmark's gather shape: 256 sequences x 4096 cached positions of
+    one decode-chain layer cache, every K/V row checked bit for bit against a
+    torch index gather on the device, sampled rows against the oracle."""
+    say("large paged gather 256 x 4096")
+    wl = workloads.decode_chain(layers=1, seed=0)
+    lay = wl["layout"]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9)
+    cache = torch.randn(wl["cache_shape"], generator=g, device="cuda").to(torch.bfloat16)
+    bt = torch.stack(lay.block_tables).cuda()
+    lens = torch.full((len(lay.block_tables),), 4096, dtype=torch.int64, device="cuda")
+    k, v = kcr.paged_kv_gather(cache, bt, lens, 4096)
+    bs = wl["block_size"]
+    pos = torch.arange(4096, device="cuda")
+    slots = bt[:, pos // bs] * bs + pos % bs                      # [256, 4096]
+    flat = cache.view(2, -1, wl["hkv"], wl["dh"])
+    assert torch.equal(k.view(torch.int16), flat[0][slots].view(torch.int16))
+    assert torch.equal(v.view(torch.int16), flat[1][slots].view(torch.int16))
+    c = np_bits(cache.cpu())
+    for b in (0, 131, 255):
+        ref = oracle.paged_gather(c, 0, lay.block_tables[b].numpy(), 4096)
+        assert np.array_equal(np_bits(k[b].cpu()), ref)

@@ -223,6 +223,45 @@ def test_rope_table(kcr):
             assert np.all(err <= np.abs(ref) * 2.0 ** -24 + 1e-10), float(err.max())
 
 
+# ---------------------------------------------------------- paged KV gather
+@pytest.mark.parametrize("dt", DTS, ids=DT_ID.get)
+@pytest.mark.parametrize("bs", [16, 7])
+def test_paged_kv_gather(kcr, dt, bs):
+    say(f"paged gather dt={dt} block_size={bs}")
+    wl = workloads.prefill(n_seqs=5, len_lo=1, len_hi=90, dtype=dt, seed=41 + bs, block_size=bs)
+    cos, sin = kcr.rope_cos_sin(wl["max_pos"], wl["dh"], wl["theta"])
+    cache = dev(wl["cache"])
+    kcr.rope_kvstore(*gpu_qkv(wl), dev(wl["positions"]), cos, sin, cache, dev(wl["slot_mapping"]))
+    lay = wl["layout"]
+    n, max_len = len(lay.lens), max(lay.lens) + 3
+    mb = (max_len + bs - 1) // bs
+    bt = torch.full((n, mb), -1, dtype=torch.int64)
+    for i, t in enumerate(lay.block_tables):
+        bt[i, :len(t)] = t
+    lens = torch.tensor(lay.lens, dtype=torch.int64)
+    fill = workloads.sentinel_cache([2, n, max_len, wl["hkv"], wl["dh"]], dt).to("cuda")
+    k, v = kcr.paged_kv_gather(cache, dev(bt), dev(lens), max_len, k_out=fill[0], v_out=fill[1])
+    c = np_bits(cache.cpu())
+    for i, L in enumerate(lay.lens):
+        for which, got in ((0, k), (1, v)):
+            ref = oracle.paged_gather(c, which, bt[i, :len(lay.block_tables[i])].numpy(), L)
+            g = np_bits(got[i].cpu())
+            assert np.array_equal(g[:L].view(np.uint8), ref.view(np.uint8)), (i, which)
+            assert (g[L:].view(np.uint8) == 0xFF).all(), "rows past the length must stay untouched"
+
+
+def test_paged_kv_gather_bad_block_skipped(kcr):
+    hkv, dh, bs, nb = 2, 128, 16, 4
+    cache = torch.randn((2, nb, bs, hkv, dh), generator=workloads.gen(5)).to(torch.bfloat16).cuda()
+    bt = torch.tensor([[1, 99], [-3, 2]], dtype=torch.int64).cuda()   # 99 and -3 are invalid
+    lens = torch.tensor([32, 32], dtype=torch.int64).cuda()
+    k = torch.zeros((2, 32, hkv, dh), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros_like(k)
+    kcr.paged_kv_gather(cache, bt, lens, 32, k_out=k, v_out=v)
+    assert torch.equal(k[0, :16], cache[0, 1]) and torch.equal(v[1, 16:], cache[1, 2])
+    assert bool((k[0, 16:] == 0).all()) and bool((v[1, :16] == 0).all())
+
+
 # ------------------------------------------------------------------ SwiGLU
 @pytest.mark.parametrize("dt", DTS, ids=DT_ID.get)
 @pytest.mark.parametrize("rows,cols", [(1, 1), (3, 7), (1, 8960), (5, 8961), (300, 100),
