@@ -51,6 +51,8 @@ def _bind(lib):
         "orc_rope_angles": (None, [P, P, I64, I, D]),
         "orc_rope_kvstore": (None, [P, I64, I64, P, I64, I64, P, I64, I64, P, D, P, P, P, P,
                                     I64, I, I, I, I, I64, I]),
+        "orc_qknorm_rope_kvstore": (None, [P, I64, I64, P, I64, I64, P, I64, I64, P, P, D, P, D, P,
+                                           P, P, P, I64, I, I, I, I, I64, I]),
         "orc_gqa_kv_head": (I, [I, I, I]),
         "orc_paged_gather": (None, [P, I, P, I64, I, I, I, I64, P, I]),
         "orc_swiglu": (None, [P, I64, P, I64, P, I64, I64, I64, I]),
@@ -156,6 +158,7 @@ def rope_kvstore(q: np.ndarray, k: np.ndarray, v: np.ndarray, positions: np.ndar
     L = L or lib()
     T, hq, d = q.shape
     hkv = k.shape[1]
+    assert d <= 1024
     qs, ks, vs = _elem_strides(q), _elem_strides(k), _elem_strides(v)
     positions = np.ascontiguousarray(positions, dtype=np.int64)
     q_rot = np.empty((T, hq, d), dtype=np.float64)
@@ -171,6 +174,32 @@ def rope_kvstore(q: np.ndarray, k: np.ndarray, v: np.ndarray, positions: np.ndar
     L.orc_rope_kvstore(_ptr(q), qs[0], qs[1], _ptr(k), ks[0], ks[1], _ptr(v), vs[0], vs[1],
                        _ptr(positions), float(theta), _ptr(q_rot), _ptr(k_rot), cptr, sptr,
                        T, hq, hkv, d, block_size, nb, _code(q))
+    return q_rot, k_rot
+
+
+def qknorm_rope_kvstore(q, k, v, q_w, k_w, eps, positions, theta, cache, slot_mapping,
+                        block_size: int = 16, L=None):
+    """As rope_kvstore, with per-head RMSNorm of every Q head (weight q_w) and
+    K head (weight k_w) before the rotation. Returns (q_rot, k_rot)."""
+    L = L or lib()
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    assert d <= 1024
+    qs, ks, vs = _elem_strides(q), _elem_strides(k), _elem_strides(v)
+    positions = np.ascontiguousarray(positions, dtype=np.int64)
+    q_w, k_w = np.ascontiguousarray(q_w), np.ascontiguousarray(k_w)
+    q_rot = np.empty((T, hq, d), dtype=np.float64)
+    k_rot = np.empty((T, hkv, d), dtype=np.float64)
+    if cache is not None:
+        assert cache.flags.c_contiguous and cache.dtype == q.dtype and cache.shape[2] == block_size
+        slot_mapping = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+        nb, cptr, sptr = cache.shape[1], _ptr(cache), _ptr(slot_mapping)
+    else:
+        nb, cptr, sptr = 0, None, None
+    L.orc_qknorm_rope_kvstore(_ptr(q), qs[0], qs[1], _ptr(k), ks[0], ks[1], _ptr(v), vs[0], vs[1],
+                              _ptr(q_w), _ptr(k_w), float(eps), _ptr(positions), float(theta),
+                              _ptr(q_rot), _ptr(k_rot), cptr, sptr, T, hq, hkv, d, block_size, nb,
+                              _code(q))
     return q_rot, k_rot
 
 

@@ -181,29 +181,57 @@ void orc_rope_angles(double* cos_out, double* sin_out, int64_t max_pos, int head
         }
 }
 
-/* Rotate-half RoPE of one head: element i pairs with element i + d/2;
+/* Rotate-half RoPE of one head given in double: element i pairs with
+ * element i + d/2;
  *   out_i       = x_i * cos - x_{i+d/2} * sin
  *   out_{i+d/2} = x_{i+d/2} * cos + x_i * sin                              */
-static void rope_head(const void* x, int64_t x_off, double* out, int64_t p, int d,
-                      double base, int dtype) {
+static void rotate_half(const double* x, double* out, int64_t p, int d, double base) {
     int half = d / 2;
     for (int i = 0; i < half; ++i) {
         double a = rope_angle(p, i, d, base);
         double c = cos(a), s = sin(a);
-        double x1 = load(x, x_off + i, dtype);
-        double x2 = load(x, x_off + i + half, dtype);
+        double x1 = x[i];
+        double x2 = x[i + half];
         out[i] = x1 * c - x2 * s;
         out[i + half] = x2 * c + x1 * s;
     }
 }
 
+/* One head read from its storage dtype and rotated. d <= 1024. */
+static void rope_head(const void* x, int64_t x_off, double* out, int64_t p, int d, double base,
+                      int dtype) {
+    double v[1024];
+    for (int e = 0; e < d; ++e) v[e] = load(x, x_off + e, dtype);
+    rotate_half(v, out, p, d, base);
+}
+
+/* The store: for each token whose slot is in [0, num_blocks * block_size):
+ * block = slot / block_size, offset = slot % block_size,
+ * cache[0, block, offset, h, :] = round(k_rot) and cache[1, block, offset, h,
+ * :] = v (bit copy). Negative slots mark padding tokens and are skipped; the
+ * scatter runs in token order, so with repeated slots the last token wins.
+ * No other cache element is touched. */
+static void scatter_kv(const double* k_rot, const void* v, int64_t v_ts, int64_t v_hs, void* cache,
+                       const int64_t* slot_mapping, int64_t T, int hkv, int d, int block_size,
+                       int64_t num_blocks, int dtype) {
+    int64_t n_slots = num_blocks * (int64_t)block_size;
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t slot = slot_mapping[t];
+        if (slot < 0 || slot >= n_slots) continue;
+        int64_t block = slot / block_size, offset = slot % block_size;
+        for (int h = 0; h < hkv; ++h) {
+            int64_t k_dst = (((0 * num_blocks + block) * block_size + offset) * hkv + h) * d;
+            int64_t v_dst = (((1 * num_blocks + block) * block_size + offset) * hkv + h) * d;
+            for (int e = 0; e < d; ++e) {
+                store(cache, k_dst + e, k_rot[(t * hkv + h) * d + e], dtype);
+                copy_bits(cache, v_dst + e, v, t * v_ts + h * v_hs + e, dtype);
+            }
+        }
+    }
+}
+
 /* Q and K heads rotated at positions[t]; q_rot [T, hq, d] and k_rot
- * [T, hkv, d] in double. Then, for each token whose slot is in
- * [0, num_blocks * block_size): block = slot / block_size,
- * offset = slot % block_size, cache[0, block, offset, h, :] = round(k_rot)
- * and cache[1, block, offset, h, :] = v (bit copy). Negative slots mark
- * padding tokens and are skipped; the scatter runs in token order, so with
- * repeated slots the last token wins. No other cache element is touched. */
+ * [T, hkv, d] in double; then the store above when a cache is given. */
 void orc_rope_kvstore(const void* q, int64_t q_ts, int64_t q_hs,
                       const void* k, int64_t k_ts, int64_t k_hs,
                       const void* v, int64_t v_ts, int64_t v_hs,
@@ -220,21 +248,52 @@ void orc_rope_kvstore(const void* q, int64_t q_ts, int64_t q_hs,
         for (int h = 0; h < hkv; ++h)
             rope_head(k, t * k_ts + h * k_hs, k_rot + (t * hkv + h) * d, p, d, base, dtype);
     }
-    if (cache == 0) return;
-    int64_t n_slots = num_blocks * (int64_t)block_size;
+    if (cache != 0)
+        scatter_kv(k_rot, v, v_ts, v_hs, cache, slot_mapping, T, hkv, d, block_size, num_blocks, dtype);
+}
+
+/* Per-head RMSNorm of a query or key head (the qk-norm applied to the
+ * narrow Q/K views of a fused QKV projection, mer.dev notes sections 0 and
+ * 3.3; RMSNorm as in the koas-w post, section 3):
+ * n_e = x_e / sqrt(sum_e x_e^2 / d + eps) * w_e. */
+static void rms_norm_head(const void* x, int64_t x_off, const void* w, double eps, int d, int dtype,
+                          double* n) {
+    double sum_sq = 0.0;
+    for (int e = 0; e < d; ++e) {
+        double v = load(x, x_off + e, dtype);
+        sum_sq += v * v;
+    }
+    double r = 1.0 / sqrt(sum_sq / (double)d + eps);
+    for (int e = 0; e < d; ++e) n[e] = load(x, x_off + e, dtype) * r * load(w, e, dtype);
+}
+
+/* As orc_rope_kvstore, with every query head normalised by q_w and every
+ * key head by k_w (each [d], eps added to the mean square) before the
+ * rotation; V is stored unchanged. d <= 1024. */
+void orc_qknorm_rope_kvstore(const void* q, int64_t q_ts, int64_t q_hs,
+                             const void* k, int64_t k_ts, int64_t k_hs,
+                             const void* v, int64_t v_ts, int64_t v_hs,
+                             const void* q_w, const void* k_w, double eps,
+                             const int64_t* positions, double base,
+                             double* q_rot, double* k_rot,
+                             void* cache, const int64_t* slot_mapping,
+                             int64_t T, int hq, int hkv, int d, int block_size,
+                             int64_t num_blocks, int dtype) {
+#pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < T; ++t) {
-        int64_t slot = slot_mapping[t];
-        if (slot < 0 || slot >= n_slots) continue;
-        int64_t block = slot / block_size, offset = slot % block_size;
+        int64_t p = positions[t];
+        double n[1024];
+        for (int h = 0; h < hq; ++h) {
+            rms_norm_head(q, t * q_ts + h * q_hs, q_w, eps, d, dtype, n);
+            rotate_half(n, q_rot + (t * hq + h) * d, p, d, base);
+        }
         for (int h = 0; h < hkv; ++h) {
-            int64_t k_dst = (((0 * num_blocks + block) * block_size + offset) * hkv + h) * d;
-            int64_t v_dst = (((1 * num_blocks + block) * block_size + offset) * hkv + h) * d;
-            for (int e = 0; e < d; ++e) {
-                store(cache, k_dst + e, k_rot[(t * hkv + h) * d + e], dtype);
-                copy_bits(cache, v_dst + e, v, t * v_ts + h * v_hs + e, dtype);
-            }
+            rms_norm_head(k, t * k_ts + h * k_hs, k_w, eps, d, dtype, n);
+            rotate_half(n, k_rot + (t * hkv + h) * d, p, d, base);
         }
     }
+    if (cache != 0)
+        scatter_kv(k_rot, v, v_ts, v_hs, cache, slot_mapping, T, hkv, d, block_size, num_blocks, dtype);
 }
 
 /* GQA: query head h reads the KV head h / (hq / hkv) (koas-w post,

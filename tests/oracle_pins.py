@@ -278,6 +278,65 @@ def pin_rope_strided_views(L):
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+# ------------------------------------------------ qk-norm + RoPE pins
+def pin_qknorm_rope_golden(L):
+    for c in golden("qknorm_rope_hand.json")["cases"]:
+        for dt in (F32, BF16):
+            d = len(c["x"])
+            x = enc(np.array(c["x"]).reshape(1, 1, d), dt)
+            w = enc(c["w"], dt)
+            qr, kr = oracle.qknorm_rope_kvstore(x, x, x, w, w, c["eps"], np.array([c["pos"]]),
+                                                c["theta"], None, None, L=L)
+            assert np.allclose(qr[0, 0], c["out"], rtol=1e-13, atol=1e-15), (c, qr)
+            assert np.array_equal(qr, kr)
+
+
+def pin_qknorm_rope_energy(L):
+    # Unit weight: the norm scales each head to mean square ms/(ms+eps) and the
+    # rotation keeps every pair's norm, so sum(out^2) = d * ms / (ms + eps).
+    q, k = _heads(3, 12, 128, BF16, 31), _heads(3, 2, 128, BF16, 32)
+    ones = enc(np.ones(128), BF16)
+    for eps in (0.0, 0.7):
+        qr, kr = oracle.qknorm_rope_kvstore(q, k, k, ones, ones, eps, np.array([5, 900, 4096]), 1e6,
+                                            None, None, L=L)
+        for got, x in ((qr, dec(q)), (kr, dec(k))):
+            ms = np.mean(x ** 2, axis=-1)
+            assert np.allclose(np.sum(got ** 2, axis=-1), 128 * ms / (ms + eps), rtol=1e-12)
+
+
+def pin_qknorm_rope_is_rope_of_rms_norm(L):
+    # Position by position, the result is the complex rotation of torch's
+    # float64 rms_norm of each head, with separate Q and K weights.
+    T, d = 4, 64
+    q, k = _heads(T, 3, d, F32, 33), _heads(T, 1, d, F32, 34)
+    rng = np.random.default_rng(35)
+    wq, wk = enc(1 + 0.1 * rng.standard_normal(d), F32), enc(0.5 + rng.random(d), F32)
+    pos = np.array([0, 3, 77, 2048])
+    qr, kr = oracle.qknorm_rope_kvstore(q, k, k, wq, wk, 1e-6, pos, 1e4, None, None, L=L)
+    ang = pos[:, None, None] * 1e4 ** (-np.arange(d // 2) * 2.0 / d)[None, None, :]
+    for got, x, w in ((qr, dec(q), dec(wq)), (kr, dec(k), dec(wk))):
+        n = F.rms_norm(torch.from_numpy(x), (d,), torch.from_numpy(w), eps=1e-6).numpy()
+        z = (n[..., : d // 2] + 1j * n[..., d // 2:]) * np.exp(1j * ang)
+        assert np.allclose(got, np.concatenate([z.real, z.imag], axis=-1), rtol=1e-10, atol=1e-12)
+
+
+def pin_qknorm_rope_store(L):
+    # The cache holds round(normed, rotated K) at the named slots and V as is;
+    # q_out and the cache image agree with the plain store for identical K.
+    wl = workloads.prefill(n_seqs=2, len_lo=3, len_hi=20, seed=36)
+    q, k, v = (np_bits(t) for t in (wl["q"], wl["k"], wl["v"]))
+    ones = enc(np.ones(128), BF16)
+    cache = np_bits(wl["cache"]).copy()
+    _, k_rot = oracle.qknorm_rope_kvstore(q, k, v, ones, ones, 0.0, wl["positions"].numpy(),
+                                          wl["theta"], cache, wl["slot_mapping"].numpy(), L=L)
+    flat = cache.reshape(2, -1, 2, 128)
+    slots = wl["slot_mapping"].numpy()
+    assert np.array_equal(flat[1][slots], np.ascontiguousarray(v))
+    got = dec(flat[0][slots])
+    assert np.all(np.abs(got - k_rot) <= np.abs(k_rot) * 2.0 ** -8 + 1e-300)
+    assert int((flat == 0xFFFF).sum()) == flat.size - 2 * len(slots) * 2 * 128
+
+
 # ----------------------------------------------------- cache scatter pins
 def _sentinel(shape, dt):
     return np_bits(workloads.sentinel_cache(shape, TORCH_DT[dt]))

@@ -19,11 +19,11 @@ MUTANTS = {
     "residual_not_stored": ("            store(x, r * x_stride + j, s, dtype);\n", ""),
     "rope_sign": ("out[i] = x1 * c - x2 * s;", "out[i] = x1 * c + x2 * s;"),
     "rope_sin_cos_swapped": ("double c = cos(a), s = sin(a);", "double c = sin(a), s = cos(a);"),
-    "rope_adjacent_pairs": ("double x2 = load(x, x_off + i + half, dtype);",
-                            "double x2 = load(x, x_off + (i ^ 1), dtype);"),
+    "rope_adjacent_pairs": ("double x2 = x[i + half];", "double x2 = x[i ^ 1];"),
     "rope_frequency_exponent": ("pow(base, -2.0 * (double)i / (double)d)",
                                 "pow(base, -1.0 * (double)i / (double)d)"),
     "rope_k_head_stride": ("rope_head(k, t * k_ts + h * k_hs,", "rope_head(k, t * k_ts + 0 * k_hs,"),
+    "qknorm_k_head_stride": ("rms_norm_head(k, t * k_ts + h * k_hs,", "rms_norm_head(k, t * k_ts + 0 * k_hs,"),
     "kv_halves_swapped": ("(((0 * num_blocks + block)", "(((1 * num_blocks + block)"),
     "skip_zero_slot": ("if (slot < 0 || slot >= n_slots) continue;",
                        "if (slot <= 0 || slot >= n_slots) continue;"),
@@ -32,6 +32,14 @@ MUTANTS = {
                           "out[r * out_stride + c] = g * sigmoid;"),
     "bf16_double_rounding": ("double n = rint(a / q);", "double n = rint((double)(float)a / q);"),
     "bf16_truncation": ("double n = rint(a / q);", "double n = floor(a / q);"),
+    "qknorm_eps_dropped": ("double r = 1.0 / sqrt(sum_sq / (double)d + eps);",
+                           "double r = 1.0 / sqrt(sum_sq / (double)d);"),
+    "qknorm_weight_of_q_for_k": ("rms_norm_head(k, t * k_ts + h * k_hs, k_w,",
+                                 "rms_norm_head(k, t * k_ts + h * k_hs, q_w,"),
+    "qknorm_weight_reversed": ("n[e] = load(x, x_off + e, dtype) * r * load(w, e, dtype);",
+                               "n[e] = load(x, x_off + e, dtype) * r * load(w, d - 1 - e, dtype);"),
+    "qknorm_rotate_before_norm_skipped": ("            rotate_half(n, k_rot + (t * hkv + h) * d, p, d, base);",
+                                          "            for (int e = 0; e < d; ++e) k_rot[(t * hkv + h) * d + e] = n[e];"),
     "gqa_modulo": ("return h / (hq / hkv);", "return h % hkv;"),
     "gather_offset_from_block": ("int64_t block = block_table[t / block_size], offset = t % block_size;",
                                  "int64_t block = block_table[t / block_size], offset = (t + 1) % block_size;"),
