@@ -158,6 +158,12 @@ def large_shapes(kcr, iters: int):
     fns = [lambda i=i: kcr.rope_kvstore(*views[i], pos, cos, sin, cache, slots, q_out=qo[i]) for i in range(3)]
     nb = rope_bytes(T, wl["hq"], wl["hkv"], wl["dh"], 2, int(torch.unique(wl["positions"]).numel()))
     run("rope_kvstore_bf16", nb, fns, f"64 seqs, T={T}, 12q/2kv x128, bf16")
+    wq = torch.ones(wl["dh"], dtype=torch.bfloat16, device=dev)
+    wk = torch.ones(wl["dh"], dtype=torch.bfloat16, device=dev)
+    fns = [lambda i=i: kcr.qknorm_rope_kvstore(*views[i], wq, wk, 1e-6, pos, cos, sin, cache, slots,
+                                               q_out=qo[i]) for i in range(3)]
+    run("qknorm_rope_kvstore_bf16", nb + 2 * wl["dh"] * 2, fns,
+        f"64 seqs, T={T}, 12q/2kv x128, per-head Q/K RMSNorm, bf16")
     del qkvs, views, cache, qo, wl
     # paged gather: one decode-chain layer cache read back for 256 sequences x 4096 positions
     B, L, bs, hkv, dh = 256, 4096, 16, 2, 128

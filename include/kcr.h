@@ -173,6 +173,29 @@ int kcr_rope_kvstore(const void* q, int64_t q_tok_stride, int64_t q_head_stride,
                      int head_dim, int block_size, int64_t num_blocks, int dtype, void* stream);
 
 /*
+ * kcr_qknorm_rope_kvstore -- kcr_rope_kvstore with a per-head RMSNorm of
+ * every query and key head before the rotation:
+ *     x <- x * (sum_e x_e^2 / head_dim + eps)^(-1/2) * w
+ * with w = q_norm_w [head_dim] for query heads and k_norm_w [head_dim] for
+ * key heads (activation dtype, 16-byte aligned); V is stored unchanged. The
+ * normalised head stays in fp32 through the rotation and is rounded once.
+ *
+ * The qk-norm that mer.dev "AsyncT vLLM notes (1)" counts among the model's
+ * RMSNorms (section 0) and runs on the narrow [N, H, D] Q/K views of the
+ * fused QKV projection (section 3.3); RMSNorm as in the koas-w.github.io
+ * 2026-03-31 post, section 3. Every other argument, limit and error is as
+ * for kcr_rope_kvstore; the weights may not overlap q_out or the cache.
+ */
+int kcr_qknorm_rope_kvstore(const void* q, int64_t q_tok_stride, int64_t q_head_stride,
+                            const void* k, int64_t k_tok_stride, int64_t k_head_stride,
+                            const void* v, int64_t v_tok_stride, int64_t v_head_stride,
+                            const void* q_norm_w, const void* k_norm_w, float eps, void* q_out,
+                            const int64_t* positions, const float* cos_tab, const float* sin_tab,
+                            int64_t max_pos, void* kv_cache, const int64_t* slot_mapping, int64_t T,
+                            int n_head, int n_kv_head, int head_dim, int block_size,
+                            int64_t num_blocks, int dtype, void* stream);
+
+/*
  * kcr_rope_cos_sin -- fill the RoPE tables on the device:
  *     cos_tab[p, i] = cos(p * theta^(-2i/head_dim)),  sin_tab likewise,
  * for p < max_pos and i < head_dim/2, evaluated in fp64 and rounded once

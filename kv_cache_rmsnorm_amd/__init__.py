@@ -39,6 +39,8 @@ _SIGS = {
     "kcr_add_rmsnorm": [_P, _I64, _P, _I64, _P, _P, _I64, _I64, _I64, _F, _I, _P],
     "kcr_rope_kvstore": [_P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _P, _P, _P, _P, _I64, _P,
                          _P, _I64, _I, _I, _I, _I, _I64, _I, _P],
+    "kcr_qknorm_rope_kvstore": [_P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _P, _P, _F, _P, _P,
+                                _P, _P, _I64, _P, _P, _I64, _I, _I, _I, _I, _I64, _I, _P],
     "kcr_rope_cos_sin": [_P, _P, _I64, _I, _D, _P],
     "kcr_swiglu": [_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I, _P],
     "kcr_paged_kv_gather": [_P, _I64, _I, _I, _I, _P, _I64, _P, _I64, _I64, _P, _P, _I, _P],
@@ -131,12 +133,7 @@ def add_rmsnorm(x: torch.Tensor, delta: torch.Tensor, w: torch.Tensor, eps: floa
     return y
 
 
-def rope_kvstore(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, positions: torch.Tensor,
-                 cos: torch.Tensor, sin: torch.Tensor, kv_cache: torch.Tensor,
-                 slot_mapping: torch.Tensor, q_out: torch.Tensor | None = None) -> torch.Tensor:
-    """q [T,Hq,D], k/v [T,Hkv,D] (views allowed), positions/slot_mapping [T]
-    int64, cos/sin [max_pos, D/2] fp32, kv_cache [2, blocks, block_size, Hkv, D].
-    Returns q_out [T,Hq,D] (contiguous); K_rot and V land in kv_cache."""
+def _rope_checks(q, k, v, positions, cos, sin, kv_cache, slot_mapping, q_out):
     dt = _dt(q, k, v, kv_cache)
     T, hq, hd = q.shape
     hkv = k.shape[1]
@@ -151,11 +148,39 @@ def rope_kvstore(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, positions: t
         raise ValueError("kv_cache must be [2, num_blocks, block_size, n_kv_head, head_dim]")
     if q_out is None:
         q_out = torch.empty((T, hq, hd), dtype=q.dtype, device=q.device)
+    return dt, T, hq, hkv, hd, q_out
+
+
+def rope_kvstore(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, positions: torch.Tensor,
+                 cos: torch.Tensor, sin: torch.Tensor, kv_cache: torch.Tensor,
+                 slot_mapping: torch.Tensor, q_out: torch.Tensor | None = None) -> torch.Tensor:
+    """q [T,Hq,D], k/v [T,Hkv,D] (views allowed), positions/slot_mapping [T]
+    int64, cos/sin [max_pos, D/2] fp32, kv_cache [2, blocks, block_size, Hkv, D].
+    Returns q_out [T,Hq,D] (contiguous); K_rot and V land in kv_cache."""
+    dt, T, hq, hkv, hd, q_out = _rope_checks(q, k, v, positions, cos, sin, kv_cache, slot_mapping, q_out)
     _check("rope_kvstore", _lib.kcr_rope_kvstore(
         q.data_ptr(), q.stride(0), q.stride(1), k.data_ptr(), k.stride(0), k.stride(1),
         v.data_ptr(), v.stride(0), v.stride(1), q_out.data_ptr(), positions.data_ptr(),
         cos.data_ptr(), sin.data_ptr(), cos.shape[0], kv_cache.data_ptr(), slot_mapping.data_ptr(),
         T, hq, hkv, hd, kv_cache.shape[2], kv_cache.shape[1], dt, _stream(q)))
+    return q_out
+
+
+def qknorm_rope_kvstore(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_norm_w: torch.Tensor,
+                        k_norm_w: torch.Tensor, eps: float, positions: torch.Tensor,
+                        cos: torch.Tensor, sin: torch.Tensor, kv_cache: torch.Tensor,
+                        slot_mapping: torch.Tensor, q_out: torch.Tensor | None = None) -> torch.Tensor:
+    """rope_kvstore with a per-head RMSNorm of every Q head (weight q_norm_w)
+    and K head (weight k_norm_w) before the rotation."""
+    dt, T, hq, hkv, hd, q_out = _rope_checks(q, k, v, positions, cos, sin, kv_cache, slot_mapping, q_out)
+    if q_norm_w.dtype != q.dtype or k_norm_w.dtype != q.dtype:
+        raise TypeError("norm weights must have the activation dtype")
+    _check("qknorm_rope_kvstore", _lib.kcr_qknorm_rope_kvstore(
+        q.data_ptr(), q.stride(0), q.stride(1), k.data_ptr(), k.stride(0), k.stride(1),
+        v.data_ptr(), v.stride(0), v.stride(1), q_norm_w.data_ptr(), k_norm_w.data_ptr(), float(eps),
+        q_out.data_ptr(), positions.data_ptr(), cos.data_ptr(), sin.data_ptr(), cos.shape[0],
+        kv_cache.data_ptr(), slot_mapping.data_ptr(), T, hq, hkv, hd, kv_cache.shape[2],
+        kv_cache.shape[1], dt, _stream(q)))
     return q_out
 
 

@@ -214,6 +214,19 @@ __device__ __forceinline__ float wave_sum(float v) {
     return (r0 + r1) + (r2 + r3);
 }
 
+// Sum over each aligned group of N consecutive lanes (N a power of two up to
+// 64); every lane of a group must be active and each gets its group's sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+    if constexpr (N >= 2) v += dpp<kDppQuadXor1>(v);
+    if constexpr (N >= 4) v += dpp<kDppQuadXor2>(v);
+    if constexpr (N >= 8) v += dpp<kDppRowHalfMirror>(v);
+    if constexpr (N >= 16) v += dpp<kDppRowMirror>(v);
+    if constexpr (N >= 32) v += __shfl_xor(v, 16);
+    if constexpr (N >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+
 // Wave index made explicitly uniform, so that row and unit indices derived
 // from it live in scalar registers.
 __device__ __forceinline__ int wave_id() {

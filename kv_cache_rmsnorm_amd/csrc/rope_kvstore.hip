@@ -44,6 +44,9 @@ struct RopeArgs {
     const int64_t* slots;
     const float* cos_t;
     const float* sin_t;
+    const void* q_w;  // qk-norm weights [dh] (QKN only)
+    const void* k_w;
+    float eps;
     int64_t q_ts, q_hs, k_ts, k_hs, v_ts, v_hs;  // elements
     int64_t max_pos, n_slots;
     uint32_t units;   // T * units per token
@@ -64,8 +67,12 @@ struct RopeCfg {
 
 // Virtual heads of a token, in KV-group order: for group g (kv_head g), the
 // query heads g*G .. g*G+G-1 (exactly those with head / G == g), then K head
-// g, then V head g.
-template <typename T, typename C>
+// g, then V head g. With QKN every Q and K head is first RMS-normalised with
+// its weight (the qk-norm of the Q/K views of a fused QKV projection, mer.dev
+// "AsyncT vLLM notes (1)", sections 0 and 3.3): the unit's lanes reduce the
+// head's sum of squares with DPP, so all of them stay active (lanes past the
+// head's last chunk read chunk 0 and count zero).
+template <typename T, typename C, bool QKN>
 __global__ __launch_bounds__(256) void rope_kvstore_kernel(const RopeArgs a) {
     using S = typename T::storage;
     constexpr int kVec = T::kVec, LPU = C::LPU, HPU = C::HPU;
@@ -73,9 +80,8 @@ __global__ __launch_bounds__(256) void rope_kvstore_kernel(const RopeArgs a) {
     const int c = threadIdx.x % LPU;
     const int half = a.dh >> 1;
     const bool lane_on = c * kVec < half;
-    const int64_t c0 = (int64_t)c * kVec;
-
-    if (!lane_on) return;
+    if (!QKN && !lane_on) return;
+    const int64_t c0 = lane_on ? (int64_t)c * kVec : 0;
     for (uint32_t u = blockIdx.x * UPW + threadIdx.x / LPU; u < a.units; u += gridDim.x * UPW) {
         const uint32_t t = fastdiv(u, a.upt);
         const int j0 = (int)(u - t * a.upt.d) * HPU;
@@ -119,6 +125,14 @@ __global__ __launch_bounds__(256) void rope_kvstore_kernel(const RopeArgs a) {
         const int64_t pc = p_ok ? p : 0;
         const bool store_kv = p_ok && slot >= 0 && slot < a.n_slots;
 
+        float wq1[kVec], wq2[kVec], wk1[kVec], wk2[kVec];
+        if constexpr (QKN) {
+            unpack<T>(ld16<T>(a.q_w, c0), wq1);
+            unpack<T>(ld16<T>(a.q_w, half + c0), wq2);
+            unpack<T>(ld16<T>(a.k_w, c0), wk1);
+            unpack<T>(ld16<T>(a.k_w, half + c0), wk2);
+        }
+
         float cs[kVec], sn[kVec];
         {
             const float* cr = a.cos_t + pc * half + c0;
@@ -138,19 +152,24 @@ __global__ __launch_bounds__(256) void rope_kvstore_kernel(const RopeArgs a) {
 #pragma unroll
         for (int h = 0; h < HPU; ++h) {
             if (kind[h] < 0) continue;
-            S* dst;
-            if (kind[h] == 0) {
-                dst = static_cast<S*>(a.q_out) + ((int64_t)t * a.hq + hh[h]) * a.dh;
-            } else {
-                if (!store_kv) continue;
-                dst = static_cast<S*>(a.cache) +
-                      (((int64_t)(kind[h] - 1) * a.n_slots + slot) * a.hkv + gg[h]) * (int64_t)a.dh;
-            }
             // Q and K rotate; V (and Q at an out-of-range position) is copied
             // as is, selected so that its bits pass through untouched.
             float f1[kVec], f2[kVec], r1[kVec], r2[kVec];
             unpack<T>(x1[h], f1);
             unpack<T>(x2[h], f2);
+            if constexpr (QKN) {
+                float ss = 0.0f;
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) ss += f1[e] * f1[e] + f2[e] * f2[e];
+                ss = group_sum<LPU>(lane_on ? ss : 0.0f);
+                const float r = __builtin_amdgcn_rsqf(ss / (float)a.dh + a.eps);
+                const bool isk = kind[h] == 1;
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) {
+                    f1[e] = f1[e] * r * (isk ? wk1[e] : wq1[e]);
+                    f2[e] = f2[e] * r * (isk ? wk2[e] : wq2[e]);
+                }
+            }
 #pragma unroll
             for (int e = 0; e < kVec; ++e) {
                 r1[e] = f1[e] * cs[e] - f2[e] * sn[e];
@@ -159,6 +178,11 @@ __global__ __launch_bounds__(256) void rope_kvstore_kernel(const RopeArgs a) {
             const u32x4 p1 = pack<T>(r1), p2 = pack<T>(r2);
             const bool rot = kind[h] < 2 && p_ok;
             const u32x4 o1 = rot ? p1 : x1[h], o2 = rot ? p2 : x2[h];
+            if (!lane_on || (kind[h] != 0 && !store_kv)) continue;
+            S* dst = kind[h] == 0
+                         ? static_cast<S*>(a.q_out) + ((int64_t)t * a.hq + hh[h]) * a.dh
+                         : static_cast<S*>(a.cache) +
+                               (((int64_t)(kind[h] - 1) * a.n_slots + slot) * a.hkv + gg[h]) * (int64_t)a.dh;
             if (C::NTS) {
                 st16_nt<T>(dst, c0, o1);
                 st16_nt<T>(dst, half + c0, o2);
@@ -170,27 +194,27 @@ __global__ __launch_bounds__(256) void rope_kvstore_kernel(const RopeArgs a) {
     }
 }
 
-template <typename T, typename C>
+template <typename T, typename C, bool QKN>
 static int launch_rope(RopeArgs a, int64_t T_tokens, void* stream, int wgs_per_cu) {
     constexpr int UPW = 256 / C::LPU;
     const int upt = (a.nvh + C::HPU - 1) / C::HPU;
     a.upt = make_fastdiv((uint32_t)upt);
     a.units = (uint32_t)(T_tokens * upt);
     const dim3 grid(grid_for(a.units, UPW, device_cus(), wgs_per_cu));
-    return launch(rope_kvstore_kernel<T, C>, grid, dim3(256), stream, a);
+    return launch(rope_kvstore_kernel<T, C, QKN>, grid, dim3(256), stream, a);
 }
 
-template <typename T, int HPU>
+template <typename T, int HPU, bool QKN>
 static int dispatch_rope_lpu(const RopeArgs& a, int64_t T_tokens, void* stream) {
     constexpr int kOnePass = 1 << 20;
     const int chunks = (a.dh / 2) / T::kVec;
-    if (chunks <= 1) return launch_rope<T, RopeCfg<1, HPU, true, true>>(a, T_tokens, stream, kOnePass);
-    if (chunks <= 2) return launch_rope<T, RopeCfg<2, HPU, true, true>>(a, T_tokens, stream, kOnePass);
-    if (chunks <= 4) return launch_rope<T, RopeCfg<4, HPU, true, true>>(a, T_tokens, stream, kOnePass);
-    if (chunks <= 8) return launch_rope<T, RopeCfg<8, HPU, true, true>>(a, T_tokens, stream, kOnePass);
-    if (chunks <= 16) return launch_rope<T, RopeCfg<16, HPU, true, true>>(a, T_tokens, stream, kOnePass);
-    if (chunks <= 32) return launch_rope<T, RopeCfg<32, HPU, true, true>>(a, T_tokens, stream, kOnePass);
-    if (chunks <= 64) return launch_rope<T, RopeCfg<64, HPU, true, true>>(a, T_tokens, stream, kOnePass);
+    if (chunks <= 1) return launch_rope<T, RopeCfg<1, HPU, true, true>, QKN>(a, T_tokens, stream, kOnePass);
+    if (chunks <= 2) return launch_rope<T, RopeCfg<2, HPU, true, true>, QKN>(a, T_tokens, stream, kOnePass);
+    if (chunks <= 4) return launch_rope<T, RopeCfg<4, HPU, true, true>, QKN>(a, T_tokens, stream, kOnePass);
+    if (chunks <= 8) return launch_rope<T, RopeCfg<8, HPU, true, true>, QKN>(a, T_tokens, stream, kOnePass);
+    if (chunks <= 16) return launch_rope<T, RopeCfg<16, HPU, true, true>, QKN>(a, T_tokens, stream, kOnePass);
+    if (chunks <= 32) return launch_rope<T, RopeCfg<32, HPU, true, true>, QKN>(a, T_tokens, stream, kOnePass);
+    if (chunks <= 64) return launch_rope<T, RopeCfg<64, HPU, true, true>, QKN>(a, T_tokens, stream, kOnePass);
     return KCR_ERR_SHAPE;
 }
 
@@ -199,10 +223,10 @@ static int dispatch_rope_lpu(const RopeArgs& a, int64_t T_tokens, void* stream) 
 // cos/sin load once and measured fastest there.
 constexpr int64_t kRopeSmallBatch = 4096;
 
-template <typename T>
+template <typename T, bool QKN>
 static int dispatch_rope(const RopeArgs& a, int64_t T_tokens, void* stream) {
-    return T_tokens <= kRopeSmallBatch ? dispatch_rope_lpu<T, 1>(a, T_tokens, stream)
-                                       : dispatch_rope_lpu<T, 2>(a, T_tokens, stream);
+    return T_tokens <= kRopeSmallBatch ? dispatch_rope_lpu<T, 1, QKN>(a, T_tokens, stream)
+                                       : dispatch_rope_lpu<T, 2, QKN>(a, T_tokens, stream);
 }
 
 // ---------------------------------------------------------- cos/sin tables
@@ -230,14 +254,16 @@ __global__ __launch_bounds__(256) void rope_table_kernel(const TableArgs a) {
 
 using namespace kcr;
 
-extern "C" int kcr_rope_kvstore(const void* q, int64_t q_tok_stride, int64_t q_head_stride,
-                                const void* k, int64_t k_tok_stride, int64_t k_head_stride,
-                                const void* v, int64_t v_tok_stride, int64_t v_head_stride,
-                                void* q_out, const int64_t* positions, const float* cos_tab,
-                                const float* sin_tab, int64_t max_pos, void* kv_cache,
-                                const int64_t* slot_mapping, int64_t T, int n_head, int n_kv_head,
-                                int head_dim, int block_size, int64_t num_blocks, int dtype,
-                                void* stream) {
+// Validates the arguments shared by the two RoPE + store entry points and
+// fills the kernel arguments; KCR_OK with *work == false means nothing to do.
+static int rope_prepare(const void* q, int64_t q_tok_stride, int64_t q_head_stride, const void* k,
+                        int64_t k_tok_stride, int64_t k_head_stride, const void* v,
+                        int64_t v_tok_stride, int64_t v_head_stride, void* q_out,
+                        const int64_t* positions, const float* cos_tab, const float* sin_tab,
+                        int64_t max_pos, void* kv_cache, const int64_t* slot_mapping, int64_t T,
+                        int n_head, int n_kv_head, int head_dim, int block_size, int64_t num_blocks,
+                        int dtype, RopeArgs* out, bool* work) {
+    *work = false;
     if (!dtype_ok(dtype)) return KCR_ERR_DTYPE;
     if (n_kv_head < 1 || n_head < 1) return KCR_ERR_SHAPE;
     if (n_head % n_kv_head != 0) return KCR_ERR_HEADS;
@@ -280,11 +306,62 @@ extern "C" int kcr_rope_kvstore(const void* q, int64_t q_tok_stride, int64_t q_h
     if (device_cus() <= 0) return KCR_ERR_DEVICE;
 
     const int group = n_head / n_kv_head;
-    RopeArgs a{q, k, v, q_out, kv_cache, positions, slot_mapping, cos_tab, sin_tab,
-               q_tok_stride, q_head_stride, k_tok_stride, k_head_stride, v_tok_stride, v_head_stride,
-               max_pos, n_slots, 0u, make_fastdiv(1u), make_fastdiv((uint32_t)(group + 2)),
-               n_kv_head * (group + 2), n_head, n_kv_head, group, head_dim};
-    return dtype == KCR_BF16 ? dispatch_rope<Bf16>(a, T, stream) : dispatch_rope<F32>(a, T, stream);
+    *out = RopeArgs{q, k, v, q_out, kv_cache, positions, slot_mapping, cos_tab, sin_tab,
+                    nullptr, nullptr, 0.0f,
+                    q_tok_stride, q_head_stride, k_tok_stride, k_head_stride, v_tok_stride, v_head_stride,
+                    max_pos, n_slots, 0u, make_fastdiv(1u), make_fastdiv((uint32_t)(group + 2)),
+                    n_kv_head * (group + 2), n_head, n_kv_head, group, head_dim};
+    *work = true;
+    return KCR_OK;
+}
+
+extern "C" int kcr_rope_kvstore(const void* q, int64_t q_tok_stride, int64_t q_head_stride,
+                                const void* k, int64_t k_tok_stride, int64_t k_head_stride,
+                                const void* v, int64_t v_tok_stride, int64_t v_head_stride,
+                                void* q_out, const int64_t* positions, const float* cos_tab,
+                                const float* sin_tab, int64_t max_pos, void* kv_cache,
+                                const int64_t* slot_mapping, int64_t T, int n_head, int n_kv_head,
+                                int head_dim, int block_size, int64_t num_blocks, int dtype,
+                                void* stream) {
+    RopeArgs a;
+    bool work;
+    const int rc = rope_prepare(q, q_tok_stride, q_head_stride, k, k_tok_stride, k_head_stride, v,
+                                v_tok_stride, v_head_stride, q_out, positions, cos_tab, sin_tab,
+                                max_pos, kv_cache, slot_mapping, T, n_head, n_kv_head, head_dim,
+                                block_size, num_blocks, dtype, &a, &work);
+    if (rc != KCR_OK || !work) return rc;
+    return dtype == KCR_BF16 ? dispatch_rope<Bf16, false>(a, T, stream)
+                             : dispatch_rope<F32, false>(a, T, stream);
+}
+
+extern "C" int kcr_qknorm_rope_kvstore(const void* q, int64_t q_tok_stride, int64_t q_head_stride,
+                                       const void* k, int64_t k_tok_stride, int64_t k_head_stride,
+                                       const void* v, int64_t v_tok_stride, int64_t v_head_stride,
+                                       const void* q_norm_w, const void* k_norm_w, float eps,
+                                       void* q_out, const int64_t* positions, const float* cos_tab,
+                                       const float* sin_tab, int64_t max_pos, void* kv_cache,
+                                       const int64_t* slot_mapping, int64_t T, int n_head,
+                                       int n_kv_head, int head_dim, int block_size,
+                                       int64_t num_blocks, int dtype, void* stream) {
+    RopeArgs a;
+    bool work;
+    const int rc = rope_prepare(q, q_tok_stride, q_head_stride, k, k_tok_stride, k_head_stride, v,
+                                v_tok_stride, v_head_stride, q_out, positions, cos_tab, sin_tab,
+                                max_pos, kv_cache, slot_mapping, T, n_head, n_kv_head, head_dim,
+                                block_size, num_blocks, dtype, &a, &work);
+    if (rc != KCR_OK || !work) return rc;
+    if (!q_norm_w || !k_norm_w) return KCR_ERR_NULL;
+    if (!aligned16(q_norm_w) || !aligned16(k_norm_w)) return KCR_ERR_ALIGN;
+    const size_t es = dtype_size(dtype);
+    const Span so = span2d(q_out, 1, 0, T * n_head * (int64_t)head_dim, es);
+    const Span sc = span2d(kv_cache, 1, 0, 2 * a.n_slots * n_kv_head * (int64_t)head_dim, es);
+    const Span wq = span2d(q_norm_w, 1, 0, head_dim, es), wk = span2d(k_norm_w, 1, 0, head_dim, es);
+    if (overlap(so, wq) || overlap(so, wk) || overlap(sc, wq) || overlap(sc, wk)) return KCR_ERR_ALIAS;
+    a.q_w = q_norm_w;
+    a.k_w = k_norm_w;
+    a.eps = eps;
+    return dtype == KCR_BF16 ? dispatch_rope<Bf16, true>(a, T, stream)
+                             : dispatch_rope<F32, true>(a, T, stream);
 }
 
 extern "C" int kcr_rope_cos_sin(float* cos_tab, float* sin_tab, int64_t max_pos, int head_dim,

@@ -34,6 +34,8 @@ def lib():
     L.kcr_rope_kvstore.argtypes = [P, I64, I64, P, I64, I64, P, I64, I64, P, P, P, P, I64, P, P,
                                    I64, I, I, I, I, I64, I, P]
     L.kcr_rope_cos_sin.argtypes = [P, P, I64, I, D, P]
+    L.kcr_qknorm_rope_kvstore.argtypes = [P, I64, I64, P, I64, I64, P, I64, I64, P, P, F, P, P, P, P,
+                                          I64, P, P, I64, I, I, I, I, I64, I, P]
     L.kcr_swiglu.argtypes = [P, I64, P, I64, P, I64, I64, I64, I, P]
     L.kcr_copy.argtypes = [P, P, I64, P]
     L.kcr_paged_kv_gather.argtypes = [P, I64, I, I, I, P, I64, P, I64, I64, P, P, I, P]
@@ -121,6 +123,28 @@ def test_rope_validation(lib):
     # contiguous q may be rotated in place
     assert _rope(lib, qts=12 * 128, k=A * 3, kts=2 * 128, v=A * 4, vts=2 * 128,
                  qo=A) in (DEVICE, OK)
+
+
+def test_qknorm_rope_validation(lib):
+    def q(wq=A * 20, wk=A * 21, **kw):
+        a = dict(q=A, qts=16 * 128, qhs=128, k=A + 12 * 128 * 2, kts=16 * 128, khs=128,
+                 v=A + 14 * 128 * 2, vts=16 * 128, vhs=128, qo=A * 8, pos=A * 9, cos=A * 10,
+                 sin=A * 11, max_pos=4096, cache=A * 16, slots=A * 12, T=4, hq=12, hkv=2, hd=128,
+                 bs=16, nb=64, dt=BF16)
+        a.update(kw)
+        return lib.kcr_qknorm_rope_kvstore(a["q"], a["qts"], a["qhs"], a["k"], a["kts"], a["khs"],
+                                           a["v"], a["vts"], a["vhs"], wq, wk, 1e-6, a["qo"], a["pos"],
+                                           a["cos"], a["sin"], a["max_pos"], a["cache"], a["slots"],
+                                           a["T"], a["hq"], a["hkv"], a["hd"], a["bs"], a["nb"],
+                                           a["dt"], None)
+    assert q() in (DEVICE, OK)
+    assert q(dt=9) == DTYPE
+    assert q(hkv=5) == HEADS
+    # with no device the shared checks stop at DEVICE before the weight checks;
+    # on a GPU machine the weight errors below are reported
+    assert q(wq=None) in (DEVICE, NULL)
+    assert q(wk=A * 21 + 4) in (DEVICE, ALIGN)
+    assert q(T=0, wq=None, wk=None) == OK
 
 
 def test_swiglu_validation(lib):

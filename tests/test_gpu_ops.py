@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import workloads
-from helpers import (assert_bits_equal, assert_close, check_rope, gpu_qkv, np_bits,
+from helpers import (assert_bits_equal, assert_close, assert_rope_close, check_rope, gpu_qkv, np_bits,
                      tol_violations)
 
 pytestmark = pytest.mark.gpu
@@ -176,6 +176,41 @@ def test_rope_shapes(kcr, hq, hkv, dh, dt):
                        wl["max_pos"])
     check_rope(wl["q"], wl["k"], wl["v"], wl["positions"], wl["cache"], slots, wl["theta"], qg, cg,
                dt, f"hq={hq} hkv={hkv} dh={dh}")
+
+
+@pytest.mark.parametrize("hq,hkv,dh", [(12, 2, 128), (16, 8, 128), (8, 1, 96), (4, 4, 256),
+                                       (2, 2, 512), (6, 3, 16)])
+@pytest.mark.parametrize("dt", DTS, ids=DT_ID.get)
+def test_qknorm_rope_kvstore(kcr, hq, hkv, dh, dt):
+    say(f"qknorm rope hq={hq} hkv={hkv} dh={dh} dt={dt}")
+    wl = workloads.prefill(n_seqs=3, len_lo=1, len_hi=60, dtype=dt, seed=hq + dh, hq=hq, hkv=hkv,
+                           dh=dh, block_size=16)
+    g = workloads.gen(dh)
+    wq = (1 + 0.1 * workloads.randn([dh], g)).to(dt)
+    wk = (0.5 + torch.rand([dh], generator=g)).to(dt)
+    slots = wl["slot_mapping"].clone()
+    slots[::4] = -1
+    cos, sin = kcr.rope_cos_sin(wl["max_pos"], dh, wl["theta"])
+    cache = dev(wl["cache"])
+    qo = kcr.qknorm_rope_kvstore(*gpu_qkv(wl), dev(wq), dev(wk), 1e-6, dev(wl["positions"]), cos,
+                                 sin, cache, dev(slots))
+    cache_ref = np_bits(wl["cache"]).copy()
+    q_rot, k_rot = oracle.qknorm_rope_kvstore(np_bits(wl["q"]), np_bits(wl["k"]), np_bits(wl["v"]),
+                                              np_bits(wq), np_bits(wk), float(np.float32(1e-6)),
+                                              wl["positions"].numpy(), wl["theta"], cache_ref,
+                                              slots.numpy())
+    assert_rope_close(qo.cpu().double().numpy(), q_rot, dt, "q_out")
+    got = np_bits(cache.cpu())
+    nb, bs = wl["cache"].shape[1:3]
+    g_flat, r_flat = got.reshape(2, nb * bs, hkv, dh), cache_ref.reshape(2, nb * bs, hkv, dh)
+    live = slots.numpy()[slots.numpy() >= 0]
+    assert np.array_equal(g_flat[1].view(np.uint8), r_flat[1].view(np.uint8)), "V half"
+    mask = np.ones(nb * bs, dtype=bool)
+    mask[live] = False
+    assert np.array_equal(g_flat[0][mask].view(np.uint8), r_flat[0][mask].view(np.uint8))
+    kg = torch.from_numpy(g_flat[0][live].view(np.int16 if dt == torch.bfloat16 else np.int32).copy())
+    order = np.nonzero(slots.numpy() >= 0)[0]
+    assert_rope_close(kg.view(dt).double().numpy(), k_rot[order], dt, "K rows")
 
 
 def test_rope_prefill_block_size_and_in_place(kcr):
