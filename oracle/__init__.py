@@ -56,6 +56,8 @@ def _bind(lib):
         "orc_gqa_kv_head": (I, [I, I, I]),
         "orc_paged_gather": (None, [P, I, P, I64, I, I, I, I64, P, I]),
         "orc_swiglu": (None, [P, I64, P, I64, P, I64, I64, I64, I]),
+        "orc_reglu": (None, [P, I64, P, I64, P, I64, I64, I64, I]),
+        "orc_clip_norm": (None, [P, I64, I64, P, I, P, I, D, D, P, I64, I, I, I]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -225,6 +227,30 @@ def swiglu(gate: np.ndarray, up: np.ndarray, L=None) -> np.ndarray:
     out = np.empty((rows, cols), dtype=np.float64)
     L.orc_swiglu(_ptr(gate), gs, _ptr(up), us, _ptr(out), cols, rows, cols, _code(gate))
     return out
+
+
+def reglu(gate: np.ndarray, up: np.ndarray, L=None) -> np.ndarray:
+    L = L or lib()
+    gate, gs = _rows(gate)
+    up, us = _rows(up)
+    rows, cols = gate.shape
+    out = np.empty((rows, cols), dtype=np.float64)
+    L.orc_reglu(_ptr(gate), gs, _ptr(up), us, _ptr(out), cols, rows, cols, _code(gate))
+    return out
+
+
+def clip_norm(x: np.ndarray, alpha: np.ndarray, gamma: np.ndarray, lo: float = -1.0,
+              hi: float = 1.0, L=None) -> np.ndarray:
+    """x [n_tok, n_head, d] (strided views allowed, last dim contiguous);
+    alpha and gamma are [d] (per channel) or [1] (scalar). Returns float64."""
+    L = L or lib()
+    n_tok, n_head, d = x.shape
+    xs = _elem_strides(x)
+    alpha, gamma = np.ascontiguousarray(alpha), np.ascontiguousarray(gamma)
+    y = np.empty((n_tok, n_head, d), dtype=np.float64)
+    L.orc_clip_norm(_ptr(x), xs[0], xs[1], _ptr(alpha), int(alpha.size > 1), _ptr(gamma),
+                    int(gamma.size > 1), float(lo), float(hi), _ptr(y), n_tok, n_head, d, _code(x))
+    return y
 
 
 def num_threads(L=None) -> int:

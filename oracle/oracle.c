@@ -27,6 +27,9 @@
  *     frequencies are the RoFormer ones, base^(-2i/d).
  *   - SwiGLU: koas-w post, section 2 ("Fused SwiGLU"): silu(gate) * up with
  *     silu(g) = g * sigmoid(g).
+ *   - Variants from mer.dev "AsyncT vLLM notes (1)": per-head Q/K RMSNorm
+ *     before RoPE (sections 0, 3.3), the paged gather (section 1.4), ReGLU
+ *     and the DyHT clip norm (sections 0, 3.3).
  *
  * Inputs arrive in their storage dtype (bf16 bit patterns or fp32) and are
  * widened exactly to double. Results are returned in double, except values
@@ -331,4 +334,43 @@ void orc_swiglu(const void* gate, int64_t gate_stride, const void* up, int64_t u
             double sigmoid = 1.0 / (1.0 + exp(-g));
             out[r * out_stride + c] = g * sigmoid * u;
         }
+}
+
+/* ----------------------------------------------------------------- ReGLU */
+
+/* out = relu(g) * u, relu(g) = g if g > 0 else 0 (the ReGLU of the mer.dev
+ * AsyncT notes, section 0, fused as relu_and_mul in section 3.3). */
+void orc_reglu(const void* gate, int64_t gate_stride, const void* up, int64_t up_stride,
+               double* out, int64_t out_stride, int64_t rows, int64_t cols, int dtype) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
+            double g = load(gate, r * gate_stride + c, dtype);
+            double u = load(up, r * up_stride + c, dtype);
+            double relu = g > 0.0 ? g : 0.0;
+            out[r * out_stride + c] = relu * u;
+        }
+}
+
+/* ------------------------------------------------------------ DyHT / clip */
+
+/* y[t, h, e] = clamp(alpha_e * x[t, h, e], lo, hi) * gamma_e over an
+ * [n_tok, n_head, d] view with token and head strides (the DyHT norm of the
+ * mer.dev AsyncT notes, section 0, y * clamp(a x, -1, 1), and its clip-norm
+ * kernel in section 3.3 with per-channel or scalar a and gamma: a scalar
+ * parameter is read at index 0 for every channel). */
+void orc_clip_norm(const void* x, int64_t x_ts, int64_t x_hs, const void* alpha, int alpha_per_ch,
+                   const void* gamma, int gamma_per_ch, double lo, double hi, double* y,
+                   int64_t n_tok, int n_head, int d, int dtype) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n_tok; ++t)
+        for (int h = 0; h < n_head; ++h)
+            for (int e = 0; e < d; ++e) {
+                double a = load(alpha, alpha_per_ch ? e : 0, dtype);
+                double g = load(gamma, gamma_per_ch ? e : 0, dtype);
+                double v = a * load(x, t * x_ts + h * x_hs + e, dtype);
+                if (v < lo) v = lo;
+                if (v > hi) v = hi;
+                y[(t * n_head + h) * d + e] = v * g;
+            }
 }

@@ -464,4 +464,46 @@ def pin_swiglu_fused_halves(L):
     assert np.array_equal(a, b)
 
 
+# ------------------------------------------------- ReGLU and clip-norm pins
+def pin_reglu_golden(L):
+    c = golden("reglu_clip_norm_hand.json")["reglu"][0]
+    for dt in (F32, BF16):
+        out = oracle.reglu(enc([c["g"]], dt), enc([c["u"]], dt), L=L)[0]
+        assert np.array_equal(out, c["out"]), out
+
+
+def pin_reglu_vs_torch(L):
+    for dt in (F32, BF16):
+        g, u = rand_rows(6, 1001, dt, 61, scale=2.0), rand_rows(6, 1001, dt, 62)
+        ref = F.relu(torch.from_numpy(dec(g))) * torch.from_numpy(dec(u))
+        assert np.allclose(oracle.reglu(g, u, L=L), ref.numpy(), rtol=0, atol=0)
+
+
+def pin_clip_norm_golden(L):
+    for c in golden("reglu_clip_norm_hand.json")["clip_norm"]:
+        for dt in (F32, BF16):
+            d = len(c["x"])
+            y = oracle.clip_norm(enc(np.array(c["x"]).reshape(1, 1, d), dt), enc(c["alpha"], dt),
+                                 enc(c["gamma"], dt), c["lo"], c["hi"], L=L)
+            assert np.array_equal(y[0, 0], c["out"]), (c, y)
+
+
+def pin_clip_norm_vs_numpy_and_bounds(L):
+    # numpy's clip on the exact products; |y| <= max(|lo|, |hi|) * |gamma|;
+    # strided [N, H, D] views give the same result as contiguous copies.
+    g = workloads.gen(63)
+    qkv = (workloads.randn([5, 16 * 64], g) * 3).to(torch.bfloat16)
+    q = qkv[:, : 12 * 64].unflatten(1, (12, 64))
+    rng = np.random.default_rng(64)
+    a = enc(rng.standard_normal(64), BF16)
+    gm = enc(1 + 0.2 * rng.standard_normal(64), BF16)
+    y = oracle.clip_norm(np_bits(q), a, gm, -1.0, 1.0, L=L)
+    x = dec(np.ascontiguousarray(np_bits(q)))
+    ref = np.clip(dec(a) * x, -1.0, 1.0) * dec(gm)
+    assert np.array_equal(y, ref)
+    assert np.all(np.abs(y) <= np.abs(dec(gm)))
+    y2 = oracle.clip_norm(np.ascontiguousarray(np_bits(q)), a, gm, -1.0, 1.0, L=L)
+    assert np.array_equal(y, y2)
+
+
 PINS = {name: fn for name, fn in sorted(globals().items()) if name.startswith("pin_")}

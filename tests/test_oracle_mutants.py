@@ -40,6 +40,12 @@ MUTANTS = {
                                "n[e] = load(x, x_off + e, dtype) * r * load(w, d - 1 - e, dtype);"),
     "qknorm_rotate_before_norm_skipped": ("            rotate_half(n, k_rot + (t * hkv + h) * d, p, d, base);",
                                           "            for (int e = 0; e < d; ++e) k_rot[(t * hkv + h) * d + e] = n[e];"),
+    "reglu_leaky": ("double relu = g > 0.0 ? g : 0.0;", "double relu = g > 0.0 ? g : 0.01 * g;"),
+    "clip_gamma_from_alpha": ("double g = load(gamma, gamma_per_ch ? e : 0, dtype);",
+                              "double g = load(alpha, alpha_per_ch ? e : 0, dtype);"),
+    "clip_upper_bound_missing": ("                if (v > hi) v = hi;\n", ""),
+    "clip_gamma_before_clamp": ("                double v = a * load(x, t * x_ts + h * x_hs + e, dtype);",
+                                "                double v = a * g * load(x, t * x_ts + h * x_hs + e, dtype);"),
     "gqa_modulo": ("return h / (hq / hkv);", "return h % hkv;"),
     "gather_offset_from_block": ("int64_t block = block_table[t / block_size], offset = t % block_size;",
                                  "int64_t block = block_table[t / block_size], offset = (t + 1) % block_size;"),
