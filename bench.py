@@ -138,6 +138,16 @@ def large_shapes(kcr, iters: int):
         fns = [lambda i=i: kcr.rmsnorm(xs[i], w, wl["eps"], out=ys[i]) for i in range(3)]
         run(f"rmsnorm_{tag}", norm_bytes(R, 2176, xs[0].element_size(), False), fns, f"[{R}, 2176] {tag}")
         del xs, ys, wl
+    # DyHT clip norm on the same rows as RMSNorm bf16, per-channel alpha and gamma
+    wl = workloads.rmsnorm_rows(rows=R, d=2176, dtype="bf16", seed=0)
+    xs = [wl["x"].to(dev)]
+    xs += [xs[0].clone() for _ in range(2)]
+    ys = [torch.empty_like(xs[0]) for _ in range(3)]
+    alpha = torch.full((2176,), 0.5, dtype=torch.bfloat16, device=dev)
+    gamma = wl["w"].to(dev)
+    fns = [lambda i=i: kcr.clip_norm(xs[i], alpha, gamma, out=ys[i]) for i in range(3)]
+    run("clip_norm_bf16", 2 * R * 2176 * 2 + 2 * 2176 * 2, fns, f"[{R}, 2176] bf16, per-channel alpha, gamma")
+    del xs, ys, wl
     wl = workloads.add_rmsnorm_rows(R, 1536, dtype="bf16", seed=0)
     xs = [wl["x"].to(dev) for _ in range(3)]
     ds = [wl["delta"].to(dev) for _ in range(3)]
@@ -186,6 +196,8 @@ def large_shapes(kcr, iters: int):
     outs = [torch.empty((8192, 8960), dtype=torch.bfloat16, device=dev) for _ in range(3)]
     fns = [lambda i=i: kcr.swiglu(gus[i][:, :8960], gus[i][:, 8960:], out=outs[i]) for i in range(3)]
     run("swiglu_bf16", swiglu_bytes(8192, 8960, 2), fns, "gate_up [8192, 17920] -> [8192, 8960] bf16")
+    fns = [lambda i=i: kcr.reglu(gus[i][:, :8960], gus[i][:, 8960:], out=outs[i]) for i in range(3)]
+    run("reglu_bf16", swiglu_bytes(8192, 8960, 2), fns, "gate_up [8192, 17920] -> [8192, 8960] bf16")
     del gus, outs, wl
     torch.cuda.empty_cache()
     return out

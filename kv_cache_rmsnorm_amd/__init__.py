@@ -43,6 +43,8 @@ _SIGS = {
                                 _P, _P, _I64, _P, _P, _I64, _I, _I, _I, _I, _I64, _I, _P],
     "kcr_rope_cos_sin": [_P, _P, _I64, _I, _D, _P],
     "kcr_swiglu": [_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I, _P],
+    "kcr_reglu": [_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I, _P],
+    "kcr_clip_norm": [_P, _I64, _I64, _P, _I64, _I64, _I64, _I, _I, _P, _I, _P, _I, _F, _F, _I, _P],
     "kcr_paged_kv_gather": [_P, _I64, _I, _I, _I, _P, _I64, _P, _I64, _I64, _P, _P, _I, _P],
     "kcr_copy": [_P, _P, _I64, _P],
     "kcr_time_next_launch": [_P, _P],
@@ -202,6 +204,41 @@ def swiglu(gate: torch.Tensor, up: torch.Tensor, out: torch.Tensor | None = None
     _check("swiglu", _lib.kcr_swiglu(gate.data_ptr(), gs, up.data_ptr(), us, out.data_ptr(), os_,
                                      rows, cols, dt, _stream(gate)))
     return out
+
+
+def reglu(gate: torch.Tensor, up: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """relu(gate) * up (same layouts as swiglu)."""
+    dt = _dt(gate, up)
+    rows, cols, gs = _rows(gate)
+    _, _, us = _rows(up)
+    if out is None:
+        out = torch.empty(gate.shape, dtype=gate.dtype, device=gate.device)
+    _, _, os_ = _rows(out)
+    _check("reglu", _lib.kcr_reglu(gate.data_ptr(), gs, up.data_ptr(), us, out.data_ptr(), os_,
+                                   rows, cols, dt, _stream(gate)))
+    return out
+
+
+def clip_norm(x: torch.Tensor, alpha: torch.Tensor, gamma: torch.Tensor, lo: float = -1.0,
+              hi: float = 1.0, out: torch.Tensor | None = None) -> torch.Tensor:
+    """clamp(alpha * x, lo, hi) * gamma over x [n_tok, n_head, d] (or [n, d]),
+    strided views allowed; alpha/gamma are [d] (per channel) or [1]."""
+    dt = _dt(x, alpha, gamma)
+    if x.dim() == 2:
+        x = x.unsqueeze(1)
+        out = out.unsqueeze(1) if out is not None else None
+        squeeze = True
+    else:
+        squeeze = False
+    n, h, d = x.shape
+    if x.stride(2) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    y = torch.empty((n, h, d), dtype=x.dtype, device=x.device) if out is None else out
+    _check("clip_norm", _lib.kcr_clip_norm(
+        x.data_ptr(), x.stride(0), x.stride(1), y.data_ptr(), y.stride(0), y.stride(1), n, h, d,
+        alpha.data_ptr(), int(alpha.numel() > 1), gamma.data_ptr(), int(gamma.numel() > 1),
+        float(lo), float(hi), dt, _stream(x)))
+    return y.squeeze(1) if squeeze else y
 
 
 def swiglu_fused(gate_up: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:

@@ -34,10 +34,16 @@ struct SwigluArgs {
     FastDiv vpr;     // vectors per row
 };
 
-__device__ __forceinline__ float silu_mul(float g, float u) {
-    const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);  // exp(-g)
-    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
-}
+// Gate activations times up.
+struct SiluMul {  // SwiGLU: silu(g) * u, silu(g) = g / (1 + exp(-g))
+    static __device__ __forceinline__ float apply(float g, float u) {
+        const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);  // exp(-g)
+        return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+    }
+};
+struct ReluMul {  // ReGLU: relu(g) * u
+    static __device__ __forceinline__ float apply(float g, float u) { return (g > 0.0f ? g : 0.0f) * u; }
+};
 
 // Launch shape: BLOCK threads, UNROLL vectors of each stream per lane before
 // any math, nontemporal loads (NTL) and stores (NTS).
@@ -47,7 +53,7 @@ struct SwigluCfg {
     static constexpr bool NTL = NTL_, NTS = NTS_;
 };
 
-template <typename T, typename C>
+template <typename T, typename C, typename Act>
 __global__ __launch_bounds__(C::BLOCK) void swiglu_kernel(const SwigluArgs a) {
     using S = typename T::storage;
     constexpr int kVec = T::kVec, B = C::BLOCK, U = C::UNROLL;
@@ -75,7 +81,7 @@ __global__ __launch_bounds__(C::BLOCK) void swiglu_kernel(const SwigluArgs a) {
                 unpack<T>(gr[k], gf);
                 unpack<T>(ur[k], uf);
 #pragma unroll
-                for (int e = 0; e < kVec; ++e) of[e] = silu_mul(gf[e], uf[e]);
+                for (int e = 0; e < kVec; ++e) of[e] = Act::apply(gf[e], uf[e]);
                 S* op = static_cast<S*>(a.out) + row[k] * a.out_stride;
                 store_raw<T, C::NTS>(op, col[k], a.cols, pack<T>(of), aligned16(op));
             }
@@ -83,19 +89,17 @@ __global__ __launch_bounds__(C::BLOCK) void swiglu_kernel(const SwigluArgs a) {
     }
 }
 
-template <typename T, typename C>
+template <typename T, typename C, typename Act>
 static int launch_swiglu(const SwigluArgs& a, void* stream, int wgs_per_cu) {
     const dim3 grid(grid_for(a.total, C::BLOCK * C::UNROLL, device_cus(), wgs_per_cu));
-    return launch(swiglu_kernel<T, C>, grid, dim3(C::BLOCK), stream, a);
+    return launch(swiglu_kernel<T, C, Act>, grid, dim3(C::BLOCK), stream, a);
 }
 
-}  // namespace kcr
-
-using namespace kcr;
-
-extern "C" int kcr_swiglu(const void* gate, int64_t gate_stride, const void* up, int64_t up_stride,
-                          void* out, int64_t out_stride, int64_t rows, int64_t cols, int dtype,
-                          void* stream) {
+// Shared argument checks of the gated activations.
+static int gated_prepare(const void* gate, int64_t gate_stride, const void* up, int64_t up_stride,
+                         void* out, int64_t out_stride, int64_t rows, int64_t cols, int dtype,
+                         SwigluArgs* a, bool* work) {
+    *work = false;
     if (!dtype_ok(dtype)) return KCR_ERR_DTYPE;
     if (rows < 0 || cols < 1) return KCR_ERR_SHAPE;
     const size_t es = dtype_size(dtype);
@@ -115,12 +119,44 @@ extern "C" int kcr_swiglu(const void* gate, int64_t gate_stride, const void* up,
         (!on_up && !rows_disjoint(out, out_stride, up, up_stride, rows, cols, es)))
         return KCR_ERR_ALIAS;
     if (device_cus() <= 0) return KCR_ERR_DEVICE;
-    SwigluArgs a{gate, up, out, gate_stride, up_stride, out_stride, cols,
-                 (uint32_t)(rows * vpr), make_fastdiv((uint32_t)vpr)};
-    // 64-lane workgroups, one vector of each stream per lane, one-pass grid,
-    // nontemporal loads and stores: the fastest shape in sweeps on MI355X.
-    using Cfg = SwigluCfg<64, 1, true, true>;
-    constexpr int kOnePass = 1 << 20;
-    return dtype == KCR_BF16 ? launch_swiglu<Bf16, Cfg>(a, stream, kOnePass)
-                             : launch_swiglu<F32, Cfg>(a, stream, kOnePass);
+    *a = SwigluArgs{gate, up, out, gate_stride, up_stride, out_stride, cols,
+                    (uint32_t)(rows * vpr), make_fastdiv((uint32_t)vpr)};
+    *work = true;
+    return KCR_OK;
+}
+
+// 64-lane workgroups, one vector of each stream per lane, one-pass grid,
+// nontemporal loads and stores: the fastest shape in sweeps on MI355X.
+using GatedCfg = SwigluCfg<64, 1, true, true>;
+constexpr int kOnePass = 1 << 20;
+
+template <typename Act>
+static int run_gated(const void* gate, int64_t gate_stride, const void* up, int64_t up_stride,
+                     void* out, int64_t out_stride, int64_t rows, int64_t cols, int dtype,
+                     void* stream) {
+    SwigluArgs a;
+    bool work;
+    const int rc = gated_prepare(gate, gate_stride, up, up_stride, out, out_stride, rows, cols, dtype,
+                                 &a, &work);
+    if (rc != KCR_OK || !work) return rc;
+    return dtype == KCR_BF16 ? launch_swiglu<Bf16, GatedCfg, Act>(a, stream, kOnePass)
+                             : launch_swiglu<F32, GatedCfg, Act>(a, stream, kOnePass);
+}
+
+}  // namespace kcr
+
+using namespace kcr;
+
+extern "C" int kcr_swiglu(const void* gate, int64_t gate_stride, const void* up, int64_t up_stride,
+                          void* out, int64_t out_stride, int64_t rows, int64_t cols, int dtype,
+                          void* stream) {
+    return run_gated<SiluMul>(gate, gate_stride, up, up_stride, out, out_stride, rows, cols, dtype,
+                              stream);
+}
+
+extern "C" int kcr_reglu(const void* gate, int64_t gate_stride, const void* up, int64_t up_stride,
+                         void* out, int64_t out_stride, int64_t rows, int64_t cols, int dtype,
+                         void* stream) {
+    return run_gated<ReluMul>(gate, gate_stride, up, up_stride, out, out_stride, rows, cols, dtype,
+                              stream);
 }

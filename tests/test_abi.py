@@ -38,6 +38,8 @@ def lib():
                                           I64, P, P, I64, I, I, I, I, I64, I, P]
     L.kcr_swiglu.argtypes = [P, I64, P, I64, P, I64, I64, I64, I, P]
     L.kcr_copy.argtypes = [P, P, I64, P]
+    L.kcr_reglu.argtypes = [P, I64, P, I64, P, I64, I64, I64, I, P]
+    L.kcr_clip_norm.argtypes = [P, I64, I64, P, I64, I64, I64, I, I, P, I, P, I, F, F, I, P]
     L.kcr_paged_kv_gather.argtypes = [P, I64, I, I, I, P, I64, P, I64, I64, P, P, I, P]
     L.kcr_strerror.argtypes = [I]
     L.kcr_strerror.restype = ctypes.c_char_p
@@ -183,6 +185,35 @@ def test_gather_validation(lib):
     assert g(bt=A * 2 + 4) == ALIGN
     assert g(v=A * 4) == ALIAS
     assert g(k=A + 64) == ALIAS                # output over the cache
+
+
+def test_reglu_validation(lib):
+    f = lib.kcr_reglu
+    I = 8960
+    assert f(A, 2 * I, A + 2 * I, 2 * I, A * 64, I, 4, I, 3, None) == DTYPE
+    assert f(A, 2 * I, A + 2 * I, 2 * I, None, I, 4, I, BF16, None) == NULL
+    assert f(A, 2 * I, A + 2 * I, 2 * I, A + 16, 2 * I, 4, I, BF16, None) == ALIAS
+    assert f(A, 2 * I, A + 2 * I, 2 * I, A * 64, I, 4, I, BF16, None) in (DEVICE, OK)
+
+
+def test_clip_norm_validation(lib):
+    f = lib.kcr_clip_norm
+    base = dict(x=A, xts=2048, xhs=128, y=A * 8, yts=1536, yhs=128, n=4, h=12, d=128, a=A * 9, apc=1,
+                g=A * 10, gpc=0, lo=-1.0, hi=1.0, dt=BF16)
+
+    def c(**kw):
+        a = dict(base, **kw)
+        return f(a["x"], a["xts"], a["xhs"], a["y"], a["yts"], a["yhs"], a["n"], a["h"], a["d"],
+                 a["a"], a["apc"], a["g"], a["gpc"], a["lo"], a["hi"], a["dt"], None)
+    assert c() in (DEVICE, OK)
+    assert c(dt=7) == DTYPE
+    assert c(lo=1.0, hi=-1.0) == SHAPE
+    assert c(xhs=100) == SHAPE                     # head stride below the head width
+    assert c(a=None) == NULL
+    assert c(x=A + 1) == ALIGN
+    assert c(y=A + 256) == ALIAS                   # output inside the strided input view
+    assert c(y=A, yts=2048, yhs=128) in (DEVICE, OK)   # exactly in place
+    assert c(n=0, x=None, y=None) == OK
 
 
 def test_copy_validation(lib):

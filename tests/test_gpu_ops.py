@@ -337,6 +337,46 @@ def test_swiglu_extremes(kcr):
     assert np.all(np.abs(out2) <= 2e-36) and np.all(out2 <= 0)
 
 
+# ------------------------------------------------------------------ ReGLU
+@pytest.mark.parametrize("dt", DTS, ids=DT_ID.get)
+@pytest.mark.parametrize("rows,cols", [(1, 8960), (7, 13), (300, 1000)])
+def test_reglu(kcr, dt, rows, cols):
+    say(f"reglu dt={dt} {rows}x{cols}")
+    wl = workloads.swiglu_fused(rows=rows, inter=cols, dtype=dt, seed=rows * cols)
+    gu = dev(wl["gate_up"])
+    out = kcr.reglu(gu[:, :cols], gu[:, cols:])
+    ref = oracle.reglu(np_bits(wl["gate"]), np_bits(wl["up"]))
+    assert_close(out.cpu().double().numpy(), ref, dt, "reglu")
+
+
+# ------------------------------------------------------------- clip norm
+@pytest.mark.parametrize("dt", DTS, ids=DT_ID.get)
+@pytest.mark.parametrize("apc,gpc", [(True, True), (False, True), (True, False), (False, False)])
+def test_clip_norm_qk_views(kcr, dt, apc, gpc):
+    say(f"clip norm dt={dt} alpha per channel={apc} gamma per channel={gpc}")
+    g = workloads.gen(70)
+    qkv = (workloads.randn([123, 16 * 128], g) * 2).to(dt)
+    q = qkv[:, : 12 * 128].unflatten(1, (12, 128))          # token stride 2048, head stride 128
+    a = (workloads.randn([128 if apc else 1], g)).to(dt)
+    gm = (1 + 0.3 * workloads.randn([128 if gpc else 1], g)).to(dt)
+    qd = dev(qkv)[:, : 12 * 128].unflatten(1, (12, 128))
+    y = kcr.clip_norm(qd, dev(a), dev(gm))
+    ref = oracle.clip_norm(np_bits(q), np_bits(a), np_bits(gm))
+    assert_close(y.cpu().double().numpy(), ref, dt, "clip norm")
+
+
+def test_clip_norm_in_place_and_ragged(kcr):
+    say("clip norm in place, ragged rows")
+    g = workloads.gen(71)
+    x = (workloads.randn([57, 3, 75], g) * 3).to(torch.bfloat16)  # 75 bf16: rows not 16-byte aligned
+    a = torch.tensor([0.7], dtype=torch.bfloat16)
+    gm = (workloads.randn([75], g)).to(torch.bfloat16)
+    ref = oracle.clip_norm(np_bits(x), np_bits(a), np_bits(gm), -0.5, 2.0)
+    xd = dev(x)
+    kcr.clip_norm(xd, dev(a), dev(gm), -0.5, 2.0, out=xd)
+    assert_close(xd.cpu().double().numpy(), ref, torch.bfloat16, "clip norm in place")
+
+
 # ------------------------------------------------------------------ copy
 def test_copy(kcr):
     src = torch.randint(-2**31, 2**31 - 1, (1 << 20,), dtype=torch.int32, device="cuda")
