@@ -6,7 +6,8 @@ benchmark's ``cpu_baseline`` leg may import this package; the library in
 
 The arithmetic lives in ``oracle.c`` (plain C, double precision, built with
 gcc). This module only marshals numpy arrays into it. bf16 data travels as
-its raw uint16 bit patterns, fp32 as float32.
+its raw uint16 bit patterns, fp16 as numpy float16 (only stored and passed on,
+never used for arithmetic here), fp32 as float32.
 
 Parity of every function is pinned in the CPU tests (closed forms,
 invariants, hand-worked cases in ``tests/golden`` and independent library
@@ -24,7 +25,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
-BF16, F32 = 0, 1
+BF16, F32, F16 = 0, 1, 2
+_STORE = {BF16: np.uint16, F32: np.float32, F16: np.float16}
 CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared"]
 
 _lib = None
@@ -88,7 +90,9 @@ def _code(a: np.ndarray) -> int:
         return BF16
     if a.dtype == np.float32:
         return F32
-    raise TypeError(f"oracle takes bf16 bits (uint16) or float32, got {a.dtype}")
+    if a.dtype == np.float16:
+        return F16
+    raise TypeError(f"oracle takes bf16 bits (uint16), float16 or float32, got {a.dtype}")
 
 
 def _rows(a: np.ndarray):
@@ -107,7 +111,7 @@ def encode(x: np.ndarray, dtype: int, L=None) -> np.ndarray:
     """Round float64 values to the storage dtype (nearest, ties to even)."""
     L = L or lib()
     x = np.ascontiguousarray(x, dtype=np.float64)
-    out = np.empty(x.shape, dtype=np.uint16 if dtype == BF16 else np.float32)
+    out = np.empty(x.shape, dtype=_STORE[dtype])
     L.orc_encode(_ptr(x), _ptr(out), x.size, dtype)
     return out
 

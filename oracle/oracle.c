@@ -31,7 +31,7 @@
  *     before RoPE (sections 0, 3.3), the paged gather (section 1.4), ReGLU
  *     and the DyHT clip norm (sections 0, 3.3).
  *
- * Inputs arrive in their storage dtype (bf16 bit patterns or fp32) and are
+ * Inputs arrive in their storage dtype (bf16 or fp16 bit patterns, or fp32) and are
  * widened exactly to double. Results are returned in double, except values
  * that the op itself defines as stored data (the updated residual, the cache
  * image), which are rounded once, to nearest with ties to even, into the
@@ -47,7 +47,7 @@
 #include <omp.h>
 #endif
 
-enum { ORC_BF16 = 0, ORC_F32 = 1 };
+enum { ORC_BF16 = 0, ORC_F32 = 1, ORC_F16 = 2 };
 
 /* ------------------------------------------------------------ dtype codec */
 
@@ -85,20 +85,58 @@ static uint16_t double_to_bf16(double v) {
     return (uint16_t)(sign | (uint16_t)(u >> 16));
 }
 
+/* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ * Exponent field 0 holds zero and the subnormals (fraction * 2^-24), field
+ * 31 the infinities and NaNs. */
+static double f16_to_double(uint16_t h) {
+    int ex = (h >> 10) & 0x1F;
+    int fr = h & 0x3FF;
+    double mag;
+    if (ex == 0) mag = ldexp((double)fr, -24);
+    else if (ex == 31) mag = fr ? NAN : INFINITY;
+    else mag = ldexp((double)(1024 + fr), ex - 25);
+    return (h & 0x8000u) ? -mag : mag;
+}
+
+/* Round a double to the nearest binary16 value, ties to even, in one step.
+ * binary16 keeps 11 significant bits; its normals start at 2^-14, below
+ * which the spacing is fixed at 2^-24. */
+static uint16_t double_to_f16(double v) {
+    uint16_t sign = signbit(v) ? 0x8000u : 0;
+    if (isnan(v)) return (uint16_t)(sign | 0x7E00u);
+    double a = fabs(v);
+    if (a == 0.0) return sign;
+    /* Largest finite value (2 - 2^-10) * 2^15 = 65504; the midpoint to the
+     * next step 2^16 is 65520, and from there on the result is inf. */
+    if (a >= 65520.0) return (uint16_t)(sign | 0x7C00u);
+    int e;
+    frexp(a, &e);
+    int lg = e - 1;
+    if (lg < -14) lg = -14;
+    double q = ldexp(1.0, lg - 10);
+    double r = rint(a / q) * q; /* exact: a binary16 value */
+    if (r < ldexp(1.0, -14)) return (uint16_t)(sign | (uint16_t)ldexp(r, 24));
+    frexp(r, &e);               /* r in [2^(e-1), 2^e) */
+    uint16_t frac = (uint16_t)(ldexp(r, 11 - e) - 1024.0);
+    return (uint16_t)(sign | (uint16_t)((e - 1 + 15) << 10) | frac);
+}
+
 static double load(const void* base, int64_t i, int dtype) {
     if (dtype == ORC_BF16) return bf16_to_double(((const uint16_t*)base)[i]);
+    if (dtype == ORC_F16) return f16_to_double(((const uint16_t*)base)[i]);
     return (double)((const float*)base)[i];
 }
 
 /* C's double -> float conversion rounds to nearest even in one step. */
 static void store(void* base, int64_t i, double v, int dtype) {
     if (dtype == ORC_BF16) ((uint16_t*)base)[i] = double_to_bf16(v);
+    else if (dtype == ORC_F16) ((uint16_t*)base)[i] = double_to_f16(v);
     else ((float*)base)[i] = (float)v;
 }
 
 static void copy_bits(void* dst, int64_t di, const void* src, int64_t si, int dtype) {
-    if (dtype == ORC_BF16) ((uint16_t*)dst)[di] = ((const uint16_t*)src)[si];
-    else ((uint32_t*)dst)[di] = ((const uint32_t*)src)[si];
+    if (dtype == ORC_F32) ((uint32_t*)dst)[di] = ((const uint32_t*)src)[si];
+    else ((uint16_t*)dst)[di] = ((const uint16_t*)src)[si];
 }
 
 void orc_encode(const double* in, void* out, int64_t n, int dtype) {

@@ -26,13 +26,13 @@ F32_FLOOR = 1.1754943508222875e-38
 
 def np_bits(t: torch.Tensor) -> np.ndarray:
     """CPU tensor -> numpy view in the oracle's storage convention (bf16 as
-    uint16 bit patterns, fp32 as float32); strides are kept."""
+    uint16 bit patterns, fp16 as float16, fp32 as float32); strides are kept."""
     t = t.detach()
     if t.device.type != "cpu":
         t = t.cpu()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
-    if t.dtype == torch.float32:
+    if t.dtype in (torch.float32, torch.float16):
         return t.numpy()
     raise TypeError(t.dtype)
 

@@ -24,8 +24,9 @@ import workloads
 from helpers import np_bits
 
 GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
-BF16, F32 = oracle.BF16, oracle.F32
-TORCH_DT = {BF16: torch.bfloat16, F32: torch.float32}
+BF16, F32, F16 = oracle.BF16, oracle.F32, oracle.F16
+TORCH_DT = {BF16: torch.bfloat16, F32: torch.float32, F16: torch.float16}
+DTS = (F32, BF16, F16)
 
 
 def golden(name):
@@ -86,17 +87,62 @@ def pin_decode_known(L):
     assert list(got) == want and math.copysign(1, got[4]) == -1
 
 
+def pin_f16_decode_every_pattern(L):
+    # All 65536 binary16 patterns against numpy's float16 widening.
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    h = bits.view(np.float16)
+    got = oracle.decode(h, L=L)
+    want = h.astype(np.float64)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint64), want[~nan].view(np.uint64))
+
+
+def pin_f16_encode_vs_numpy(L):
+    # numpy rounds float64 -> float16 to nearest even in one step; the values
+    # span the subnormals, the normals and the overflow threshold.
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal(200000) * np.exp2(rng.integers(-30, 18, 200000))
+    x = np.concatenate([x, [65519.99, 65520.0, -65520.0, 2.0 ** -25, 2.0 ** -26, 1e-9, -0.0]])
+    got = oracle.encode(x, F16, L=L)
+    with np.errstate(over="ignore"):
+        want = x.astype(np.float16)
+    assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+
+
+def pin_f16_ties_closed_form(L):
+    # Exact midpoints between neighbouring finite binary16 values go to the
+    # one with an even last bit; a nudge of one part in 2^30 either way goes
+    # to the nearer neighbour. Built from the bit patterns alone.
+    pos = np.arange(0, 0x7C00, dtype=np.uint32)
+    lo = pos[:-1].astype(np.uint16).view(np.float16).astype(np.float64)
+    hi = pos[1:].astype(np.uint16).view(np.float16).astype(np.float64)
+    mid = (lo + hi) / 2                      # exact in float64
+    even = np.where(pos[:-1] % 2 == 0, pos[:-1], pos[1:]).astype(np.uint16)
+    assert np.array_equal(oracle.encode(mid, F16, L=L).view(np.uint16), even)
+    assert np.array_equal(oracle.encode(-mid, F16, L=L).view(np.uint16), even | 0x8000)
+    gap = hi - lo
+    assert np.array_equal(oracle.encode(mid - gap * 2.0 ** -30, F16, L=L).view(np.uint16),
+                          pos[:-1].astype(np.uint16))
+    assert np.array_equal(oracle.encode(mid + gap * 2.0 ** -30, F16, L=L).view(np.uint16),
+                          pos[1:].astype(np.uint16))
+    # 65504 is the largest finite value; its midpoint to 2^16 rounds to inf
+    top = oracle.encode(np.array([65504.0, 65519.0, 65520.0, math.inf, -math.inf]), F16, L=L)
+    assert list(top.view(np.uint16)) == [0x7BFF, 0x7BFF, 0x7C00, 0x7C00, 0xFC00]
+    assert np.isnan(oracle.encode(np.array([math.nan]), F16, L=L)[0])
+
+
 # ----------------------------------------------------------- RMSNorm pins
 def pin_rmsnorm_golden(L):
     for c in golden("rmsnorm_hand.json")["cases"]:
-        for dt in (F32, BF16):
+        for dt in DTS:
             y = oracle.rmsnorm(enc([c["x"]], dt), enc(c["w"], dt), c["eps"], L=L)
             assert np.allclose(y[0], c["y"], rtol=1e-14, atol=0), (c, y)
 
 
 def pin_rmsnorm_meansq_closed_form(L):
     # Unit weight: y = x / sqrt(ms + eps), so mean(y^2) = ms / (ms + eps).
-    for dt in (F32, BF16):
+    for dt in DTS:
         x = rand_rows(16, 2176, dt, seed=3)
         xd = dec(x)
         for eps in (0.5, 1e-6):
@@ -106,7 +152,7 @@ def pin_rmsnorm_meansq_closed_form(L):
 
 
 def pin_rmsnorm_constant_row(L):
-    for dt in (F32, BF16):
+    for dt in DTS:
         for c in (0.75, -3.0, 100.0):
             w = enc(np.linspace(0.5, 1.5, 37), dt)
             y = oracle.rmsnorm(enc(np.full((1, 37), c), dt), w, 0.25, L=L)
@@ -122,7 +168,7 @@ def pin_rmsnorm_scale_invariance(L):
 
 
 def pin_rmsnorm_vs_torch(L):
-    for dt in (F32, BF16):
+    for dt in DTS:
         for d in (1, 7, 1536, 2176):
             x = rand_rows(9, d, dt, seed=5 + d, scale=3.0)
             w = enc(1 + 0.1 * np.random.default_rng(d).standard_normal(d), dt)
@@ -141,7 +187,7 @@ def pin_rmsnorm_row_stride(L):
 
 # ------------------------------------------------------ add + RMSNorm pins
 def pin_add_rmsnorm_zero_delta(L):
-    for dt in (F32, BF16):
+    for dt in DTS:
         x = rand_rows(5, 1536, dt, seed=7)
         w = enc(1 + 0.1 * np.random.default_rng(7).standard_normal(1536), dt)
         zero = enc(np.zeros((5, 1536)), dt)
@@ -155,7 +201,7 @@ def pin_add_rmsnorm_sum_rounding(L):
     # x_new = round(x + delta): for two bf16 (or fp32) inputs torch's float32
     # add is exact or rounds far from a bf16 tie, so the fp32 add followed by
     # torch's bf16 cast is an independent route to the same bits.
-    for dt in (F32, BF16):
+    for dt in DTS:
         x = rand_rows(7, 2048, dt, seed=8)
         dl = rand_rows(7, 2048, dt, seed=9, scale=0.01)
         xn, _ = oracle.add_rmsnorm(x, dl, enc(np.ones(2048), dt), 1e-6, L=L)
@@ -193,7 +239,7 @@ def _one_head(x, dt, pos, theta, L):
 
 def pin_rope_golden(L):
     for c in golden("rope_hand.json")["cases"]:
-        for dt in (F32, BF16):
+        for dt in DTS:
             qr, kr = _one_head(c["x"], dt, c["pos"], c["theta"], L)
             assert np.allclose(qr, c["out"], rtol=1e-13, atol=1e-15), (c, qr)
             assert np.array_equal(qr, kr)
@@ -205,7 +251,7 @@ def _heads(T, H, d, dt, seed):
 
 
 def pin_rope_position_zero_identity(L):
-    for dt in (F32, BF16):
+    for dt in DTS:
         q, k = _heads(3, 12, 128, dt, 14), _heads(3, 2, 128, dt, 15)
         qr, kr = oracle.rope_kvstore(q, k, k, np.zeros(3, np.int64), 1e6, None, None, L=L)
         assert np.array_equal(qr, dec(q)) and np.array_equal(kr, dec(k))
@@ -281,7 +327,7 @@ def pin_rope_strided_views(L):
 # ------------------------------------------------ qk-norm + RoPE pins
 def pin_qknorm_rope_golden(L):
     for c in golden("qknorm_rope_hand.json")["cases"]:
-        for dt in (F32, BF16):
+        for dt in DTS:
             d = len(c["x"])
             x = enc(np.array(c["x"]).reshape(1, 1, d), dt)
             w = enc(c["w"], dt)
@@ -344,7 +390,7 @@ def _sentinel(shape, dt):
 
 def pin_scatter_golden(L):
     for c in golden("scatter_hand.json")["cases"]:
-        for dt in (F32, BF16):
+        for dt in DTS:
             bs, nb, hkv, d = c["block_size"], c["num_blocks"], c["hkv"], c["d"]
             k, v = enc(c["k"], dt), enc(c["v"], dt)
             cache = _sentinel([2, nb, bs, hkv, d], dt)
@@ -402,7 +448,7 @@ def pin_gather_golden(L):
     # written at slots 5 and 0 at its positions 1 and 2, and the sentinel at
     # its never-written positions 0 and 3.
     c = golden("scatter_hand.json")["cases"][0]
-    for dt in (F32, BF16):
+    for dt in DTS:
         cache = _sentinel([2, c["num_blocks"], c["block_size"], c["hkv"], c["d"]], dt)
         oracle.rope_kvstore(enc(c["k"], dt), enc(c["k"], dt), enc(c["v"], dt),
                             np.array(c["positions"]), 1e6, cache, np.array(c["slots"]),
@@ -450,7 +496,7 @@ def pin_swiglu_limits(L):
 
 
 def pin_swiglu_vs_torch(L):
-    for dt in (F32, BF16):
+    for dt in DTS:
         g, u = rand_rows(7, 1000, dt, 26, scale=2.0), rand_rows(7, 1000, dt, 27)
         out = oracle.swiglu(g, u, L=L)
         ref = F.silu(torch.from_numpy(dec(g))) * torch.from_numpy(dec(u))
@@ -467,13 +513,13 @@ def pin_swiglu_fused_halves(L):
 # ------------------------------------------------- ReGLU and clip-norm pins
 def pin_reglu_golden(L):
     c = golden("reglu_clip_norm_hand.json")["reglu"][0]
-    for dt in (F32, BF16):
+    for dt in DTS:
         out = oracle.reglu(enc([c["g"]], dt), enc([c["u"]], dt), L=L)[0]
         assert np.array_equal(out, c["out"]), out
 
 
 def pin_reglu_vs_torch(L):
-    for dt in (F32, BF16):
+    for dt in DTS:
         g, u = rand_rows(6, 1001, dt, 61, scale=2.0), rand_rows(6, 1001, dt, 62)
         ref = F.relu(torch.from_numpy(dec(g))) * torch.from_numpy(dec(u))
         assert np.allclose(oracle.reglu(g, u, L=L), ref.numpy(), rtol=0, atol=0)
@@ -481,7 +527,7 @@ def pin_reglu_vs_torch(L):
 
 def pin_clip_norm_golden(L):
     for c in golden("reglu_clip_norm_hand.json")["clip_norm"]:
-        for dt in (F32, BF16):
+        for dt in DTS:
             d = len(c["x"])
             y = oracle.clip_norm(enc(np.array(c["x"]).reshape(1, 1, d), dt), enc(c["alpha"], dt),
                                  enc(c["gamma"], dt), c["lo"], c["hi"], L=L)

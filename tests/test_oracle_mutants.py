@@ -46,6 +46,12 @@ MUTANTS = {
     "clip_upper_bound_missing": ("                if (v > hi) v = hi;\n", ""),
     "clip_gamma_before_clamp": ("                double v = a * load(x, t * x_ts + h * x_hs + e, dtype);",
                                 "                double v = a * g * load(x, t * x_ts + h * x_hs + e, dtype);"),
+    "f16_bias_off_by_one": ("else mag = ldexp((double)(1024 + fr), ex - 25);",
+                            "else mag = ldexp((double)(1024 + fr), ex - 24);"),
+    "f16_no_subnormal_spacing": ("    if (lg < -14) lg = -14;\n    double q = ldexp(1.0, lg - 10);",
+                                 "    double q = ldexp(1.0, lg - 10);"),
+    "f16_truncates": ("double r = rint(a / q) * q;", "double r = floor(a / q) * q;"),
+    "f16_overflow_at_max": ("if (a >= 65520.0) return", "if (a >= 65504.0) return"),
     "gqa_modulo": ("return h / (hq / hkv);", "return h % hkv;"),
     "gather_offset_from_block": ("int64_t block = block_table[t / block_size], offset = t % block_size;",
                                  "int64_t block = block_table[t / block_size], offset = (t + 1) % block_size;"),

@@ -38,11 +38,11 @@ EPS = 1.0e-6
 BLOCK_SIZE = 16
 
 # Fill pattern for cache bytes that a call must leave alone: all-ones bits,
-# a NaN in both bf16 and fp32, so an accidental read-modify-write shows up.
-SENTINEL_BITS = {torch.bfloat16: 0xFFFF, torch.float32: 0xFFFFFFFF}
+# a NaN in bf16, fp16 and fp32, so an accidental read-modify-write shows up.
+SENTINEL_BITS = {torch.bfloat16: 0xFFFF, torch.float16: 0xFFFF, torch.float32: 0xFFFFFFFF}
 
-_DT = {"bf16": torch.bfloat16, "f32": torch.float32, torch.bfloat16: torch.bfloat16,
-       torch.float32: torch.float32}
+_DT = {"bf16": torch.bfloat16, "f32": torch.float32, "f16": torch.float16,
+       torch.bfloat16: torch.bfloat16, torch.float32: torch.float32, torch.float16: torch.float16}
 
 
 def as_dtype(dt) -> torch.dtype:
@@ -66,7 +66,7 @@ def sentinel_cache(shape, dtype) -> torch.Tensor:
     """A cache tensor whose every element holds the all-ones bit pattern."""
     dtype = as_dtype(dtype)
     t = torch.empty(shape, dtype=dtype)
-    if dtype == torch.bfloat16:
+    if dtype.itemsize == 2:
         t.view(torch.int16).fill_(-1)
     else:
         t.view(torch.int32).fill_(-1)
