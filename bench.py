@@ -129,7 +129,7 @@ def large_shapes(kcr, iters: int):
         log(f"{name}: {st['median_us']:.1f} us median, {gbs:.0f} GB/s ({100 * gbs / PEAK_GBS:.1f}% of peak)")
 
     R = 131072
-    for dt, tag in ((torch.bfloat16, "bf16"), (torch.float32, "f32")):
+    for dt, tag in ((torch.bfloat16, "bf16"), (torch.float32, "f32"), (torch.float16, "f16")):
         wl = workloads.rmsnorm_rows(rows=R, d=2176, dtype=tag, seed=0)
         xs = [wl["x"].to(dev)]
         xs += [xs[0].clone() for _ in range(2)]
@@ -138,6 +138,29 @@ def large_shapes(kcr, iters: int):
         fns = [lambda i=i: kcr.rmsnorm(xs[i], w, wl["eps"], out=ys[i]) for i in range(3)]
         run(f"rmsnorm_{tag}", norm_bytes(R, 2176, xs[0].element_size(), False), fns, f"[{R}, 2176] {tag}")
         del xs, ys, wl
+    # rows wider than the register-resident engine: the two-pass kernel,
+    # LDS-staged (65536 bf16 = 128 KB rows) and re-reading (262144 bf16)
+    for rows, d, add, name in ((2048, 65536, False, "rmsnorm_bf16_wide_staged"),
+                               (512, 262144, False, "rmsnorm_bf16_wide_reread"),
+                               (2048, 65536, True, "add_rmsnorm_bf16_wide_staged")):
+        if add:
+            wl = workloads.add_rmsnorm_rows(rows, d, dtype="bf16", seed=0)
+            xs = [wl["x"].to(dev) for _ in range(3)]
+            ds = [wl["delta"].to(dev) for _ in range(3)]
+        else:
+            wl = workloads.rmsnorm_rows(rows=rows, d=d, dtype="bf16", seed=0)
+            xs = [wl["x"].to(dev)]
+            xs += [xs[0].clone() for _ in range(2)]
+        ys = [torch.empty_like(xs[0]) for _ in range(3)]
+        w = wl["w"].to(dev)
+        if add:
+            fns = [lambda i=i: kcr.add_rmsnorm(xs[i], ds[i], w, wl["eps"], out=ys[i]) for i in range(3)]
+        else:
+            fns = [lambda i=i: kcr.rmsnorm(xs[i], w, wl["eps"], out=ys[i]) for i in range(3)]
+        run(name, norm_bytes(rows, d, 2, add), fns, f"[{rows}, {d}] bf16")
+        del xs, ys, wl
+        if add:
+            del ds
     # DyHT clip norm on the same rows as RMSNorm bf16, per-channel alpha and gamma
     wl = workloads.rmsnorm_rows(rows=R, d=2176, dtype="bf16", seed=0)
     xs = [wl["x"].to(dev)]
@@ -232,6 +255,54 @@ def graph_op_us(kcr, chain, reps: int):
         torch.cuda.synchronize()
         out[name] = e0.elapsed_time(e1) * 1e3 / (reps * len(fns))
         del g
+    return out
+
+
+def rmsnorm_sweep(kcr, reps: int):
+    """RMSNorm over [2 x 256, D] rows, the microbenchmark shape of the Zhihu
+    "RMSNorm in Triton" page (D = 128 ... 8196; FP32, FP16, BF16). Each point
+    is the per-launch time inside a captured graph of 64 launches over 16
+    rotated buffer sets, so it includes the graph's per-node launch cost;
+    GB/s counts the algorithmic bytes (x read, y written, w once)."""
+    import torch
+    from kv_cache_rmsnorm_amd.chain import norm_bytes
+    rows, sets, launches = 512, 16, 64
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    out = {}
+    for dt, tag in ((torch.float32, "f32"), (torch.float16, "f16"), (torch.bfloat16, "bf16")):
+        out[tag] = {}
+        for d in (128, 256, 512, 1024, 1536, 2048, 2176, 4096, 8192, 8196):
+            xs = [torch.randn((rows, d), generator=g, device="cuda").to(dt) for _ in range(sets)]
+            ys = [torch.empty_like(x) for x in xs]
+            w = torch.randn((d,), generator=g, device="cuda").to(dt)
+            fns = [lambda i=i: kcr.rmsnorm(xs[i % sets], w, 1e-6, out=ys[i % sets]) for i in range(launches)]
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                for f in fns:
+                    f()
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for f in fns:
+                    f()
+            for _ in range(3):
+                graph.replay()
+            torch.cuda.synchronize()
+            e0, e1 = events(2)
+            e0.record()
+            for _ in range(reps):
+                graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (reps * launches)
+            nb = norm_bytes(rows, d, xs[0].element_size(), False)
+            out[tag][str(d)] = dict(us=round(us, 3), gbs=round(nb / (us * 1e-6) / 1e9, 1))
+            del graph, xs, ys
+        log(f"sweep [512, D] {tag}: " + ", ".join(f"{d}:{v['us']:.2f}us/{v['gbs']:.0f}GB/s"
+                                                 for d, v in out[tag].items()))
     return out
 
 
@@ -396,6 +467,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--skip-large", action="store_true", help="skip the per-kernel large shapes")
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--skip-sweep", action="store_true", help="skip the [512, D] RMSNorm sweep")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="only launch each kernel eagerly (for rocprofv3 --pmc runs); no JSON line")
     args = ap.parse_args()
@@ -471,6 +543,7 @@ def main():
     log("in-graph per-launch us: " + ", ".join(f"{k} {v:.2f}" for k, v in op_graph.items()))
     ceiling = copy_ceiling(kcr, args.kernel_iters)
     kernels = {} if args.skip_large else large_shapes(kcr, args.kernel_iters)
+    sweep = {} if args.skip_sweep else rmsnorm_sweep(kcr, max(10, args.steps // 5))
 
     traffic, traffic_note = counter_traffic("swiglu")
     achieved = sw_bytes / (sw_us * 1e-6) / 1e9
@@ -509,8 +582,10 @@ def main():
         "cpu_baseline": cpu,
         "ceiling": ceiling,
         "kernels": kernels,
+        "rmsnorm_sweep_512xD": sweep,
         "device": torch.cuda.get_device_name(0),
         "cus": kcr.device_cus(),
+        "lds_per_block": torch.cuda.get_device_properties(0).shared_memory_per_block,
     }
     print(json.dumps(line), flush=True)
 

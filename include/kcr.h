@@ -43,7 +43,8 @@ extern "C" {
 
 typedef enum kcr_dtype {
     KCR_BF16 = 0, /* bfloat16 storage, fp32 arithmetic */
-    KCR_F32 = 1   /* float32 storage and arithmetic */
+    KCR_F32 = 1,  /* float32 storage and arithmetic */
+    KCR_F16 = 2   /* IEEE binary16 storage, fp32 arithmetic */
 } kcr_dtype;
 
 enum kcr_status {
@@ -58,10 +59,14 @@ enum kcr_status {
     KCR_ERR_DEVICE = -8  /* no usable HIP device is current */
 };
 
-/* Largest row width of the register-resident RMSNorm: 32768 bf16 or
- * 16384 fp32 elements (one 256-lane workgroup, 16 x 16 bytes per lane). */
-#define KCR_NORM_MAX_D_BF16 32768
-#define KCR_NORM_MAX_D_F32 16384
+/* Row widths of kcr_rmsnorm / kcr_add_rmsnorm. Rows of up to 4096 16-byte
+ * vectors (32768 bf16/fp16 or 16384 fp32 elements) are held in registers
+ * and read from HBM once. Wider rows take a two-pass form, one workgroup per
+ * row: rows of up to about 160 KB are staged in LDS and still read once;
+ * wider rows are read twice. KCR_NORM_MAX_D bounds every dtype. */
+#define KCR_NORM_REG_MAX_D_16 32768
+#define KCR_NORM_REG_MAX_D_F32 16384
+#define KCR_NORM_MAX_D (1 << 30)
 /* Largest head_dim accepted by kcr_rope_kvstore. */
 #define KCR_ROPE_MAX_HEAD_DIM 512
 
@@ -85,7 +90,7 @@ enum kcr_status {
  *   eps  added to the mean square before the reciprocal square root
  *
  * y may be x itself (same pointer and stride: in-place); any other overlap
- * of y with x or w is KCR_ERR_ALIAS. 1 <= d <= KCR_NORM_MAX_D_* else
+ * of y with x or w is KCR_ERR_ALIAS. 1 <= d <= KCR_NORM_MAX_D else
  * KCR_ERR_SHAPE.
  */
 int kcr_rmsnorm(const void* x, int64_t x_stride, const void* w, void* y, int64_t y_stride,

@@ -25,8 +25,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkcr.so")
 
-BF16, F32 = 0, 1
-_DTYPE = {torch.bfloat16: BF16, torch.float32: F32}
+BF16, F32, F16 = 0, 1, 2
+_DTYPE = {torch.bfloat16: BF16, torch.float32: F32, torch.float16: F16}
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python kv_cache_rmsnorm_amd/build.py`")

@@ -1,7 +1,8 @@
 """Builds libkcr.so, the gfx950 HIP library behind the C ABI in include/kcr.h.
 
 Every source in csrc/ is compiled by hipcc for gfx950 only, in parallel, and
-linked into kv_cache_rmsnorm_amd/libkcr.so. Packed-fp32 instruction
+linked into kv_cache_rmsnorm_amd/libkcr.so. norm_inst.hip is compiled once
+per storage type and norm variant (six objects). Packed-fp32 instruction
 selection is switched off for the device code.
 """
 from __future__ import annotations
@@ -29,9 +30,15 @@ CXXFLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OUT_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CXXFLAGS, "-c", src, "-o", obj]
+# (storage type, add variant) pairs of the row-norm engine
+NORM_VARIANTS = [(t, add) for t in ("Bf16", "F16", "F32") for add in (0, 1)]
+
+
+def _compile(job) -> str:
+    src, defines = job
+    tag = "".join(f"_{v}" for _, v in defines)
+    obj = os.path.join(OUT_DIR, os.path.basename(src) + tag + ".o")
+    cmd = [HIPCC, *CXXFLAGS, *[f"-D{k}={v}" for k, v in defines], "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
@@ -47,14 +54,19 @@ def build(verbose: bool = True) -> str:
     """Compile every csrc/*.hip for gfx950 and link libkcr.so (always rebuilds)."""
     os.makedirs(OUT_DIR, exist_ok=True)
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    jobs = min(len(sources), max(1, min(8, os.cpu_count() or 1)))
+    inst = os.path.join(CSRC, "norm_inst.hip")
+    work = [(s, ()) for s in sources if s != inst]
+    work += [(inst, (("KCR_NORM_T", t), ("KCR_NORM_ADD", add))) for t, add in NORM_VARIANTS]
+    # the norm instantiations are the slowest; start them first
+    work.sort(key=lambda j: j[0] != inst)
+    jobs = min(len(work), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, sources))
+        objs = list(ex.map(_compile, work))
     tmp = LIB + ".tmp"
     subprocess.run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], check=True)
     os.replace(tmp, LIB)
     if verbose:
-        print(f"built {LIB} from {len(sources)} sources")
+        print(f"built {LIB} from {len(sources)} sources ({len(work)} objects)")
     return LIB
 
 

@@ -98,6 +98,7 @@ extern "C" int kcr_clip_norm(const void* x, int64_t x_tok_stride, int64_t x_head
                total, make_fastdiv((uint32_t)vpr), make_fastdiv((uint32_t)n_head),
                alpha_per_channel ? 1 : 0, gamma_per_channel ? 1 : 0};
     const dim3 grid((total + 63) / 64);
-    return dtype == KCR_BF16 ? launch(clip_norm_kernel<Bf16>, grid, dim3(64), stream, a)
-                             : launch(clip_norm_kernel<F32>, grid, dim3(64), stream, a);
+    return by_dtype(dtype, [&](auto t) {
+        return launch(clip_norm_kernel<decltype(t)>, grid, dim3(64), stream, a);
+    });
 }

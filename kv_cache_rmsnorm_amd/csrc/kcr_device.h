@@ -1,6 +1,6 @@
 // kcr_device.h -- device-side building blocks shared by the gfx950 kernels:
-// 16-byte vector loads and stores with an element-wise tail, bf16 <-> fp32
-// conversion, and the wave64 sum reduction.
+// 16-byte vector loads and stores with an element-wise tail, bf16 and fp16
+// <-> fp32 conversion, and the wave64 sum reduction.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -11,6 +11,7 @@ namespace kcr {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // Storage types. kVec is the number of elements in one 16-byte vector, the
 // unit of every global load and store (global_load_dwordx4 /
@@ -22,6 +23,10 @@ struct Bf16 {
 struct F32 {
     using storage = float;
     static constexpr int kVec = 4;
+};
+struct F16 {
+    using storage = uint16_t;
+    static constexpr int kVec = 8;
 };
 
 // ---------------------------------------------------------------- codec
@@ -40,6 +45,20 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(pack_bf16x2(f, 0.0f) & 0xffffu);
 }
 
+// IEEE binary16: widening to fp32 is exact (subnormals included); narrowing
+// rounds to nearest even, overflowing to inf, in the default float mode.
+__device__ __forceinline__ f32x2 f16x2_to_f32(uint32_t w) {
+    return __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    f32x2 f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+}
+__device__ __forceinline__ float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
 // Unpack a 16-byte vector into kVec floats, and pack back.
 template <typename T>
 __device__ __forceinline__ void unpack(const u32x4& v, float* f);
@@ -49,6 +68,15 @@ __device__ __forceinline__ void unpack<Bf16>(const u32x4& v, float* f) {
     for (int j = 0; j < 4; ++j) {
         f[2 * j] = bf16_lo(v[j]);
         f[2 * j + 1] = bf16_hi(v[j]);
+    }
+}
+template <>
+__device__ __forceinline__ void unpack<F16>(const u32x4& v, float* f) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const f32x2 p = f16x2_to_f32(v[j]);
+        f[2 * j] = p[0];
+        f[2 * j + 1] = p[1];
     }
 }
 template <>
@@ -67,6 +95,13 @@ __device__ __forceinline__ u32x4 pack<Bf16>(const float* f) {
     return v;
 }
 template <>
+__device__ __forceinline__ u32x4 pack<F16>(const float* f) {
+    u32x4 v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = pack_f16x2(f[2 * j], f[2 * j + 1]);
+    return v;
+}
+template <>
 __device__ __forceinline__ u32x4 pack<F32>(const float* f) {
     u32x4 v;
 #pragma unroll
@@ -82,6 +117,10 @@ __device__ __forceinline__ float load_one<Bf16>(const void* base, int64_t i) {
     return bf16_to_f32(static_cast<const uint16_t*>(base)[i]);
 }
 template <>
+__device__ __forceinline__ float load_one<F16>(const void* base, int64_t i) {
+    return f16_to_f32(static_cast<const uint16_t*>(base)[i]);
+}
+template <>
 __device__ __forceinline__ float load_one<F32>(const void* base, int64_t i) {
     return static_cast<const float*>(base)[i];
 }
@@ -90,6 +129,10 @@ __device__ __forceinline__ void store_one(void* base, int64_t i, float v);
 template <>
 __device__ __forceinline__ void store_one<Bf16>(void* base, int64_t i, float v) {
     static_cast<uint16_t*>(base)[i] = f32_to_bf16(v);
+}
+template <>
+__device__ __forceinline__ void store_one<F16>(void* base, int64_t i, float v) {
+    static_cast<uint16_t*>(base)[i] = f32_to_f16(v);
 }
 template <>
 __device__ __forceinline__ void store_one<F32>(void* base, int64_t i, float v) {
@@ -149,7 +192,7 @@ __device__ __forceinline__ void store_vec(void* base, int64_t elem, int64_t n, c
 // is 16-byte aligned; when it is, every vector wholly inside the row moves
 // with one 16-byte access, and otherwise (and for the vector that straddles
 // the end of the row) element by element. Elements past the end of the row
-// read as zero bits (+0.0 in both dtypes) and are never written.
+// read as zero bits (+0.0 in every dtype) and are never written.
 __host__ __device__ __forceinline__ bool aligned16(const void* p) {
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }

@@ -16,8 +16,18 @@ constexpr int kMaxDevices = 64;
 // Compute units of the current device, cached per device (0 if no device).
 int device_cus();
 
-inline size_t dtype_size(int dtype) { return dtype == KCR_BF16 ? 2 : 4; }
-inline bool dtype_ok(int dtype) { return dtype == KCR_BF16 || dtype == KCR_F32; }
+inline size_t dtype_size(int dtype) { return dtype == KCR_F32 ? 4 : 2; }
+inline bool dtype_ok(int dtype) { return dtype == KCR_BF16 || dtype == KCR_F32 || dtype == KCR_F16; }
+
+// Calls fn(Bf16{}), fn(F16{}) or fn(F32{}) for a dtype that passed dtype_ok.
+template <typename Fn>
+inline int by_dtype(int dtype, Fn&& fn) {
+    switch (dtype) {
+        case KCR_BF16: return fn(Bf16{});
+        case KCR_F16: return fn(F16{});
+        default: return fn(F32{});
+    }
+}
 
 inline bool aligned_elem(const void* p, size_t esize) {
     return (reinterpret_cast<uintptr_t>(p) & (esize - 1)) == 0;
@@ -90,8 +100,10 @@ TimingEvents& next_launch_events();
 // runtime's verdict for this launch. When the calling thread armed timing
 // events, the launch goes through hipExtLaunchKernel, which stamps them at
 // the kernel's own start and end.
+// `lds` is the dynamic LDS size in bytes.
 template <typename Args>
-inline int launch(void (*kern)(Args), dim3 grid, dim3 block, void* stream, const Args& args) {
+inline int launch(void (*kern)(Args), dim3 grid, dim3 block, void* stream, const Args& args,
+                  size_t lds = 0) {
     Args copy = args;
     void* params[] = {&copy};
     TimingEvents& ev = next_launch_events();
@@ -99,10 +111,10 @@ inline int launch(void (*kern)(Args), dim3 grid, dim3 block, void* stream, const
     if (ev.start || ev.stop) {
         const TimingEvents use = ev;
         ev = TimingEvents{};
-        e = hipExtLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, params, 0,
+        e = hipExtLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, params, lds,
                                static_cast<hipStream_t>(stream), use.start, use.stop, 0);
     } else {
-        e = hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, params, 0,
+        e = hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, params, lds,
                             static_cast<hipStream_t>(stream));
     }
     return e == hipSuccess ? KCR_OK : KCR_ERR_LAUNCH;

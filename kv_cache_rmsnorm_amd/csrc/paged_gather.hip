@@ -99,6 +99,7 @@ extern "C" int kcr_paged_kv_gather(const void* kv_cache, int64_t num_blocks, int
                  num_blocks * block_size * row, tokens, (uint32_t)cpt, (uint32_t)(row / vec),
                  make_fastdiv((uint32_t)max_len), make_fastdiv((uint32_t)block_size)};
     const dim3 grid((tokens + 3) / 4);
-    return dtype == KCR_BF16 ? launch(paged_gather_kernel<Bf16>, grid, dim3(256), stream, a)
-                             : launch(paged_gather_kernel<F32>, grid, dim3(256), stream, a);
+    // The gather moves bits: both 2-byte dtypes take the same kernel.
+    return dtype == KCR_F32 ? launch(paged_gather_kernel<F32>, grid, dim3(256), stream, a)
+                            : launch(paged_gather_kernel<Bf16>, grid, dim3(256), stream, a);
 }

@@ -330,8 +330,7 @@ extern "C" int kcr_rope_kvstore(const void* q, int64_t q_tok_stride, int64_t q_h
                                 max_pos, kv_cache, slot_mapping, T, n_head, n_kv_head, head_dim,
                                 block_size, num_blocks, dtype, &a, &work);
     if (rc != KCR_OK || !work) return rc;
-    return dtype == KCR_BF16 ? dispatch_rope<Bf16, false>(a, T, stream)
-                             : dispatch_rope<F32, false>(a, T, stream);
+    return by_dtype(dtype, [&](auto t) { return dispatch_rope<decltype(t), false>(a, T, stream); });
 }
 
 extern "C" int kcr_qknorm_rope_kvstore(const void* q, int64_t q_tok_stride, int64_t q_head_stride,
@@ -360,8 +359,7 @@ extern "C" int kcr_qknorm_rope_kvstore(const void* q, int64_t q_tok_stride, int6
     a.q_w = q_norm_w;
     a.k_w = k_norm_w;
     a.eps = eps;
-    return dtype == KCR_BF16 ? dispatch_rope<Bf16, true>(a, T, stream)
-                             : dispatch_rope<F32, true>(a, T, stream);
+    return by_dtype(dtype, [&](auto t) { return dispatch_rope<decltype(t), true>(a, T, stream); });
 }
 
 extern "C" int kcr_rope_cos_sin(float* cos_tab, float* sin_tab, int64_t max_pos, int head_dim,

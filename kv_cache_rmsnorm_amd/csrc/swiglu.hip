@@ -139,8 +139,9 @@ static int run_gated(const void* gate, int64_t gate_stride, const void* up, int6
     const int rc = gated_prepare(gate, gate_stride, up, up_stride, out, out_stride, rows, cols, dtype,
                                  &a, &work);
     if (rc != KCR_OK || !work) return rc;
-    return dtype == KCR_BF16 ? launch_swiglu<Bf16, GatedCfg, Act>(a, stream, kOnePass)
-                             : launch_swiglu<F32, GatedCfg, Act>(a, stream, kOnePass);
+    return by_dtype(dtype, [&](auto t) {
+        return launch_swiglu<decltype(t), GatedCfg, Act>(a, stream, kOnePass);
+    });
 }
 
 }  // namespace kcr

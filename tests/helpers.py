@@ -1,9 +1,12 @@
 """Test-side helpers: bit views between torch and numpy, and the comparison
 rules shared by the parity tests.
 
-Comparison rules (bf16 and fp32 outputs against the fp64 oracle):
+Comparison rules (bf16, fp16 and fp32 outputs against the fp64 oracle):
   * bf16: |gpu - ref| <= 2 * ulp_bf16(ref)  or  |gpu - ref| <= 1e-2, with
     ulp_bf16(y) = 2^(floor(log2|y|) - 7) (2^-133 at the bottom of the range);
+  * fp16: |gpu - ref| <= 2 * ulp_f16(ref), ulp_f16(y) = 2^(max(floor(log2|y|),
+    -14) - 10): the kernels compute in fp32 (relative error ~1e-6 here) and
+    round once, so they land within one fp16 ulp; the second ulp is margin;
   * fp32: |gpu - ref| <= 1e-5 * |ref|, with an absolute floor at the fp32
     normal minimum (1.2e-38) for results that underflow;
   * integer, index and copied data: bit-exact;
@@ -20,6 +23,7 @@ import workloads
 
 BF16_ATOL = 1e-2
 BF16_ULPS = 2.0
+F16_ULPS = 2.0
 F32_RTOL = 1e-5
 F32_FLOOR = 1.1754943508222875e-38
 
@@ -48,6 +52,12 @@ def ulp_bf16(ref: np.ndarray) -> np.ndarray:
     return np.where(a > 0, np.exp2(e - 7.0), 2.0 ** -133)
 
 
+def ulp_f16(ref: np.ndarray) -> np.ndarray:
+    a = np.abs(ref)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.exp2(np.maximum(e, -14.0) - 10.0)
+
+
 def tol_violations(got: np.ndarray, ref: np.ndarray, dtype) -> np.ndarray:
     """Boolean mask of elements outside the tolerance for ``dtype``."""
     got = np.asarray(got, dtype=np.float64)
@@ -55,6 +65,8 @@ def tol_violations(got: np.ndarray, ref: np.ndarray, dtype) -> np.ndarray:
     err = np.abs(got - ref)
     if dtype in (torch.bfloat16, "bf16"):
         ok = (err <= BF16_ULPS * ulp_bf16(ref)) | (err <= BF16_ATOL)
+    elif dtype in (torch.float16, "f16"):
+        ok = err <= F16_ULPS * ulp_f16(ref)
     else:
         ok = err <= np.maximum(F32_RTOL * np.abs(ref), F32_FLOOR)
     ok |= (got == ref)  # covers matching infinities
@@ -97,7 +109,8 @@ def assert_rope_close(got, ref, dt, what):
     """bf16: the common rule. fp32: |got - ref| <= 1e-5 * the norm of the
     rotation pair (i, i + d/2), which the rotation preserves; a relative
     bound per element would be meaningless where x_i c - x_{i+d/2} s
-    cancels."""
+    cancels. fp16: 2 fp16 ulps of the result plus the fp32 pair-norm term
+    (the rotation is done in fp32 and rounded once)."""
     if dt == torch.bfloat16:
         assert_close(got, ref, dt, what)
         return
@@ -105,7 +118,10 @@ def assert_rope_close(got, ref, dt, what):
     pn = np.sqrt(ref[..., :half] ** 2 + ref[..., half:] ** 2)
     scale = np.concatenate([pn, pn], axis=-1)
     err = np.abs(got - ref)
-    bad = err > np.maximum(1e-5 * scale, 1.2e-38)
+    bound = np.maximum(1e-5 * scale, 1.2e-38)
+    if dt == torch.float16:
+        bound = bound + F16_ULPS * ulp_f16(ref)
+    bad = err > bound
     assert not bad.any(), f"{what}: {int(bad.sum())} outside 1e-5 of the pair norm, max {err.max()}"
 
 
@@ -130,7 +146,7 @@ def check_rope(q, k, v, positions, cache0, slots, theta, q_gpu, cache_gpu, dt, w
     # K rows of live slots against the fp64 rotation
     tok = {int(s): t for t, s in enumerate(slots.numpy()) if 0 <= s < nb * bs}
     order = np.array([tok[int(s)] for s in live], dtype=np.int64)
-    kg = torch.from_numpy(g_flat[0][live].view(np.int16 if dt == torch.bfloat16 else np.int32).copy())
+    kg = torch.from_numpy(g_flat[0][live].view(np.int16 if dt.itemsize == 2 else np.int32).copy())
     kg = kg.view(dt).double().numpy()
     assert_rope_close(kg, k_rot[order], dt, f"{what}: K rows")
 

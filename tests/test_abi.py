@@ -14,7 +14,7 @@ HEADER = os.path.join(ROOT, "include", "kcr.h")
 LIB = os.path.join(ROOT, "kv_cache_rmsnorm_amd", "libkcr.so")
 
 OK, NULL, SHAPE, DTYPE, ALIGN, HEADS, ALIAS, LAUNCH, DEVICE = 0, -1, -2, -3, -4, -5, -6, -7, -8
-BF16, F32 = 0, 1
+BF16, F32, F16 = 0, 1, 2
 A = 1 << 20  # fake 16-byte-aligned device addresses, never dereferenced
 
 
@@ -69,8 +69,14 @@ def test_rmsnorm_validation(lib):
     assert f(A, 1536, A * 2, A * 3, 1536, 4, 1536, 1e-6, 7, None) == DTYPE
     assert f(A, 1536, A * 2, A * 3, 1536, -1, 1536, 1e-6, BF16, None) == SHAPE
     assert f(A, 1536, A * 2, A * 3, 1536, 4, 0, 1e-6, BF16, None) == SHAPE
-    assert f(A, 40000, A * 2, A * 3, 40000, 4, 40000, 1e-6, BF16, None) == SHAPE
-    assert f(A, 20000, A * 2, A * 3, 20000, 4, 20000, 1e-6, F32, None) == SHAPE
+    big = (1 << 30) + 1                                   # above KCR_NORM_MAX_D
+    assert f(A, big, A * 2, A * 3, big, 4, big, 1e-6, BF16, None) == SHAPE
+    # rows wider than the register-resident engine take the two-pass kernel
+    assert f(A, 40000, A * 2, A * 3, 40000, 4, 40000, 1e-6, BF16, None) in (DEVICE, OK)
+    assert f(A, 200000, A * 64, A * 128, 200000, 4, 200000, 1e-6, F32, None) in (DEVICE, OK)
+    # binary16 storage: accepted, 2-byte element alignment
+    assert f(A, 1536, A * 2, A * 3, 1536, 4, 1536, 1e-6, F16, None) in (DEVICE, OK)
+    assert f(A + 1, 1536, A * 2, A * 3, 1536, 4, 1536, 1e-6, F16, None) == ALIGN
     assert f(None, 1536, None, None, 1536, 0, 1536, 1e-6, BF16, None) == OK  # no work, no launch
     assert f(None, 1536, A * 2, A * 3, 1536, 4, 1536, 1e-6, BF16, None) == NULL
     assert f(A + 1, 1536, A * 2, A * 3, 1536, 4, 1536, 1e-6, BF16, None) == ALIGN
@@ -176,7 +182,7 @@ def test_gather_validation(lib):
         return f(a["c"], a["nb"], a["bs"], a["hkv"], a["hd"], a["bt"], a["mb"], a["ln"], a["n"],
                  a["ml"], a["k"], a["v"], a["dt"], None)
     assert g() in (DEVICE, OK)
-    assert g(dt=2) == DTYPE
+    assert g(dt=7) == DTYPE
     assert g(hkv=1, hd=4) == SHAPE             # 4 bf16 per row: not a 16-byte multiple
     assert g(ml=129) == SHAPE                  # more positions than the table can name
     assert g(n=0, c=None, bt=None) == OK

@@ -4,8 +4,8 @@ edge cases: widths 1..32768 including primes and 16-byte-misaligned tails,
 strided views, in-place forms, padding slots, out-of-range indices, empty
 calls and non-default streams.
 
-Tolerances (written out in helpers.py): bf16 within 2 ulp or 1e-2, fp32
-within 1e-5 relative; the updated residual, V and every untouched cache byte
+Tolerances (written out in helpers.py): bf16 within 2 ulp or 1e-2, fp16
+within 2 ulp, fp32 within 1e-5 relative; the updated residual, V and every untouched cache byte
 bit-exact."""
 import numpy as np
 import pytest
@@ -18,8 +18,8 @@ from helpers import (assert_bits_equal, assert_close, assert_rope_close, check_r
 
 pytestmark = pytest.mark.gpu
 
-DTS = [torch.bfloat16, torch.float32]
-DT_ID = {torch.bfloat16: "bf16", torch.float32: "f32"}
+DTS = [torch.bfloat16, torch.float32, torch.float16]
+DT_ID = {torch.bfloat16: "bf16", torch.float32: "f32", torch.float16: "f16"}
 
 
 @pytest.fixture(scope="module")
@@ -59,6 +59,64 @@ def test_rmsnorm_widest_bf16(kcr, d):
     y = kcr.rmsnorm(dev(wl["x"]), dev(wl["w"]), wl["eps"])
     ref = oracle.rmsnorm(np_bits(wl["x"]), np_bits(wl["w"]), float(np.float32(wl["eps"])))
     assert_close(y.cpu().double().numpy(), ref, torch.bfloat16, f"rmsnorm d={d}")
+
+
+# Rows wider than the register-resident engine (4096 vectors): the two-pass
+# kernel, LDS-staged while a row fits in 160 KB, else reading the row twice.
+WIDE = [(torch.bfloat16, 32769), (torch.bfloat16, 40000), (torch.bfloat16, 65536),
+        (torch.bfloat16, 81000), (torch.bfloat16, 100003), (torch.float16, 50001),
+        (torch.float16, 131072), (torch.float32, 16385), (torch.float32, 40000),
+        (torch.float32, 50001)]
+
+
+@pytest.mark.parametrize("dt,d", WIDE, ids=lambda v: DT_ID.get(v, str(v)))
+def test_rmsnorm_wide_two_pass(kcr, dt, d):
+    say(f"rmsnorm two-pass dt={dt} d={d}")
+    wl = workloads.rmsnorm_rows(rows=7, d=d, dtype=dt, seed=d)
+    y = kcr.rmsnorm(dev(wl["x"]), dev(wl["w"]), wl["eps"])
+    ref = oracle.rmsnorm(np_bits(wl["x"]), np_bits(wl["w"]), float(np.float32(wl["eps"])))
+    assert_close(y.cpu().double().numpy(), ref, dt, f"rmsnorm d={d}")
+
+
+@pytest.mark.parametrize("dt,d", [(torch.bfloat16, 40000), (torch.bfloat16, 100003),
+                                  (torch.float32, 20000), (torch.float32, 50001),
+                                  (torch.float16, 65543)], ids=lambda v: DT_ID.get(v, str(v)))
+def test_add_rmsnorm_wide_two_pass(kcr, dt, d):
+    say(f"add_rmsnorm two-pass dt={dt} d={d}")
+    wl = workloads.add_rmsnorm_rows(6, d, dtype=dt, seed=d)
+    x = dev(wl["x"])
+    y = kcr.add_rmsnorm(x, dev(wl["delta"]), dev(wl["w"]), wl["eps"])
+    xn, ref = oracle.add_rmsnorm(np_bits(wl["x"]), np_bits(wl["delta"]), np_bits(wl["w"]),
+                                 float(np.float32(wl["eps"])))
+    assert np.array_equal(np_bits(x).view(np.uint8), xn.view(np.uint8)), "residual not bit-exact"
+    assert_close(y.cpu().double().numpy(), ref, dt, f"add_rmsnorm d={d}")
+
+
+def test_rmsnorm_wide_in_place_strided(kcr):
+    say("rmsnorm two-pass, strided rows, in place")
+    wl = workloads.rmsnorm_rows(rows=5, d=90001, dtype="bf16", seed=5)
+    buf = torch.zeros((5, 90017), dtype=torch.bfloat16)
+    buf[:, :90001] = wl["x"]
+    xd = dev(buf)[:, :90001]
+    kcr.rmsnorm(xd, dev(wl["w"]), wl["eps"], out=xd)
+    ref = oracle.rmsnorm(np_bits(wl["x"]), np_bits(wl["w"]), float(np.float32(wl["eps"])))
+    assert_close(xd.cpu().double().numpy(), ref, torch.bfloat16, "in place")
+    assert bool((dev(buf)[:, 90001:] == 0).all())
+
+
+def test_rmsnorm_wide_row_loop(kcr):
+    # more rows than the two-pass grid (65536 workgroups): the row loop; the
+    # oracle checks sampled rows on both sides of the wrap
+    rows, d = 65536 + 37, 32776
+    say(f"rmsnorm two-pass row loop rows={rows} d={d}")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+    x = torch.randn((rows, d), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    w = torch.randn((d,), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    y = kcr.rmsnorm(x, w, 1e-6)
+    pick = torch.tensor([0, 1, 65535, 65536, 65537, rows - 1], device="cuda")
+    ref = oracle.rmsnorm(np_bits(x[pick].cpu()), np_bits(w.cpu()), float(np.float32(1e-6)))
+    assert_close(y[pick].cpu().double().numpy(), ref, torch.bfloat16, "sampled rows")
 
 
 @pytest.mark.parametrize("dt", DTS, ids=DT_ID.get)
