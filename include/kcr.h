@@ -15,10 +15,10 @@
  *    one call share that dtype; arithmetic is done in fp32 and every output
  *    element is rounded once (to nearest, ties to even) into the dtype.
  *  - Alignment: every pointer must be aligned to its element size
- *    (KCR_ERR_ALIGN otherwise). Rows whose base address is 16-byte aligned
- *    move with 16-byte vector loads and stores; other rows (for example the
- *    rows of a densely packed tensor whose width is not a multiple of 16
- *    bytes) are accessed element by element, correct but slower.
+ *    (KCR_ERR_ALIGN otherwise). Rows whose base address is 4-byte aligned
+ *    move with 16-byte vector loads and stores; other rows (a 2-byte dtype
+ *    at an odd element offset, e.g. the rows of a densely packed tensor of
+ *    odd width) are accessed element by element, correct but slower.
  *    kcr_rope_kvstore is stricter, see there.
  *  - Arguments are validated on the host before anything is launched; a
  *    negative return code means nothing was enqueued. A call with no work

@@ -13,7 +13,7 @@
 // head, vector), split by multiply-shift division; 64-lane workgroups, a
 // one-pass grid, nontemporal loads and stores. Per-channel parameters are
 // read as vectors (L1-resident), scalars as one element. A head row whose
-// base is not 16-byte aligned is accessed element by element.
+// base is not dword aligned is accessed element by element.
 #include "kcr_device.h"
 #include "kcr_host.h"
 
@@ -33,7 +33,10 @@ struct ClipArgs {
     int32_t alpha_pc, gamma_pc;
 };
 
-template <typename T>
+// APC / GPC: alpha / gamma per channel (else one scalar). VEC: every head
+// row of x and y starts on a dword boundary (checked on the host), so no
+// per-row alignment test is compiled in.
+template <typename T, bool APC, bool GPC, bool VEC>
 __global__ __launch_bounds__(64) void clip_norm_kernel(const ClipArgs a) {
     using S = typename T::storage;
     constexpr int kVec = T::kVec;
@@ -46,16 +49,16 @@ __global__ __launch_bounds__(64) void clip_norm_kernel(const ClipArgs a) {
     const S* xp = static_cast<const S*>(a.x) + (int64_t)t * a.x_ts + (int64_t)h * a.x_hs;
     S* yp = static_cast<S*>(a.y) + (int64_t)t * a.y_ts + (int64_t)h * a.y_hs;
     float xf[kVec], af[kVec], gf[kVec], yf[kVec];
-    unpack<T>(load_raw<T, true>(xp, col, a.d, aligned16(xp)), xf);
-    if (a.alpha_pc) {
-        unpack<T>(load_raw<T, false>(a.alpha, col, a.d, aligned16(a.alpha)), af);
+    unpack<T>(load_raw<T, true>(xp, col, a.d, VEC || vec_ok(xp)), xf);
+    if constexpr (APC) {
+        unpack<T>(load_raw<T, false>(a.alpha, col, a.d, VEC || vec_ok(a.alpha)), af);
     } else {
         const float s = load_one<T>(a.alpha, 0);
 #pragma unroll
         for (int e = 0; e < kVec; ++e) af[e] = s;
     }
-    if (a.gamma_pc) {
-        unpack<T>(load_raw<T, false>(a.gamma, col, a.d, aligned16(a.gamma)), gf);
+    if constexpr (GPC) {
+        unpack<T>(load_raw<T, false>(a.gamma, col, a.d, VEC || vec_ok(a.gamma)), gf);
     } else {
         const float s = load_one<T>(a.gamma, 0);
 #pragma unroll
@@ -63,7 +66,13 @@ __global__ __launch_bounds__(64) void clip_norm_kernel(const ClipArgs a) {
     }
 #pragma unroll
     for (int e = 0; e < kVec; ++e) yf[e] = fminf(fmaxf(af[e] * xf[e], a.lo), a.hi) * gf[e];
-    store_raw<T, true>(yp, col, a.d, pack<T>(yf), aligned16(yp));
+    store_raw<T, true>(yp, col, a.d, pack<T>(yf), VEC || vec_ok(yp));
+}
+
+template <typename T, bool APC, bool GPC>
+static int launch_clip(const ClipArgs& a, dim3 grid, void* stream, bool vec) {
+    return vec ? launch(clip_norm_kernel<T, APC, GPC, true>, grid, dim3(64), stream, a)
+               : launch(clip_norm_kernel<T, APC, GPC, false>, grid, dim3(64), stream, a);
 }
 
 }  // namespace kcr
@@ -98,7 +107,17 @@ extern "C" int kcr_clip_norm(const void* x, int64_t x_tok_stride, int64_t x_head
                total, make_fastdiv((uint32_t)vpr), make_fastdiv((uint32_t)n_head),
                alpha_per_channel ? 1 : 0, gamma_per_channel ? 1 : 0};
     const dim3 grid((total + 63) / 64);
+    auto rows_ok = [es](const void* p, int64_t ts, int64_t hs) {
+        return vec_ok(p) && (ts * (int64_t)es) % 4 == 0 && (hs * (int64_t)es) % 4 == 0;
+    };
+    const bool vec = rows_ok(x, x_tok_stride, x_head_stride) && rows_ok(y, y_tok_stride, y_head_stride) &&
+                     (!alpha_per_channel || vec_ok(alpha)) && (!gamma_per_channel || vec_ok(gamma));
     return by_dtype(dtype, [&](auto t) {
-        return launch(clip_norm_kernel<decltype(t)>, grid, dim3(64), stream, a);
+        using T = decltype(t);
+        if (alpha_per_channel)
+            return gamma_per_channel ? launch_clip<T, true, true>(a, grid, stream, vec)
+                                     : launch_clip<T, true, false>(a, grid, stream, vec);
+        return gamma_per_channel ? launch_clip<T, false, true>(a, grid, stream, vec)
+                                 : launch_clip<T, false, false>(a, grid, stream, vec);
     });
 }

@@ -9,6 +9,10 @@
 namespace kcr {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// The same 16 bytes at 4-byte alignment: global_load/store_dwordx4 need
+// only dword alignment, so rows that start 4 or 8 bytes past a 16-byte
+// boundary (e.g. 8196 bf16 elements per row) still move as whole vectors.
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -144,20 +148,21 @@ __device__ __forceinline__ void store_one<F32>(void* base, int64_t i, float v) {
 // 16-byte aligned whenever the base and the row stride are.
 template <typename T>
 __device__ __forceinline__ u32x4 ld16(const void* base, int64_t elem) {
-    return *reinterpret_cast<const u32x4*>(static_cast<const typename T::storage*>(base) + elem);
+    return *reinterpret_cast<const u32x4_a4*>(static_cast<const typename T::storage*>(base) + elem);
 }
 template <typename T>
 __device__ __forceinline__ u32x4 ld16_nt(const void* base, int64_t elem) {
     return __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4*>(static_cast<const typename T::storage*>(base) + elem));
+        reinterpret_cast<const u32x4_a4*>(static_cast<const typename T::storage*>(base) + elem));
 }
 template <typename T>
 __device__ __forceinline__ void st16(void* base, int64_t elem, const u32x4& v) {
-    *reinterpret_cast<u32x4*>(static_cast<typename T::storage*>(base) + elem) = v;
+    *reinterpret_cast<u32x4_a4*>(static_cast<typename T::storage*>(base) + elem) = v;
 }
 template <typename T>
 __device__ __forceinline__ void st16_nt(void* base, int64_t elem, const u32x4& v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(static_cast<typename T::storage*>(base) + elem));
+    const u32x4_a4 w = v;
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4_a4*>(static_cast<typename T::storage*>(base) + elem));
 }
 
 // Loads the vector that starts at element `elem` of a row of `n` elements:
@@ -189,12 +194,16 @@ __device__ __forceinline__ void store_vec(void* base, int64_t elem, int64_t n, c
 
 // Raw-bit variants: the vector starting at element `elem` of a row of `n`
 // elements, as it sits in memory. `vec` says whether the row's base address
-// is 16-byte aligned; when it is, every vector wholly inside the row moves
-// with one 16-byte access, and otherwise (and for the vector that straddles
-// the end of the row) element by element. Elements past the end of the row
+// is dword aligned (vec_ok); when it is, every vector wholly inside the row
+// moves with one 16-byte access, and otherwise (and for the vector that
+// straddles the end of the row) element by element. Elements past the end of the row
 // read as zero bits (+0.0 in every dtype) and are never written.
 __host__ __device__ __forceinline__ bool aligned16(const void* p) {
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+// Whether a row starting at `p` can move as 16-byte vectors (dword-aligned).
+__host__ __device__ __forceinline__ bool vec_ok(const void* p) {
+    return (reinterpret_cast<uintptr_t>(p) & 3u) == 0;
 }
 
 template <typename T, bool NT>

@@ -30,6 +30,10 @@ int run_norm(const NormArgs& a, void* stream);
 // of 64 lanes, 8 vectors per lane); wider rows take the two-pass kernel.
 constexpr int kRegMaxVec = 8 * 64 * 8;
 
+// Calls with at least this many rows may take a measured per-width shape
+// (norm_engine.h, launch_tuned) instead of norm_shape's.
+constexpr int64_t kTunedMinRows = 4096;
+
 // LDS bytes a workgroup may take on the current device.
 size_t lds_per_block();
 

@@ -12,17 +12,21 @@
 //    row, so each load instruction of a wave reads 1 KiB of consecutive
 //    bytes, and the row is read from HBM exactly once into registers (the
 //    one-pass form of the csdn "Qwen3 from scratch (4-2)" page).
-//  * WPR waves share a row (1..8, chosen per width, see norm_shape), with a
-//    two-slot LDS exchange of the wave partial sums when WPR > 1.
+//  * WPR waves share a row (1..8, chosen per width, see norm_shape), with an
+//    LDS exchange of the wave partial sums when WPR > 1. A row group may
+//    take RPG rows, all read before any is written: longer read-only then
+//    write-only phases per wave stream HBM better on MI355X.
 //  * The sum of squares is reduced in-wave with DPP and v_readlane (no LDS,
 //    no barrier when WPR = 1).
 //  * Ragged widths (1536, 2176, primes) need no power-of-two padding: only
 //    the vector that straddles the end of a row is read element by element.
-//    A row whose base is not 16-byte aligned (odd widths packed densely) is
-//    accessed element by element; the choice is uniform per row.
-//  * One-pass grid (a workgroup per GROUPS rows) with nontemporal loads and
-//    stores: on MI355X this streams HBM 10-20% faster than a persistent
-//    grid-stride loop; the weight is read once per workgroup (from L2).
+//    Vectors need only dword alignment, so rows of e.g. 8196 bf16 still move
+//    as 16-byte vectors; a row at an odd 2-byte offset (odd widths packed
+//    densely) is accessed element by element; the choice is uniform per row.
+//  * One-pass grid (a workgroup per GROUPS * RPG rows, no loop) with
+//    nontemporal loads and stores: on MI355X this streams HBM 10-20% faster
+//    than a persistent grid-stride loop; the weight is read once per
+//    workgroup (from L2).
 //  * Rows wider than the register-resident engine (4096 vectors) take the
 //    two-pass form of the Zhihu "RMSNorm in Triton" page (loop 1: sum of
 //    squares; loop 2: reload, scale, write), one 1024-lane workgroup per
@@ -45,107 +49,152 @@ __device__ __forceinline__ void* row_ptr(void* base, int64_t row, int64_t stride
 }
 
 // Launch shape of the row engine: VPT 16-byte vectors per lane, WPR waves
-// per row, GROUPS rows per workgroup, nontemporal loads (NTL) and stores
+// per row, GROUPS row groups per workgroup, RPG rows per row group (all RPG
+// rows are read before any is written), nontemporal loads (NTL) and stores
 // (NTS) for the streamed rows.
-template <int VPT_, int WPR_, int GROUPS_, bool NTL_, bool NTS_>
+template <int VPT_, int WPR_, int GROUPS_, bool NTL_, bool NTS_, int RPG_ = 1>
 struct NormCfg {
-    static constexpr int VPT = VPT_, WPR = WPR_, GROUPS = GROUPS_;
+    static constexpr int VPT = VPT_, WPR = WPR_, GROUPS = GROUPS_, RPG = RPG_;
     static constexpr bool NTL = NTL_, NTS = NTS_;
     static constexpr int BLOCK = 64 * WPR * GROUPS;
 };
 
-template <typename T, typename C, bool ADD>
+// VEC: the host has checked that every row base (x, delta, y, w) is dword
+// aligned, so the kernel carries no per-row alignment test (measured 3-4%
+// faster than testing each row at run time).
+template <typename T, typename C, bool ADD, bool VEC>
 __global__ __launch_bounds__(C::BLOCK) void row_norm_kernel(const NormArgs a) {
-    constexpr int kVec = T::kVec, VPT = C::VPT, WPR = C::WPR, GROUPS = C::GROUPS;
+    constexpr int kVec = T::kVec, VPT = C::VPT, WPR = C::WPR, GROUPS = C::GROUPS, RPG = C::RPG;
     constexpr int LANES = 64 * WPR;
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
     const int grp = wave / WPR;                    // row group within the workgroup
     const int rl = (wave % WPR) * 64 + lane;       // lane within the row group
     const int64_t d = a.d;
+    // One pass: workgroup b owns rows [b * GROUPS * RPG, (b + 1) * GROUPS * RPG).
+    // (A loop over several row blocks per workgroup measured 2-5% slower: the
+    // compiler then waits for the weight before the first row load.)
+    const int64_t row0 = ((int64_t)blockIdx.x * GROUPS + grp) * RPG;
 
-    // The weight, once per workgroup, in registers.
-    const bool vw = aligned16(a.w);
+    // The weight, once per workgroup (an L2 hit), in registers.
+    const bool vw = VEC || vec_ok(a.w);
     u32x4 wr[VPT];
 #pragma unroll
     for (int j = 0; j < VPT; ++j) wr[j] = load_raw<T, false>(a.w, (int64_t)(j * LANES + rl) * kVec, d, vw);
 
-    __shared__ float part[2][GROUPS][WPR];
-    int it = 0;
-    // The loop bound depends only on the workgroup, so every wave reaches
-    // every barrier; `live` is uniform per row group.
-    for (int64_t base = (int64_t)blockIdx.x * GROUPS; base < a.rows;
-         base += (int64_t)gridDim.x * GROUPS, ++it) {
-        const int64_t row = base + grp;
-        const bool live = row < a.rows;
-        u32x4 xr[VPT];
-        float ss = 0.0f;
-        bool vx = false;
-        if (live) {
-            const void* xrow = row_ptr<T>(a.x, row, a.x_stride);
-            vx = aligned16(xrow);  // row-uniform: vector or element access
+    // All RPG rows are read before any is written. `live[r]` is uniform per
+    // row group; every wave reaches the barrier.
+    u32x4 xr[RPG][VPT];
+    float ss[RPG];
+    bool live[RPG], vx[RPG];
+#pragma unroll
+    for (int r = 0; r < RPG; ++r) {
+        live[r] = row0 + r < a.rows;
+        ss[r] = 0.0f;
+        vx[r] = false;
+        if (live[r]) {
+            const void* xrow = row_ptr<T>(a.x, row0 + r, a.x_stride);
+            vx[r] = VEC || vec_ok(xrow);  // row-uniform: vector or element access
 #pragma unroll
             for (int j = 0; j < VPT; ++j)
-                xr[j] = load_raw<T, C::NTL>(xrow, (int64_t)(j * LANES + rl) * kVec, d, vx);
-            if constexpr (ADD) {
-                const void* drow = row_ptr<T>(a.delta, row, a.delta_stride);
-                const bool vd = aligned16(drow);
-                u32x4 dr[VPT];
+                xr[r][j] = load_raw<T, C::NTL>(xrow, (int64_t)(j * LANES + rl) * kVec, d, vx[r]);
+        }
+    }
+    if constexpr (ADD) {
+        u32x4 dr[RPG][VPT];
 #pragma unroll
-                for (int j = 0; j < VPT; ++j)
-                    dr[j] = load_raw<T, C::NTL>(drow, (int64_t)(j * LANES + rl) * kVec, d, vd);
-                void* orow = row_ptr<T>(a.x_out, row, a.x_stride);
+        for (int r = 0; r < RPG; ++r) {
+            if (!live[r]) continue;
+            const void* drow = row_ptr<T>(a.delta, row0 + r, a.delta_stride);
+            const bool vd = VEC || vec_ok(drow);
 #pragma unroll
-                for (int j = 0; j < VPT; ++j) {
-                    float xf[kVec], df[kVec];
-                    unpack<T>(xr[j], xf);
-                    unpack<T>(dr[j], df);
+            for (int j = 0; j < VPT; ++j)
+                dr[r][j] = load_raw<T, C::NTL>(drow, (int64_t)(j * LANES + rl) * kVec, d, vd);
+        }
 #pragma unroll
-                    for (int e = 0; e < kVec; ++e) xf[e] += df[e];
-                    xr[j] = pack<T>(xf);  // the rounded sum: stored, and normalised below
-                    store_raw<T, C::NTS>(orow, (int64_t)(j * LANES + rl) * kVec, d, xr[j], vx);
-                }
+        for (int r = 0; r < RPG; ++r) {
+            if (!live[r]) continue;
+            void* orow = row_ptr<T>(a.x_out, row0 + r, a.x_stride);
+#pragma unroll
+            for (int j = 0; j < VPT; ++j) {
+                float xf[kVec], df[kVec];
+                unpack<T>(xr[r][j], xf);
+                unpack<T>(dr[r][j], df);
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) xf[e] += df[e];
+                xr[r][j] = pack<T>(xf);  // the rounded sum: stored, and normalised below
+                store_raw<T, C::NTS>(orow, (int64_t)(j * LANES + rl) * kVec, d, xr[r][j], vx[r]);
             }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < RPG; ++r) {
+        if (live[r]) {
 #pragma unroll
             for (int j = 0; j < VPT; ++j) {
                 float xf[kVec];
-                unpack<T>(xr[j], xf);
+                unpack<T>(xr[r][j], xf);
 #pragma unroll
-                for (int e = 0; e < kVec; ++e) ss += xf[e] * xf[e];
+                for (int e = 0; e < kVec; ++e) ss[r] += xf[e] * xf[e];
             }
         }
-        ss = wave_sum(ss);
-        if constexpr (WPR > 1) {
-            float* slot = part[it & 1][grp];
-            if (lane == 0) slot[wave % WPR] = ss;
-            __syncthreads();
-            ss = 0.0f;
+        ss[r] = wave_sum(ss[r]);
+    }
+    if constexpr (WPR > 1) {
+        __shared__ float part[RPG][GROUPS][WPR];
+        if (lane == 0) {
 #pragma unroll
-            for (int i = 0; i < WPR; ++i) ss += slot[i];
+            for (int r = 0; r < RPG; ++r) part[r][grp][wave % WPR] = ss[r];
         }
-        if (live) {
-            const float r = __builtin_amdgcn_rsqf(ss / (float)a.d + a.eps);
-            void* yrow = row_ptr<T>(a.y, row, a.y_stride);
-            const bool vy = aligned16(yrow);
+        __syncthreads();
 #pragma unroll
-            for (int j = 0; j < VPT; ++j) {
-                float xf[kVec], wf[kVec], yf[kVec];
-                unpack<T>(xr[j], xf);
-                unpack<T>(wr[j], wf);
+        for (int r = 0; r < RPG; ++r) {
+            ss[r] = 0.0f;
 #pragma unroll
-                for (int e = 0; e < kVec; ++e) yf[e] = xf[e] * r * wf[e];
-                store_raw<T, C::NTS>(yrow, (int64_t)(j * LANES + rl) * kVec, d, pack<T>(yf), vy);
-            }
+            for (int i = 0; i < WPR; ++i) ss[r] += part[r][grp][i];
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < RPG; ++r) {
+        if (!live[r]) continue;
+        const float rs = __builtin_amdgcn_rsqf(ss[r] / (float)a.d + a.eps);
+        void* yrow = row_ptr<T>(a.y, row0 + r, a.y_stride);
+        const bool vy = VEC || vec_ok(yrow);
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            float xf[kVec], wf[kVec], yf[kVec];
+            unpack<T>(xr[r][j], xf);
+            unpack<T>(wr[j], wf);
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) yf[e] = xf[e] * rs * wf[e];
+            store_raw<T, C::NTS>(yrow, (int64_t)(j * LANES + rl) * kVec, d, pack<T>(yf), vy);
         }
     }
 }
 
-// Launches with a grid of ceil(rows / GROUPS) workgroups, capped at
-// `wgs_per_cu` resident rounds per CU (a large cap gives a one-pass grid).
-template <typename T, typename C, bool ADD>
-static int launch_norm(const NormArgs& a, void* stream, int wgs_per_cu) {
-    const dim3 grid(grid_for(a.rows, C::GROUPS, device_cus(), wgs_per_cu));
-    return launch(row_norm_kernel<T, C, ADD>, grid, dim3(C::BLOCK), stream, a);
+// Launches ceil(rows / (GROUPS * RPG)) workgroups. A grid holds at most
+// 2^32 - 1 work-items, so a call with more rows than that covers is split
+// into several launches over consecutive row ranges.
+template <typename T, typename C, bool ADD, bool VEC = true>
+static int launch_norm(const NormArgs& a, void* stream) {
+    constexpr int64_t kRowsPerWg = (int64_t)C::GROUPS * C::RPG;
+    constexpr int64_t kMaxWgs = (int64_t)0xFFFFFFFFu / C::BLOCK;
+    constexpr int64_t es = sizeof(typename T::storage);
+    const int64_t per_launch = kMaxWgs * kRowsPerWg;
+    for (int64_t off = 0; off < a.rows; off += per_launch) {
+        NormArgs c = a;
+        c.rows = a.rows - off < per_launch ? a.rows - off : per_launch;
+        c.x = static_cast<const char*>(a.x) + off * a.x_stride * es;
+        c.y = static_cast<char*>(a.y) + off * a.y_stride * es;
+        if (ADD) {
+            c.x_out = static_cast<char*>(a.x_out) + off * a.x_stride * es;
+            c.delta = static_cast<const char*>(a.delta) + off * a.delta_stride * es;
+        }
+        const dim3 grid((uint32_t)((c.rows + kRowsPerWg - 1) / kRowsPerWg));
+        const int rc = launch(row_norm_kernel<T, C, ADD, VEC>, grid, dim3(C::BLOCK), stream, c);
+        if (rc != KCR_OK) return rc;
+    }
+    return KCR_OK;
 }
 
 // ------------------------------------------------------------ wide rows
@@ -167,13 +216,13 @@ __global__ __launch_bounds__(kWideThreads) void wide_norm_kernel(const NormArgs 
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int64_t d = a.d;
     const int nvec = (a.d + kVec - 1) / kVec;
-    const bool vw = aligned16(a.w);
+    const bool vw = vec_ok(a.w);
     int it = 0;
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x, ++it) {
         const void* xrow = row_ptr<T>(a.x, row, a.x_stride);
-        const bool vx = aligned16(xrow);
+        const bool vx = vec_ok(xrow);
         const void* drow = ADD ? row_ptr<T>(a.delta, row, a.delta_stride) : nullptr;
-        const bool vd = ADD && aligned16(drow);
+        const bool vd = ADD && vec_ok(drow);
         void* orow = ADD ? row_ptr<T>(a.x_out, row, a.x_stride) : nullptr;
         float ss = 0.0f;
         for (int v0 = tid; v0 < nvec; v0 += kWideThreads * kWideUnroll) {
@@ -226,7 +275,7 @@ __global__ __launch_bounds__(kWideThreads) void wide_norm_kernel(const NormArgs 
 
         const void* src = ADD ? static_cast<const void*>(orow) : xrow;
         void* yrow = row_ptr<T>(a.y, row, a.y_stride);
-        const bool vy = aligned16(yrow);
+        const bool vy = vec_ok(yrow);
         for (int v = tid; v < nvec; v += kWideThreads) {
             const u32x4 xv = STAGED ? stage[v] : load_raw<T, false>(src, (int64_t)v * kVec, d, vx);
             const u32x4 wv = load_raw<T, false>(a.w, (int64_t)v * kVec, d, vw);
@@ -262,10 +311,9 @@ static int launch_wide(const NormArgs& a, void* stream) {
 // ------------------------------------------------------------ dispatch
 template <typename T, bool ADD, int VPT, int WPR>
 static int launch_g(const NormArgs& a, void* stream, int groups) {
-    constexpr int kOnePass = 1 << 20;  // grid cap per CU: effectively one pass
-    if (groups == 4) return launch_norm<T, NormCfg<VPT, WPR, 4, true, true>, ADD>(a, stream, kOnePass);
-    if (groups == 2) return launch_norm<T, NormCfg<VPT, WPR, 2, true, true>, ADD>(a, stream, kOnePass);
-    return launch_norm<T, NormCfg<VPT, WPR, 1, true, true>, ADD>(a, stream, kOnePass);
+    if (groups == 4) return launch_norm<T, NormCfg<VPT, WPR, 4, true, true>, ADD>(a, stream);
+    if (groups == 2) return launch_norm<T, NormCfg<VPT, WPR, 2, true, true>, ADD>(a, stream);
+    return launch_norm<T, NormCfg<VPT, WPR, 1, true, true>, ADD>(a, stream);
 }
 
 template <typename T, bool ADD, int WPR>
@@ -283,9 +331,75 @@ static int launch_w(const NormArgs& a, void* stream, int vpt, int groups) {
     return KCR_ERR_SHAPE;
 }
 
+// Shapes measured best for plain rows at common model widths on MI355X
+// (about 570 MB per call, four repeats each), 2.5-5% above the rule's shape
+// there; other widths, small calls and the add variant take the rule.
+template <typename T>
+static int launch_tuned(const NormArgs& a, void* stream) {
+    if constexpr (T::kVec == 8) {
+        switch (a.d) {
+            case 1536: return launch_norm<T, NormCfg<1, 3, 2, true, true, 2>, false>(a, stream);
+            case 2048: return launch_norm<T, NormCfg<3, 2, 1, true, true, 1>, false>(a, stream);
+            case 2176: return launch_norm<T, NormCfg<3, 2, 2, true, true, 2>, false>(a, stream);
+            case 4096: return launch_norm<T, NormCfg<1, 8, 1, true, true, 2>, false>(a, stream);
+            case 5120: return launch_norm<T, NormCfg<4, 3, 2, true, true, 1>, false>(a, stream);
+        }
+    } else {
+        if (a.d == 1024) return launch_norm<T, NormCfg<1, 4, 1, true, true, 1>, false>(a, stream);
+    }
+    return 1;  // not in the table
+}
+
+// Whether every row of the call starts on a dword boundary (base pointers
+// and strides in bytes); always true for fp32.
+template <typename T, bool ADD>
+static bool rows_dword_aligned(const NormArgs& a) {
+    constexpr int64_t es = sizeof(typename T::storage);
+    auto ok = [](const void* p, int64_t stride) { return vec_ok(p) && (stride * es) % 4 == 0; };
+    return ok(a.x, a.x_stride) && ok(a.y, a.y_stride) && vec_ok(a.w) &&
+           (!ADD || ok(a.delta, a.delta_stride));
+}
+
+// Calls with rows at odd 2-byte offsets (element access for those rows): a
+// small fixed family of shapes that test each row's alignment at run time.
+template <typename T, bool ADD>
+static int launch_unaligned(const NormArgs& a, void* stream) {
+    const int64_t nvec = (a.d + T::kVec - 1) / T::kVec;
+    if (nvec <= 8 * 64) {
+        switch ((nvec + 63) / 64) {
+            case 1: return launch_norm<T, NormCfg<1, 1, 2, true, true>, ADD, false>(a, stream);
+            case 2: return launch_norm<T, NormCfg<2, 1, 2, true, true>, ADD, false>(a, stream);
+            case 3: return launch_norm<T, NormCfg<3, 1, 2, true, true>, ADD, false>(a, stream);
+            case 4: return launch_norm<T, NormCfg<4, 1, 2, true, true>, ADD, false>(a, stream);
+            case 5: return launch_norm<T, NormCfg<5, 1, 2, true, true>, ADD, false>(a, stream);
+            case 6: return launch_norm<T, NormCfg<6, 1, 2, true, true>, ADD, false>(a, stream);
+            case 7: return launch_norm<T, NormCfg<7, 1, 2, true, true>, ADD, false>(a, stream);
+            case 8: return launch_norm<T, NormCfg<8, 1, 2, true, true>, ADD, false>(a, stream);
+        }
+    }
+    switch ((nvec + 511) / 512) {
+        case 1: return launch_norm<T, NormCfg<1, 8, 1, true, true>, ADD, false>(a, stream);
+        case 2: return launch_norm<T, NormCfg<2, 8, 1, true, true>, ADD, false>(a, stream);
+        case 3: return launch_norm<T, NormCfg<3, 8, 1, true, true>, ADD, false>(a, stream);
+        case 4: return launch_norm<T, NormCfg<4, 8, 1, true, true>, ADD, false>(a, stream);
+        case 5: return launch_norm<T, NormCfg<5, 8, 1, true, true>, ADD, false>(a, stream);
+        case 6: return launch_norm<T, NormCfg<6, 8, 1, true, true>, ADD, false>(a, stream);
+        case 7: return launch_norm<T, NormCfg<7, 8, 1, true, true>, ADD, false>(a, stream);
+        case 8: return launch_norm<T, NormCfg<8, 8, 1, true, true>, ADD, false>(a, stream);
+    }
+    return KCR_ERR_SHAPE;
+}
+
 template <typename T, bool ADD>
 int run_norm(const NormArgs& a, void* stream) {
     if ((a.d + T::kVec - 1) / T::kVec > kRegMaxVec) return launch_wide<T, ADD>(a, stream);
+    if constexpr (sizeof(typename T::storage) < 4) {
+        if (!rows_dword_aligned<T, ADD>(a)) return launch_unaligned<T, ADD>(a, stream);
+    }
+    if (!ADD && a.rows >= kTunedMinRows) {
+        const int rc = launch_tuned<T>(a, stream);
+        if (rc <= 0) return rc;
+    }
     const NormShape s = norm_shape((a.d + T::kVec - 1) / T::kVec, ADD);
     switch (s.wpr) {
         case 1: return launch_w<T, ADD, 1>(a, stream, s.vpt, s.groups);

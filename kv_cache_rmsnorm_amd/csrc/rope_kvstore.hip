@@ -82,7 +82,11 @@ __global__ __launch_bounds__(256) void rope_kvstore_kernel(const RopeArgs a) {
     const bool lane_on = c * kVec < half;
     if (!QKN && !lane_on) return;
     const int64_t c0 = lane_on ? (int64_t)c * kVec : 0;
-    for (uint32_t u = blockIdx.x * UPW + threadIdx.x / LPU; u < a.units; u += gridDim.x * UPW) {
+    // One pass, no loop: unit u of the grid (a loop over several units per
+    // lane measured slower on the row kernels).
+    const uint32_t u = blockIdx.x * UPW + threadIdx.x / LPU;
+    if (u >= a.units) return;  // all lanes of a unit leave together
+    {
         const uint32_t t = fastdiv(u, a.upt);
         const int j0 = (int)(u - t * a.upt.d) * HPU;
         // Position and slot first, then every head of the unit: the head
@@ -194,27 +198,43 @@ __global__ __launch_bounds__(256) void rope_kvstore_kernel(const RopeArgs a) {
     }
 }
 
+// One workgroup per UPW units. A grid holds at most 2^32 - 1 work-items, so
+// a call with more tokens than that covers is split into launches over
+// consecutive token ranges (q, k, v, q_out, positions and slots offset).
 template <typename T, typename C, bool QKN>
-static int launch_rope(RopeArgs a, int64_t T_tokens, void* stream, int wgs_per_cu) {
+static int launch_rope(RopeArgs a, int64_t T_tokens, void* stream) {
+    using S = typename T::storage;
     constexpr int UPW = 256 / C::LPU;
-    const int upt = (a.nvh + C::HPU - 1) / C::HPU;
+    const int64_t upt = (a.nvh + C::HPU - 1) / C::HPU;
     a.upt = make_fastdiv((uint32_t)upt);
-    a.units = (uint32_t)(T_tokens * upt);
-    const dim3 grid(grid_for(a.units, UPW, device_cus(), wgs_per_cu));
-    return launch(rope_kvstore_kernel<T, C, QKN>, grid, dim3(256), stream, a);
+    const int64_t max_tokens = ((int64_t)0xFFFFFFFFu / 256) * UPW / upt;
+    for (int64_t t0 = 0; t0 < T_tokens; t0 += max_tokens) {
+        RopeArgs c = a;
+        const int64_t n = T_tokens - t0 < max_tokens ? T_tokens - t0 : max_tokens;
+        c.q = static_cast<const S*>(a.q) + t0 * a.q_ts;
+        c.k = static_cast<const S*>(a.k) + t0 * a.k_ts;
+        c.v = static_cast<const S*>(a.v) + t0 * a.v_ts;
+        c.q_out = static_cast<S*>(a.q_out) + t0 * (int64_t)a.hq * a.dh;
+        c.pos = a.pos + t0;
+        c.slots = a.slots + t0;
+        c.units = (uint32_t)(n * upt);
+        const dim3 grid((uint32_t)((c.units + UPW - 1) / UPW));
+        const int rc = launch(rope_kvstore_kernel<T, C, QKN>, grid, dim3(256), stream, c);
+        if (rc != KCR_OK) return rc;
+    }
+    return KCR_OK;
 }
 
 template <typename T, int HPU, bool QKN>
 static int dispatch_rope_lpu(const RopeArgs& a, int64_t T_tokens, void* stream) {
-    constexpr int kOnePass = 1 << 20;
     const int chunks = (a.dh / 2) / T::kVec;
-    if (chunks <= 1) return launch_rope<T, RopeCfg<1, HPU, true, true>, QKN>(a, T_tokens, stream, kOnePass);
-    if (chunks <= 2) return launch_rope<T, RopeCfg<2, HPU, true, true>, QKN>(a, T_tokens, stream, kOnePass);
-    if (chunks <= 4) return launch_rope<T, RopeCfg<4, HPU, true, true>, QKN>(a, T_tokens, stream, kOnePass);
-    if (chunks <= 8) return launch_rope<T, RopeCfg<8, HPU, true, true>, QKN>(a, T_tokens, stream, kOnePass);
-    if (chunks <= 16) return launch_rope<T, RopeCfg<16, HPU, true, true>, QKN>(a, T_tokens, stream, kOnePass);
-    if (chunks <= 32) return launch_rope<T, RopeCfg<32, HPU, true, true>, QKN>(a, T_tokens, stream, kOnePass);
-    if (chunks <= 64) return launch_rope<T, RopeCfg<64, HPU, true, true>, QKN>(a, T_tokens, stream, kOnePass);
+    if (chunks <= 1) return launch_rope<T, RopeCfg<1, HPU, true, true>, QKN>(a, T_tokens, stream);
+    if (chunks <= 2) return launch_rope<T, RopeCfg<2, HPU, true, true>, QKN>(a, T_tokens, stream);
+    if (chunks <= 4) return launch_rope<T, RopeCfg<4, HPU, true, true>, QKN>(a, T_tokens, stream);
+    if (chunks <= 8) return launch_rope<T, RopeCfg<8, HPU, true, true>, QKN>(a, T_tokens, stream);
+    if (chunks <= 16) return launch_rope<T, RopeCfg<16, HPU, true, true>, QKN>(a, T_tokens, stream);
+    if (chunks <= 32) return launch_rope<T, RopeCfg<32, HPU, true, true>, QKN>(a, T_tokens, stream);
+    if (chunks <= 64) return launch_rope<T, RopeCfg<64, HPU, true, true>, QKN>(a, T_tokens, stream);
     return KCR_ERR_SHAPE;
 }
 

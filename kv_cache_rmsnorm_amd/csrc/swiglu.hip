@@ -8,11 +8,12 @@
 //
 // gfx950 design
 //  * The index space is rows x ceil(cols / kVec) 16-byte vectors, flattened;
-//    thread i of a workgroup takes vectors base + i, base + 256 + i, ... so
-//    every wave instruction moves 1 KiB of consecutive bytes. The (row,
-//    vector) split uses a precomputed multiply-shift division, so strided
-//    gate/up halves of a fused gate_up buffer need no copy. Rows whose base
-//    is not 16-byte aligned are accessed element by element.
+//    consecutive lanes take consecutive vectors, so every wave instruction
+//    moves 1 KiB of consecutive bytes. The (row, vector) split uses a
+//    precomputed multiply-shift division, so strided gate/up halves of a
+//    fused gate_up buffer need no copy. Rows whose base is not dword
+//    aligned are accessed element by element (a kernel variant that the
+//    host picks only when some row needs it).
 //  * One vector of gate and of up per lane, 64-lane workgroups, a one-pass
 //    grid and nontemporal loads and stores: on MI355X many small waves
 //    stream HBM faster than fewer waves with more loads each.
@@ -53,46 +54,49 @@ struct SwigluCfg {
     static constexpr bool NTL = NTL_, NTS = NTS_;
 };
 
-template <typename T, typename C, typename Act>
+// One pass, no loop: thread i of workgroup b takes vectors
+// b * BLOCK * UNROLL + k * BLOCK + i. VEC: the host has checked that every
+// row base of gate, up and out is dword aligned, so no per-row alignment
+// test is compiled in.
+template <typename T, typename C, typename Act, bool VEC>
 __global__ __launch_bounds__(C::BLOCK) void swiglu_kernel(const SwigluArgs a) {
     using S = typename T::storage;
     constexpr int kVec = T::kVec, B = C::BLOCK, U = C::UNROLL;
-    const uint32_t step = gridDim.x * (uint32_t)(B * U);
-    for (uint32_t base = blockIdx.x * (uint32_t)(B * U) + threadIdx.x; base < a.total; base += step) {
-        u32x4 gr[U], ur[U];
-        int64_t row[U], col[U];
+    const uint32_t base = blockIdx.x * (uint32_t)(B * U) + threadIdx.x;
+    u32x4 gr[U], ur[U];
+    int64_t row[U], col[U];
 #pragma unroll
-        for (int k = 0; k < U; ++k) {
-            const uint32_t idx = base + k * (uint32_t)B;
-            if (idx < a.total) {
-                const uint32_t r = fastdiv(idx, a.vpr);
-                row[k] = r;
-                col[k] = (int64_t)(idx - r * a.vpr.d) * kVec;
-                const S* gp = static_cast<const S*>(a.g) + row[k] * a.g_stride;
-                const S* up = static_cast<const S*>(a.u) + row[k] * a.u_stride;
-                gr[k] = load_raw<T, C::NTL>(gp, col[k], a.cols, aligned16(gp));
-                ur[k] = load_raw<T, C::NTL>(up, col[k], a.cols, aligned16(up));
-            }
+    for (int k = 0; k < U; ++k) {
+        const uint32_t idx = base + k * (uint32_t)B;
+        if (idx < a.total) {
+            const uint32_t r = fastdiv(idx, a.vpr);
+            row[k] = r;
+            col[k] = (int64_t)(idx - r * a.vpr.d) * kVec;
+            const S* gp = static_cast<const S*>(a.g) + row[k] * a.g_stride;
+            const S* up = static_cast<const S*>(a.u) + row[k] * a.u_stride;
+            gr[k] = load_raw<T, C::NTL>(gp, col[k], a.cols, VEC || vec_ok(gp));
+            ur[k] = load_raw<T, C::NTL>(up, col[k], a.cols, VEC || vec_ok(up));
         }
+    }
 #pragma unroll
-        for (int k = 0; k < U; ++k) {
-            if (base + k * (uint32_t)B < a.total) {
-                float gf[kVec], uf[kVec], of[kVec];
-                unpack<T>(gr[k], gf);
-                unpack<T>(ur[k], uf);
+    for (int k = 0; k < U; ++k) {
+        if (base + k * (uint32_t)B < a.total) {
+            float gf[kVec], uf[kVec], of[kVec];
+            unpack<T>(gr[k], gf);
+            unpack<T>(ur[k], uf);
 #pragma unroll
-                for (int e = 0; e < kVec; ++e) of[e] = Act::apply(gf[e], uf[e]);
-                S* op = static_cast<S*>(a.out) + row[k] * a.out_stride;
-                store_raw<T, C::NTS>(op, col[k], a.cols, pack<T>(of), aligned16(op));
-            }
+            for (int e = 0; e < kVec; ++e) of[e] = Act::apply(gf[e], uf[e]);
+            S* op = static_cast<S*>(a.out) + row[k] * a.out_stride;
+            store_raw<T, C::NTS>(op, col[k], a.cols, pack<T>(of), VEC || vec_ok(op));
         }
     }
 }
 
 template <typename T, typename C, typename Act>
-static int launch_swiglu(const SwigluArgs& a, void* stream, int wgs_per_cu) {
-    const dim3 grid(grid_for(a.total, C::BLOCK * C::UNROLL, device_cus(), wgs_per_cu));
-    return launch(swiglu_kernel<T, C, Act>, grid, dim3(C::BLOCK), stream, a);
+static int launch_swiglu(const SwigluArgs& a, void* stream, bool vec) {
+    const dim3 grid((uint32_t)(((int64_t)a.total + C::BLOCK * C::UNROLL - 1) / (C::BLOCK * C::UNROLL)));
+    return vec ? launch(swiglu_kernel<T, C, Act, true>, grid, dim3(C::BLOCK), stream, a)
+               : launch(swiglu_kernel<T, C, Act, false>, grid, dim3(C::BLOCK), stream, a);
 }
 
 // Shared argument checks of the gated activations.
@@ -128,7 +132,6 @@ static int gated_prepare(const void* gate, int64_t gate_stride, const void* up, 
 // 64-lane workgroups, one vector of each stream per lane, one-pass grid,
 // nontemporal loads and stores: the fastest shape in sweeps on MI355X.
 using GatedCfg = SwigluCfg<64, 1, true, true>;
-constexpr int kOnePass = 1 << 20;
 
 template <typename Act>
 static int run_gated(const void* gate, int64_t gate_stride, const void* up, int64_t up_stride,
@@ -139,9 +142,10 @@ static int run_gated(const void* gate, int64_t gate_stride, const void* up, int6
     const int rc = gated_prepare(gate, gate_stride, up, up_stride, out, out_stride, rows, cols, dtype,
                                  &a, &work);
     if (rc != KCR_OK || !work) return rc;
-    return by_dtype(dtype, [&](auto t) {
-        return launch_swiglu<decltype(t), GatedCfg, Act>(a, stream, kOnePass);
-    });
+    const size_t es = dtype_size(dtype);
+    auto rows_ok = [es](const void* p, int64_t stride) { return vec_ok(p) && (stride * (int64_t)es) % 4 == 0; };
+    const bool vec = rows_ok(gate, gate_stride) && rows_ok(up, up_stride) && rows_ok(out, out_stride);
+    return by_dtype(dtype, [&](auto t) { return launch_swiglu<decltype(t), GatedCfg, Act>(a, stream, vec); });
 }
 
 }  // namespace kcr

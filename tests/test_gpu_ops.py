@@ -37,8 +37,11 @@ def say(*a):
 
 
 # ------------------------------------------------------------------ RMSNorm
-NORM_WIDTHS = [1, 7, 8, 9, 63, 64, 65, 127, 511, 512, 513, 1000, 1536, 2048, 2176, 3001, 4095,
-               4096, 4097, 8191, 8192, 8193, 12289, 16384]
+# 1538, 2180 and 8196 put 2-byte rows 4 or 8 bytes past a 16-byte boundary
+# (dword-aligned vectors); odd widths alternate with 2-byte offsets (element
+# access).
+NORM_WIDTHS = [1, 7, 8, 9, 63, 64, 65, 127, 511, 512, 513, 1000, 1536, 1538, 2048, 2176, 2180, 3001,
+               4095, 4096, 4097, 8191, 8192, 8193, 8196, 12289, 16384]
 
 
 @pytest.mark.parametrize("dt", DTS, ids=DT_ID.get)
@@ -117,6 +120,36 @@ def test_rmsnorm_wide_row_loop(kcr):
     pick = torch.tensor([0, 1, 65535, 65536, 65537, rows - 1], device="cuda")
     ref = oracle.rmsnorm(np_bits(x[pick].cpu()), np_bits(w.cpu()), float(np.float32(1e-6)))
     assert_close(y[pick].cpu().double().numpy(), ref, torch.bfloat16, "sampled rows")
+
+
+# Widths with a measured launch shape of their own when a call has at least
+# 4096 rows (some read two rows per row group before writing either); 4099
+# rows leave the last group half empty.
+TUNED = [(torch.bfloat16, 1536), (torch.bfloat16, 2048), (torch.bfloat16, 2176),
+         (torch.bfloat16, 4096), (torch.bfloat16, 5120), (torch.float16, 2176),
+         (torch.float16, 4096), (torch.float32, 1024)]
+
+
+@pytest.mark.parametrize("dt,d", TUNED, ids=lambda v: DT_ID.get(v, str(v)))
+def test_rmsnorm_tuned_widths(kcr, dt, d):
+    rows = 4099
+    say(f"rmsnorm tuned shape dt={dt} d={d} rows={rows}")
+    wl = workloads.rmsnorm_rows(rows=rows, d=d, dtype=dt, seed=d + 1)
+    y = kcr.rmsnorm(dev(wl["x"]), dev(wl["w"]), wl["eps"])
+    ref = oracle.rmsnorm(np_bits(wl["x"]), np_bits(wl["w"]), float(np.float32(wl["eps"])))
+    assert_close(y.cpu().double().numpy(), ref, dt, f"rmsnorm d={d}")
+
+
+def test_rmsnorm_tuned_in_place_strided(kcr):
+    rows, d = 4097, 2176
+    say(f"rmsnorm tuned shape, strided rows in place, rows={rows}")
+    wl = workloads.rmsnorm_rows(rows=rows, d=d, dtype="bf16", seed=3)
+    buf = torch.zeros((rows, d + 24), dtype=torch.bfloat16)
+    buf[:, :d] = wl["x"]
+    xd = dev(buf)[:, :d]
+    kcr.rmsnorm(xd, dev(wl["w"]), wl["eps"], out=xd)
+    ref = oracle.rmsnorm(np_bits(wl["x"]), np_bits(wl["w"]), float(np.float32(wl["eps"])))
+    assert_close(xd.cpu().double().numpy(), ref, torch.bfloat16, "in place")
 
 
 @pytest.mark.parametrize("dt", DTS, ids=DT_ID.get)
