@@ -34,6 +34,10 @@ constexpr int kRegMaxVec = 8 * 64 * 8;
 // (norm_engine.h, launch_tuned) instead of norm_shape's.
 constexpr int64_t kTunedMinRows = 4096;
 
+// Calls that stream at most this many bytes take one row group per
+// workgroup (norm_engine.h, launch_small).
+constexpr int64_t kNormSmallCallBytes = 32ll << 20;
+
 // LDS bytes a workgroup may take on the current device.
 size_t lds_per_block();
 

@@ -225,28 +225,31 @@ static int launch_rope(RopeArgs a, int64_t T_tokens, void* stream) {
     return KCR_OK;
 }
 
-template <typename T, int HPU, bool QKN>
+template <typename T, int HPU, bool QKN, bool NTS>
 static int dispatch_rope_lpu(const RopeArgs& a, int64_t T_tokens, void* stream) {
     const int chunks = (a.dh / 2) / T::kVec;
-    if (chunks <= 1) return launch_rope<T, RopeCfg<1, HPU, true, true>, QKN>(a, T_tokens, stream);
-    if (chunks <= 2) return launch_rope<T, RopeCfg<2, HPU, true, true>, QKN>(a, T_tokens, stream);
-    if (chunks <= 4) return launch_rope<T, RopeCfg<4, HPU, true, true>, QKN>(a, T_tokens, stream);
-    if (chunks <= 8) return launch_rope<T, RopeCfg<8, HPU, true, true>, QKN>(a, T_tokens, stream);
-    if (chunks <= 16) return launch_rope<T, RopeCfg<16, HPU, true, true>, QKN>(a, T_tokens, stream);
-    if (chunks <= 32) return launch_rope<T, RopeCfg<32, HPU, true, true>, QKN>(a, T_tokens, stream);
-    if (chunks <= 64) return launch_rope<T, RopeCfg<64, HPU, true, true>, QKN>(a, T_tokens, stream);
+    if (chunks <= 1) return launch_rope<T, RopeCfg<1, HPU, true, NTS>, QKN>(a, T_tokens, stream);
+    if (chunks <= 2) return launch_rope<T, RopeCfg<2, HPU, true, NTS>, QKN>(a, T_tokens, stream);
+    if (chunks <= 4) return launch_rope<T, RopeCfg<4, HPU, true, NTS>, QKN>(a, T_tokens, stream);
+    if (chunks <= 8) return launch_rope<T, RopeCfg<8, HPU, true, NTS>, QKN>(a, T_tokens, stream);
+    if (chunks <= 16) return launch_rope<T, RopeCfg<16, HPU, true, NTS>, QKN>(a, T_tokens, stream);
+    if (chunks <= 32) return launch_rope<T, RopeCfg<32, HPU, true, NTS>, QKN>(a, T_tokens, stream);
+    if (chunks <= 64) return launch_rope<T, RopeCfg<64, HPU, true, NTS>, QKN>(a, T_tokens, stream);
     return KCR_ERR_SHAPE;
 }
 
-// One virtual head per unit spreads small batches over the most
-// workgroups; prefill-sized batches take two per unit, which reuses each
-// cos/sin load once and measured fastest there.
+// One virtual head per unit spreads decode batches (up to 4096 tokens) over
+// the most workgroups; prefill-sized batches take two per unit, which reuses
+// each cos/sin load once and measured fastest there. Stores stay
+// nontemporal at every size: cached stores of q_out and the cache rows made
+// the 28-layer, batch-256 decode chain 28 us slower per step on MI355X (each
+// kernel then writes its dirty L2 lines back before the next one starts).
 constexpr int64_t kRopeSmallBatch = 4096;
 
 template <typename T, bool QKN>
 static int dispatch_rope(const RopeArgs& a, int64_t T_tokens, void* stream) {
-    return T_tokens <= kRopeSmallBatch ? dispatch_rope_lpu<T, 1, QKN>(a, T_tokens, stream)
-                                       : dispatch_rope_lpu<T, 2, QKN>(a, T_tokens, stream);
+    return T_tokens <= kRopeSmallBatch ? dispatch_rope_lpu<T, 1, QKN, true>(a, T_tokens, stream)
+                                       : dispatch_rope_lpu<T, 2, QKN, true>(a, T_tokens, stream);
 }
 
 // ---------------------------------------------------------- cos/sin tables
