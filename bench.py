@@ -17,6 +17,7 @@ Prints ONE JSON line:
   cpu_baseline the CPU fp64 oracle on a bounded sample of the same workload
   kernels      each kernel at its large shape on cold, rotated buffers
   ceiling      1 GiB device copies: the library's copy kernel and hipMemcpy
+  decode_token_b1  per-op latency of the batch-1 decode token
 """
 from __future__ import annotations
 
@@ -306,6 +307,69 @@ def rmsnorm_sweep(kcr, reps: int):
     return out
 
 
+def decode_token_latency(kcr, reps: int):
+    """The batch-1 decode token (x[1,1536], Q[1,12,128] / K,V[1,2,128] at
+    position 37 into slot 597, gate/up[1,8960]; bf16): each op's time per
+    launch inside a captured graph of 64 back-to-back launches (which
+    includes the graph's per-node cost), and its kernel duration stamped by
+    HIP events at the kernel's own start and end (median of 200). At this
+    size the data sits in cache, so latency, not GB/s, is the figure."""
+    import torch
+    import workloads
+    dev = torch.device("cuda")
+    wl = workloads.decode_token(seed=0)
+    x, w = wl["x"].to(dev), wl["w"].to(dev)
+    y = torch.empty_like(x)
+    h = x.clone()
+    delta = wl["gate"][:, :1536].contiguous().to(dev)
+    q, k, v = wl["q"].to(dev), wl["k"].to(dev), wl["v"].to(dev)
+    pos, slots = wl["positions"].to(dev), wl["slot_mapping"].to(dev)
+    cos, sin = kcr.rope_cos_sin(wl["max_pos"], 128, wl["theta"], device=dev)
+    cache = wl["cache"].to(dev)
+    q_out = torch.empty_like(q)
+    gate, up = wl["gate"].to(dev), wl["up"].to(dev)
+    act = torch.empty_like(gate)
+    ops = {
+        "rmsnorm": lambda: kcr.rmsnorm(x, w, wl["eps"], out=y),
+        "add_rmsnorm": lambda: kcr.add_rmsnorm(h, delta, w, wl["eps"], out=y),
+        "rope_kvstore": lambda: kcr.rope_kvstore(q, k, v, pos, cos, sin, cache, slots, q_out=q_out),
+        "swiglu": lambda: kcr.swiglu(gate, up, out=act),
+    }
+    out = {}
+    for name, fn in ops.items():
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(64):
+                fn()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = events(2)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        in_graph = e0.elapsed_time(e1) * 1e3 / (reps * 64)
+        del g
+        ev = events(400)
+        for i in range(200):
+            timed_launch(kcr, fn, ev[2 * i], ev[2 * i + 1])
+        torch.cuda.synchronize()
+        st = kernel_stats([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(200)])
+        out[name] = dict(in_graph_us_per_launch=round(in_graph, 3), kernel_median_us=round(st["median_us"], 3),
+                         kernel_p20_us=round(st["p20_us"], 3), kernel_p80_us=round(st["p80_us"], 3))
+    log("decode token (batch 1): " + ", ".join(f"{k} {v['in_graph_us_per_launch']:.2f} us/launch in graph, "
+                                               f"{v['kernel_median_us']:.2f} us kernel" for k, v in out.items()))
+    return out
+
+
 def launch_floor(kcr, n_launch: int, reps: int):
     """Per-node time of a captured graph of n_launch minimal launches (a
     16-byte copy): what one graph node costs with (almost) no work."""
@@ -498,7 +562,7 @@ def main():
     # eager warm-up, then per-kernel durations inside whole steps
     chain.step_eager()
     torch.cuda.synchronize()
-    per_op, sums = instrumented_steps(kcr, chain, max(3, args.steps // 10))
+    per_op, sums = instrumented_steps(kcr, chain, max(3, args.steps // 5))
     sw = per_op["swiglu"]
     sw_us = 1e3 * statistics.fmean(sw)
     sw_bytes = swiglu_bytes(B, inter, 2)
@@ -541,6 +605,7 @@ def main():
     op_graph = graph_op_us(kcr, chain, max(10, args.steps // 2))
     chain.reset_residual()
     log("in-graph per-launch us: " + ", ".join(f"{k} {v:.2f}" for k, v in op_graph.items()))
+    token = decode_token_latency(kcr, max(10, args.steps // 2))
     ceiling = copy_ceiling(kcr, args.kernel_iters)
     kernels = {} if args.skip_large else large_shapes(kcr, args.kernel_iters)
     sweep = {} if args.skip_sweep else rmsnorm_sweep(kcr, max(10, args.steps // 5))
@@ -577,6 +642,7 @@ def main():
         "launch_floor_share_of_step": round(4 * len(chain.layers) * floor_us / (ms * 1e3), 4),
         "op_event_stamped_mean_us": op_us,
         "op_in_graph_us": {k: round(v, 3) for k, v in op_graph.items()},
+        "decode_token_b1": token,
         "timed_wall_s": round(wall_s, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -8,9 +8,11 @@ configuration), against the CPU fp64 oracle:
   4 SwiGLU of a fused gate_up [8192, 2 x 8960]
   5 the 28-layer batch-256 decode chain, replayed from a captured HIP graph
 
-At the large shapes the oracle checks sampled rows/tokens one by one and
-whole-tensor properties cover the rest (residual and V bit-exact, untouched
-cache slots still hold the sentinel)."""
+At the large shapes (including those of the NEXT rows the benchmark times:
+the per-head Q/K norm, the clip norm, ReGLU and the wide-row kernel) the
+oracle checks sampled rows/tokens one by one and whole-tensor properties
+cover the rest (residual and V bit-exact, untouched cache slots still hold
+the sentinel)."""
 import numpy as np
 import pytest
 import torch
@@ -90,6 +92,11 @@ def test_config4_swiglu(kcr):
     out = kcr.swiglu_fused(wl["gate_up"].cuda())
     ref = oracle.swiglu(np_bits(wl["gate"]), np_bits(wl["up"]))
     assert_close(out.cpu().double().numpy(), ref, torch.bfloat16, "config 4")
+    # ReGLU on the same fused buffer (the benchmark times both at this shape)
+    gu = wl["gate_up"].cuda()
+    out = kcr.reglu(gu[:, :8960], gu[:, 8960:])
+    ref = oracle.reglu(np_bits(wl["gate"]), np_bits(wl["up"]))
+    assert_close(out.cpu().double().numpy(), ref, torch.bfloat16, "config 4 reglu")
 
 
 def test_config5_decode_chain_graph(kcr):
@@ -137,7 +144,7 @@ def test_config5_decode_chain_graph(kcr):
 
 def test_large_rmsnorm_sampled(kcr):
     R, d = 131072, 2176
-    for dt in ("bf16", "f32"):
+    for dt in ("bf16", "f32", "f16"):
         say(f"large rmsnorm [{R}, {d}] {dt}, sampled rows")
         wl = workloads.rmsnorm_rows(rows=R, d=d, dtype=dt, seed=0)
         y = kcr.rmsnorm(wl["x"].cuda(), wl["w"].cuda(), wl["eps"]).cpu()
@@ -212,3 +219,62 @@ def test_large_paged_gather_sampled(kcr):
     for b in (0, 131, 255):
         ref = oracle.paged_gather(c, 0, lay.block_tables[b].numpy(), 4096)
         assert np.array_equal(np_bits(k[b].cpu()), ref)
+
+
+def test_large_qknorm_rope_sampled(kcr):
+    """Per-head Q/K RMSNorm + RoPE + paged store at the benchmark's prefill
+    shape (64 sequences), with non-unit norm weights."""
+    say("large prefill qknorm + rope + store, 64 seqs, sampled tokens")
+    wl = workloads.prefill(n_seqs=64, dtype="bf16", seed=0)
+    T, hkv, dh = wl["qkv"].shape[0], wl["hkv"], wl["dh"]
+    g = workloads.gen(11)
+    wq = (1 + 0.2 * workloads.randn([dh], g)).to(torch.bfloat16)
+    wk = (0.5 + torch.rand([dh], generator=g)).to(torch.bfloat16)
+    eps = 1e-6
+    cos, sin = kcr.rope_cos_sin(wl["max_pos"], dh, wl["theta"])
+    cache = wl["cache"].cuda()
+    q, k, v = gpu_qkv(wl)
+    slots = wl["slot_mapping"].cuda()
+    qo = kcr.qknorm_rope_kvstore(q, k, v, wq.cuda(), wk.cuda(), eps, wl["positions"].cuda(), cos, sin,
+                                 cache, slots)
+    flat = cache.view(2, -1, hkv, dh)
+    assert torch.equal(flat[1][slots].view(torch.int16), v.view(torch.int16))
+    assert int((cache.view(torch.int16) == -1).sum()) == cache.numel() - 2 * T * hkv * dh
+    toks = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(4).choice(T, 500, replace=False)]))
+    q_rot, k_rot = oracle.qknorm_rope_kvstore(np_bits(wl["q"][toks]), np_bits(wl["k"][toks]),
+                                              np_bits(wl["v"][toks]), np_bits(wq), np_bits(wk),
+                                              f32eps(eps), wl["positions"].numpy()[toks], wl["theta"],
+                                              None, None)
+    assert_rope_close(qo.cpu()[toks].double().numpy(), q_rot, torch.bfloat16, "sampled q_out")
+    k_got = flat[0][slots[torch.from_numpy(toks).cuda()]].cpu().double().numpy()
+    assert_rope_close(k_got, k_rot, torch.bfloat16, "sampled K slots")
+
+
+def test_large_clip_norm_sampled(kcr):
+    """The DyHT clip norm at the benchmark's shape: [131072, 2176] bf16 with
+    per-channel alpha and gamma."""
+    R, d = 131072, 2176
+    say(f"large clip norm [{R}, {d}] bf16, sampled rows")
+    wl = workloads.rmsnorm_rows(rows=R, d=d, dtype="bf16", seed=0)
+    g = workloads.gen(12)
+    alpha = (0.5 * workloads.randn([d], g)).to(torch.bfloat16)
+    gamma = wl["w"]
+    y = kcr.clip_norm(wl["x"].cuda(), alpha.cuda(), gamma.cuda()).cpu()
+    rows = np.unique(np.concatenate([[0, R - 1], wl["outlier_rows"].numpy()[:50],
+                                     np.random.default_rng(5).choice(R, 400, replace=False)]))
+    ref = oracle.clip_norm(np_bits(wl["x"][rows]).reshape(len(rows), 1, d), np_bits(alpha), np_bits(gamma))
+    assert_close(y[rows].double().numpy(), ref.reshape(len(rows), d), torch.bfloat16, "sampled rows")
+    assert bool((y.abs() <= gamma.abs().float().max() + 1e-6).all())
+
+
+@pytest.mark.parametrize("rows,d", [(2048, 65536), (512, 262144)])
+def test_large_wide_rmsnorm_sampled(kcr, rows, d):
+    """The two-pass wide-row kernel at the benchmark's shapes: LDS-staged rows
+    of 128 KB, and rows of 512 KB that are read twice."""
+    say(f"large wide rmsnorm [{rows}, {d}] bf16, sampled rows")
+    wl = workloads.rmsnorm_rows(rows=rows, d=d, dtype="bf16", seed=0)
+    y = kcr.rmsnorm(wl["x"].cuda(), wl["w"].cuda(), wl["eps"]).cpu()
+    pick = np.unique(np.concatenate([[0, rows - 1], wl["outlier_rows"].numpy()[:4],
+                                     np.random.default_rng(6).choice(rows, 24, replace=False)]))
+    ref = oracle.rmsnorm(np_bits(wl["x"][pick]), np_bits(wl["w"]), f32eps(wl["eps"]))
+    assert_close(y[pick].double().numpy(), ref, torch.bfloat16, "sampled wide rows")
