@@ -13,7 +13,8 @@ Prints ONE JSON line:
   ms_per_step  decode-step fused-op latency (graph replay)
   roofline     dominant kernel (swiglu at the chain's shape): algorithmic
                bytes per launch / its mean duration, measured with events
-               stamped at kernel start and end (hipExtLaunchKernel)
+               stamped at kernel start and end (hipExtLaunchKernel) in whole
+               steps that run back to back behind graph replays
   cpu_baseline the CPU fp64 oracle on a bounded sample of the same workload
   kernels      each kernel at its large shape on cold, rotated buffers
   ceiling      1 GiB device copies: the library's copy kernel and hipMemcpy
@@ -74,14 +75,20 @@ def chain_ops(kcr, chain, L):
     ]
 
 
-def instrumented_steps(kcr, chain, n_steps):
-    """Eager steps with every launch's kernel duration stamped; returns
-    {op: [ms, ...]} and the per-step kernel-time sums."""
+def instrumented_steps(kcr, chain, n_steps, prelude: int = 10):
+    """Whole eager steps with every launch's kernel duration stamped at the
+    kernel's own start and end; returns {op: [ms, ...]} and the per-step
+    kernel-time sums. Each step is enqueued behind `prelude` replays of the
+    captured step, so the GPU is still busy with them while the host enqueues
+    the step's launches, which then run back to back as in the timed graph
+    replays rather than spaced out by host launch time."""
     import torch
     per_op, sums = {}, []
     n_launch = 4 * len(chain.layers)
     ev = events(2 * n_launch)
     for _ in range(n_steps):
+        for _ in range(prelude):
+            chain.step_graph()
         names = []
         i = 0
         for L in chain.layers:
@@ -559,9 +566,10 @@ def main():
     B, inter = chain.h.shape[0], chain.inter
     log(f"step moves {nbytes['step']} algorithmic bytes over {4 * len(chain.layers)} launches")
 
-    # eager warm-up, then per-kernel durations inside whole steps
+    # eager warm-up and capture, then per-kernel durations inside whole steps
     chain.step_eager()
     torch.cuda.synchronize()
+    chain.capture()
     per_op, sums = instrumented_steps(kcr, chain, max(3, args.steps // 5))
     sw = per_op["swiglu"]
     sw_us = 1e3 * statistics.fmean(sw)
@@ -582,7 +590,6 @@ def main():
     eager_ms = e0.elapsed_time(e1) / n_eager
 
     # graph replay: the timed region
-    chain.capture()
     for _ in range(args.warmup):
         chain.step_graph()
     torch.cuda.synchronize()

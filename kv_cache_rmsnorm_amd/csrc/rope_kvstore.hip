@@ -58,10 +58,10 @@ struct RopeArgs {
 
 // Launch shape: LPU lanes per unit (one 16-byte chunk of each half head per
 // lane), HPU virtual heads per unit, nontemporal loads (NTL) and stores (NTS)
-// for the streamed heads.
-template <int LPU_, int HPU_, bool NTL_, bool NTS_>
+// for the streamed heads, BLOCK lanes per workgroup.
+template <int LPU_, int HPU_, bool NTL_, bool NTS_, int BLOCK_ = 256>
 struct RopeCfg {
-    static constexpr int LPU = LPU_, HPU = HPU_;
+    static constexpr int LPU = LPU_, HPU = HPU_, BLOCK = BLOCK_;
     static constexpr bool NTL = NTL_, NTS = NTS_;
 };
 
@@ -73,10 +73,10 @@ struct RopeCfg {
 // head's sum of squares with DPP, so all of them stay active (lanes past the
 // head's last chunk read chunk 0 and count zero).
 template <typename T, typename C, bool QKN>
-__global__ __launch_bounds__(256) void rope_kvstore_kernel(const RopeArgs a) {
+__global__ __launch_bounds__(C::BLOCK) void rope_kvstore_kernel(const RopeArgs a) {
     using S = typename T::storage;
     constexpr int kVec = T::kVec, LPU = C::LPU, HPU = C::HPU;
-    constexpr int UPW = 256 / LPU;  // units per workgroup
+    constexpr int UPW = C::BLOCK / LPU;  // units per workgroup
     const int c = threadIdx.x % LPU;
     const int half = a.dh >> 1;
     const bool lane_on = c * kVec < half;
@@ -204,10 +204,10 @@ __global__ __launch_bounds__(256) void rope_kvstore_kernel(const RopeArgs a) {
 template <typename T, typename C, bool QKN>
 static int launch_rope(RopeArgs a, int64_t T_tokens, void* stream) {
     using S = typename T::storage;
-    constexpr int UPW = 256 / C::LPU;
+    constexpr int UPW = C::BLOCK / C::LPU;
     const int64_t upt = (a.nvh + C::HPU - 1) / C::HPU;
     a.upt = make_fastdiv((uint32_t)upt);
-    const int64_t max_tokens = ((int64_t)0xFFFFFFFFu / 256) * UPW / upt;
+    const int64_t max_tokens = ((int64_t)0xFFFFFFFFu / C::BLOCK) * UPW / upt;
     for (int64_t t0 = 0; t0 < T_tokens; t0 += max_tokens) {
         RopeArgs c = a;
         const int64_t n = T_tokens - t0 < max_tokens ? T_tokens - t0 : max_tokens;
@@ -219,37 +219,39 @@ static int launch_rope(RopeArgs a, int64_t T_tokens, void* stream) {
         c.slots = a.slots + t0;
         c.units = (uint32_t)(n * upt);
         const dim3 grid((uint32_t)((c.units + UPW - 1) / UPW));
-        const int rc = launch(rope_kvstore_kernel<T, C, QKN>, grid, dim3(256), stream, c);
+        const int rc = launch(rope_kvstore_kernel<T, C, QKN>, grid, dim3(C::BLOCK), stream, c);
         if (rc != KCR_OK) return rc;
     }
     return KCR_OK;
 }
 
-template <typename T, int HPU, bool QKN, bool NTS>
+template <typename T, int HPU, bool QKN, int BLOCK>
 static int dispatch_rope_lpu(const RopeArgs& a, int64_t T_tokens, void* stream) {
     const int chunks = (a.dh / 2) / T::kVec;
-    if (chunks <= 1) return launch_rope<T, RopeCfg<1, HPU, true, NTS>, QKN>(a, T_tokens, stream);
-    if (chunks <= 2) return launch_rope<T, RopeCfg<2, HPU, true, NTS>, QKN>(a, T_tokens, stream);
-    if (chunks <= 4) return launch_rope<T, RopeCfg<4, HPU, true, NTS>, QKN>(a, T_tokens, stream);
-    if (chunks <= 8) return launch_rope<T, RopeCfg<8, HPU, true, NTS>, QKN>(a, T_tokens, stream);
-    if (chunks <= 16) return launch_rope<T, RopeCfg<16, HPU, true, NTS>, QKN>(a, T_tokens, stream);
-    if (chunks <= 32) return launch_rope<T, RopeCfg<32, HPU, true, NTS>, QKN>(a, T_tokens, stream);
-    if (chunks <= 64) return launch_rope<T, RopeCfg<64, HPU, true, NTS>, QKN>(a, T_tokens, stream);
+    if (chunks <= 1) return launch_rope<T, RopeCfg<1, HPU, true, true, BLOCK>, QKN>(a, T_tokens, stream);
+    if (chunks <= 2) return launch_rope<T, RopeCfg<2, HPU, true, true, BLOCK>, QKN>(a, T_tokens, stream);
+    if (chunks <= 4) return launch_rope<T, RopeCfg<4, HPU, true, true, BLOCK>, QKN>(a, T_tokens, stream);
+    if (chunks <= 8) return launch_rope<T, RopeCfg<8, HPU, true, true, BLOCK>, QKN>(a, T_tokens, stream);
+    if (chunks <= 16) return launch_rope<T, RopeCfg<16, HPU, true, true, BLOCK>, QKN>(a, T_tokens, stream);
+    if (chunks <= 32) return launch_rope<T, RopeCfg<32, HPU, true, true, BLOCK>, QKN>(a, T_tokens, stream);
+    if (chunks <= 64) return launch_rope<T, RopeCfg<64, HPU, true, true, BLOCK>, QKN>(a, T_tokens, stream);
     return KCR_ERR_SHAPE;
 }
 
-// One virtual head per unit spreads decode batches (up to 4096 tokens) over
-// the most workgroups; prefill-sized batches take two per unit, which reuses
-// each cos/sin load once and measured fastest there. Stores stay
-// nontemporal at every size: cached stores of q_out and the cache rows made
-// the 28-layer, batch-256 decode chain 28 us slower per step on MI355X (each
-// kernel then writes its dirty L2 lines back before the next one starts).
+// Decode batches (up to 4096 tokens): one virtual head per unit spreads the
+// work over the most workgroups, and 128-lane workgroups measured 2.8 us
+// faster per step than 256-lane ones in the 28-layer, batch-256 decode chain
+// on MI355X. Prefill-sized batches take two heads per unit, which reuses
+// each cos/sin load once, in 256-lane workgroups (64 and 128 lanes measured
+// the same there). Stores stay nontemporal at every size: cached stores of
+// q_out and the cache rows made the decode chain 28 us slower per step
+// (each kernel then writes its dirty L2 lines back before the next starts).
 constexpr int64_t kRopeSmallBatch = 4096;
 
 template <typename T, bool QKN>
 static int dispatch_rope(const RopeArgs& a, int64_t T_tokens, void* stream) {
-    return T_tokens <= kRopeSmallBatch ? dispatch_rope_lpu<T, 1, QKN, true>(a, T_tokens, stream)
-                                       : dispatch_rope_lpu<T, 2, QKN, true>(a, T_tokens, stream);
+    return T_tokens <= kRopeSmallBatch ? dispatch_rope_lpu<T, 1, QKN, 128>(a, T_tokens, stream)
+                                       : dispatch_rope_lpu<T, 2, QKN, 256>(a, T_tokens, stream);
 }
 
 // ---------------------------------------------------------- cos/sin tables
