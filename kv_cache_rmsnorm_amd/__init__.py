@@ -84,6 +84,19 @@ def _dt(*ts: torch.Tensor) -> int:
     return _DTYPE[dt]
 
 
+def _expect(cond: bool, msg: str) -> None:
+    """Shape checks the C ABI cannot make: it sees only pointers, so a tensor
+    smaller than the sizes passed with it would be read or written past its
+    end."""
+    if not cond:
+        raise ValueError(msg)
+
+
+def _same(a: torch.Tensor, b: torch.Tensor, what: str) -> None:
+    _expect(tuple(a.shape) == tuple(b.shape), f"{what}: shape {tuple(a.shape)} != {tuple(b.shape)}")
+    _expect(a.dtype == b.dtype and a.device == b.device, f"{what}: dtype/device mismatch")
+
+
 def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
@@ -115,7 +128,9 @@ def rmsnorm(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
             out: torch.Tensor | None = None) -> torch.Tensor:
     dt = _dt(x, w)
     rows, d, xs = _rows(x)
+    _expect(w.dim() == 1 and w.numel() == d and w.is_contiguous(), "w must be a contiguous [d] vector")
     y = torch.empty_like(x, memory_format=torch.contiguous_format) if out is None else out
+    _same(y, x, "rmsnorm out")
     _, _, ys = _rows(y)
     _check("rmsnorm", _lib.kcr_rmsnorm(x.data_ptr(), xs, w.data_ptr(), y.data_ptr(), ys, rows, d,
                                        float(eps), dt, _stream(x)))
@@ -127,8 +142,11 @@ def add_rmsnorm(x: torch.Tensor, delta: torch.Tensor, w: torch.Tensor, eps: floa
     """x is updated in place to x + delta; returns rmsnorm(x + delta) * w."""
     dt = _dt(x, delta, w)
     rows, d, xs = _rows(x)
+    _same(delta, x, "add_rmsnorm delta")
     _, _, ds = _rows(delta)
+    _expect(w.dim() == 1 and w.numel() == d and w.is_contiguous(), "w must be a contiguous [d] vector")
     y = torch.empty_like(x, memory_format=torch.contiguous_format) if out is None else out
+    _same(y, x, "add_rmsnorm out")
     _, _, ys = _rows(y)
     _check("add_rmsnorm", _lib.kcr_add_rmsnorm(x.data_ptr(), xs, delta.data_ptr(), ds, w.data_ptr(),
                                                y.data_ptr(), ys, rows, d, float(eps), dt, _stream(x)))
@@ -137,8 +155,19 @@ def add_rmsnorm(x: torch.Tensor, delta: torch.Tensor, w: torch.Tensor, eps: floa
 
 def _rope_checks(q, k, v, positions, cos, sin, kv_cache, slot_mapping, q_out):
     dt = _dt(q, k, v, kv_cache)
+    _expect(q.dim() == 3 and k.dim() == 3 and v.dim() == 3, "q, k, v must be [T, heads, head_dim]")
     T, hq, hd = q.shape
     hkv = k.shape[1]
+    _expect(tuple(k.shape) == (T, hkv, hd) and tuple(v.shape) == (T, hkv, hd),
+            "k and v must be [T, n_kv_head, head_dim] with q's T and head_dim")
+    _expect(q.stride(2) == 1 and k.stride(2) == 1 and v.stride(2) == 1,
+            "the head dimension of q, k, v must be contiguous")
+    _expect(positions.dim() == 1 and positions.numel() == T and slot_mapping.dim() == 1
+            and slot_mapping.numel() == T, "positions and slot_mapping must be [T]")
+    _expect(positions.device == q.device and slot_mapping.device == q.device and cos.device == q.device
+            and sin.device == q.device, "all tensors must be on q's device")
+    _expect(cos.dim() == 2 and cos.shape[1] == hd // 2 and tuple(sin.shape) == tuple(cos.shape),
+            "cos and sin must both be [max_pos, head_dim / 2]")
     if positions.dtype != torch.int64 or slot_mapping.dtype != torch.int64:
         raise TypeError("positions and slot_mapping must be int64")
     if cos.dtype != torch.float32 or sin.dtype != torch.float32:
@@ -150,6 +179,8 @@ def _rope_checks(q, k, v, positions, cos, sin, kv_cache, slot_mapping, q_out):
         raise ValueError("kv_cache must be [2, num_blocks, block_size, n_kv_head, head_dim]")
     if q_out is None:
         q_out = torch.empty((T, hq, hd), dtype=q.dtype, device=q.device)
+    _expect(tuple(q_out.shape) == (T, hq, hd) and q_out.is_contiguous() and q_out.dtype == q.dtype
+            and q_out.device == q.device, "q_out must be a contiguous [T, n_head, head_dim] tensor like q")
     return dt, T, hq, hkv, hd, q_out
 
 
@@ -177,6 +208,9 @@ def qknorm_rope_kvstore(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_nor
     dt, T, hq, hkv, hd, q_out = _rope_checks(q, k, v, positions, cos, sin, kv_cache, slot_mapping, q_out)
     if q_norm_w.dtype != q.dtype or k_norm_w.dtype != q.dtype:
         raise TypeError("norm weights must have the activation dtype")
+    _expect(q_norm_w.numel() == hd and k_norm_w.numel() == hd and q_norm_w.is_contiguous()
+            and k_norm_w.is_contiguous() and q_norm_w.device == q.device and k_norm_w.device == q.device,
+            "q_norm_w and k_norm_w must be contiguous [head_dim] vectors on q's device")
     _check("qknorm_rope_kvstore", _lib.kcr_qknorm_rope_kvstore(
         q.data_ptr(), q.stride(0), q.stride(1), k.data_ptr(), k.stride(0), k.stride(1),
         v.data_ptr(), v.stride(0), v.stride(1), q_norm_w.data_ptr(), k_norm_w.data_ptr(), float(eps),
@@ -194,13 +228,20 @@ def rope_cos_sin(max_pos: int, head_dim: int, theta: float, device="cuda"):
     return cos, sin
 
 
-def swiglu(gate: torch.Tensor, up: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+def _gated_args(gate: torch.Tensor, up: torch.Tensor, out: torch.Tensor | None, what: str):
     dt = _dt(gate, up)
+    _same(up, gate, f"{what} up")
     rows, cols, gs = _rows(gate)
     _, _, us = _rows(up)
     if out is None:
         out = torch.empty(gate.shape, dtype=gate.dtype, device=gate.device)
+    _same(out, gate, f"{what} out")
     _, _, os_ = _rows(out)
+    return dt, rows, cols, gs, us, out, os_
+
+
+def swiglu(gate: torch.Tensor, up: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    dt, rows, cols, gs, us, out, os_ = _gated_args(gate, up, out, "swiglu")
     _check("swiglu", _lib.kcr_swiglu(gate.data_ptr(), gs, up.data_ptr(), us, out.data_ptr(), os_,
                                      rows, cols, dt, _stream(gate)))
     return out
@@ -208,12 +249,7 @@ def swiglu(gate: torch.Tensor, up: torch.Tensor, out: torch.Tensor | None = None
 
 def reglu(gate: torch.Tensor, up: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """relu(gate) * up (same layouts as swiglu)."""
-    dt = _dt(gate, up)
-    rows, cols, gs = _rows(gate)
-    _, _, us = _rows(up)
-    if out is None:
-        out = torch.empty(gate.shape, dtype=gate.dtype, device=gate.device)
-    _, _, os_ = _rows(out)
+    dt, rows, cols, gs, us, out, os_ = _gated_args(gate, up, out, "reglu")
     _check("reglu", _lib.kcr_reglu(gate.data_ptr(), gs, up.data_ptr(), us, out.data_ptr(), os_,
                                    rows, cols, dt, _stream(gate)))
     return out
@@ -230,10 +266,15 @@ def clip_norm(x: torch.Tensor, alpha: torch.Tensor, gamma: torch.Tensor, lo: flo
         squeeze = True
     else:
         squeeze = False
+    _expect(x.dim() == 3, "x must be [n_tok, n_head, d] or [n, d]")
     n, h, d = x.shape
     if x.stride(2) != 1:
         raise ValueError("the last dimension must be contiguous")
+    for name, p in (("alpha", alpha), ("gamma", gamma)):
+        _expect(p.numel() in (1, d) and p.is_contiguous(), f"{name} must be a contiguous [d] or [1] tensor")
     y = torch.empty((n, h, d), dtype=x.dtype, device=x.device) if out is None else out
+    _same(y, x, "clip_norm out")
+    _expect(y.stride(2) == 1, "the last dimension of out must be contiguous")
     _check("clip_norm", _lib.kcr_clip_norm(
         x.data_ptr(), x.stride(0), x.stride(1), y.data_ptr(), y.stride(0), y.stride(1), n, h, d,
         alpha.data_ptr(), int(alpha.numel() > 1), gamma.data_ptr(), int(gamma.numel() > 1),
@@ -255,7 +296,13 @@ def paged_kv_gather(kv_cache: torch.Tensor, block_tables: torch.Tensor, seq_lens
     Rows past a sequence's length are left as allocated (uninitialized when
     the outputs are created here)."""
     dt = _dt(kv_cache)
+    _expect(kv_cache.dim() == 5 and kv_cache.shape[0] == 2,
+            "kv_cache must be [2, num_blocks, block_size, n_kv_head, head_dim]")
     _, nb, bs, hkv, hd = kv_cache.shape
+    _expect(block_tables.dim() == 2 and seq_lens.dim() == 1 and seq_lens.numel() == block_tables.shape[0],
+            "block_tables must be [n_seqs, max_blocks] and seq_lens [n_seqs]")
+    _expect(block_tables.device == kv_cache.device and seq_lens.device == kv_cache.device,
+            "all tensors must be on the cache's device")
     n = block_tables.shape[0]
     if block_tables.dtype != torch.int64 or seq_lens.dtype != torch.int64:
         raise TypeError("block_tables and seq_lens must be int64")
@@ -264,6 +311,9 @@ def paged_kv_gather(kv_cache: torch.Tensor, block_tables: torch.Tensor, seq_lens
     shape = (n, max_len, hkv, hd)
     k_out = torch.empty(shape, dtype=kv_cache.dtype, device=kv_cache.device) if k_out is None else k_out
     v_out = torch.empty(shape, dtype=kv_cache.dtype, device=kv_cache.device) if v_out is None else v_out
+    for name, o in (("k_out", k_out), ("v_out", v_out)):
+        _expect(tuple(o.shape) == shape and o.is_contiguous() and o.dtype == kv_cache.dtype
+                and o.device == kv_cache.device, f"{name} must be a contiguous {shape} tensor like the cache")
     _check("paged_kv_gather", _lib.kcr_paged_kv_gather(
         kv_cache.data_ptr(), nb, bs, hkv, hd, block_tables.data_ptr(), block_tables.shape[1],
         seq_lens.data_ptr(), n, max_len, k_out.data_ptr(), v_out.data_ptr(), dt, _stream(kv_cache)))
@@ -275,6 +325,7 @@ def copy_(dst: torch.Tensor, src: torch.Tensor) -> torch.Tensor:
     n = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() < n or not (dst.is_contiguous() and src.is_contiguous()):
         raise ValueError("copy_ needs contiguous tensors, dst at least as large as src")
+    _expect(dst.device.type == "cuda" and src.device == dst.device, "copy_ takes two tensors on one device")
     _check("copy", _lib.kcr_copy(dst.data_ptr(), src.data_ptr(), n, _stream(src)))
     return dst
 

@@ -35,6 +35,8 @@
 //    wider rows are read twice (the second time mostly from L2/MALL).
 #pragma once
 
+#include <atomic>
+
 #include "norm.h"
 
 namespace kcr {
@@ -293,17 +295,32 @@ __global__ __launch_bounds__(kWideThreads) void wide_norm_kernel(const NormArgs 
 constexpr size_t kWideStaticLds = 2 * kWideWaves * sizeof(float);
 constexpr int64_t kWideGridCap = 1 << 16;
 
+// The staged kernel's dynamic-LDS limit is raised once per device to all
+// the device allows beyond the kernel's static LDS, so every staged launch
+// fits under it and concurrent calls with different widths never race on
+// the attribute.
+template <typename T, bool ADD>
+static bool wide_lds_ready(size_t limit) {
+    static std::atomic<int> done[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
+    if (done[dev].load(std::memory_order_acquire)) return true;
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(wide_norm_kernel<T, ADD, true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)limit) != hipSuccess)
+        return false;
+    done[dev].store(1, std::memory_order_release);
+    return true;
+}
+
 template <typename T, bool ADD>
 static int launch_wide(const NormArgs& a, void* stream) {
     const int64_t nvec = (a.d + T::kVec - 1) / T::kVec;
     const dim3 grid((uint32_t)(a.rows < kWideGridCap ? a.rows : kWideGridCap));
     const size_t stage = (size_t)nvec * 16;
-    if (stage + kWideStaticLds <= lds_per_block()) {
-        auto kern = wide_norm_kernel<T, ADD, true>;
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)stage) != hipSuccess)
-            return KCR_ERR_LAUNCH;
-        return launch(kern, grid, dim3(kWideThreads), stream, a, stage);
+    const size_t lds = lds_per_block();
+    if (lds > kWideStaticLds && stage <= lds - kWideStaticLds) {
+        if (!wide_lds_ready<T, ADD>(lds - kWideStaticLds)) return KCR_ERR_LAUNCH;
+        return launch(wide_norm_kernel<T, ADD, true>, grid, dim3(kWideThreads), stream, a, stage);
     }
     return launch(wide_norm_kernel<T, ADD, false>, grid, dim3(kWideThreads), stream, a);
 }

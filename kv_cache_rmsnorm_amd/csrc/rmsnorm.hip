@@ -1,21 +1,24 @@
 // rmsnorm.hip -- the C entry points kcr_rmsnorm and kcr_add_rmsnorm:
 // argument checks, then the row-norm engine (norm_engine.h).
+#include <atomic>
+
 #include "norm.h"
 
 namespace kcr {
 
 // LDS bytes a workgroup may take on the current device (160 KB on gfx950),
-// queried once per device.
+// queried once per device (0 if there is no usable device).
 size_t lds_per_block() {
-    static size_t cache[64] = {};
+    static std::atomic<size_t> cache[kMaxDevices];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (!cache[dev]) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) v = 0;
-        cache[dev] = v > 0 ? (size_t)v : 1;
-    }
-    return cache[dev];
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    size_t n = cache[dev].load(std::memory_order_relaxed);
+    if (n) return n;
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0)
+        return 0;
+    cache[dev].store((size_t)v, std::memory_order_relaxed);
+    return (size_t)v;
 }
 
 static int check_norm_common(int64_t rows, int64_t d, int dtype, const void* w, const void* y,
