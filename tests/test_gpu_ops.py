@@ -55,7 +55,11 @@ def test_rmsnorm_widths(kcr, dt, d):
     assert_close(y.cpu().double().numpy(), ref, dt, f"rmsnorm d={d}")
 
 
-@pytest.mark.parametrize("d", [20000, 24577, 32768])
+# 20000..32768: 8 waves of up to 8 vectors in registers; just past the
+# register limit (32776), odd widths at 2-byte row offsets (40001, 49999) and
+# whole 112 KB / 128 KB rows (57344, 65536) take the LDS-staged two-pass
+# kernel.
+@pytest.mark.parametrize("d", [20000, 24577, 32768, 32776, 40001, 49999, 57344, 65536])
 def test_rmsnorm_widest_bf16(kcr, d):
     say(f"rmsnorm bf16 wide d={d}")
     wl = workloads.rmsnorm_rows(rows=9, d=d, dtype="bf16", seed=d)
