@@ -478,3 +478,42 @@ def test_copy(kcr):
     dst = torch.empty_like(src)
     kcr.copy_(dst, src)
     assert torch.equal(dst, src)
+
+
+def test_concurrent_host_threads(kcr):
+    """Two host threads call the library at once (ctypes releases the GIL),
+    each on its own stream, with row widths that take the LDS-staged
+    two-pass kernel at different staging sizes, plus a register-resident
+    width. Every result must equal the same call made alone."""
+    import threading
+    say("concurrent calls from two host threads")
+    cases = []
+    for d in (40000, 65536, 2176):
+        wl = workloads.rmsnorm_rows(rows=6, d=d, dtype="bf16", seed=d)
+        x, w = dev(wl["x"]), dev(wl["w"])
+        cases.append((x, w, kcr.rmsnorm(x, w, wl["eps"]).clone(), wl["eps"]))
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(order):
+        s = torch.cuda.Stream()
+        try:
+            with torch.cuda.stream(s):
+                for _ in range(25):
+                    for i in order:
+                        x, w, ref, eps = cases[i]
+                        y = kcr.rmsnorm(x, w, eps)
+                        s.synchronize()
+                        if not torch.equal(y.view(torch.int16), ref.view(torch.int16)):
+                            errors.append(f"case {i} differs")
+        except Exception as e:  # reported below, in the test's own thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(o,)) for o in ((0, 1, 2), (1, 0, 2))]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=60)
+    assert not any(th.is_alive() for th in threads), "a worker thread did not finish"
+    torch.cuda.synchronize()
+    assert not errors, errors[:3]
