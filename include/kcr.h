@@ -210,10 +210,25 @@ int kcr_qknorm_rope_kvstore(const void* q, int64_t q_tok_stride, int64_t q_head_
  * Frequencies are the RoFormer ones.
  *
  *   cos_tab, sin_tab [max_pos, head_dim/2] fp32 device outputs, 16-byte
- *   aligned; head_dim even and >= 2; max_pos >= 0.
+ *   aligned; head_dim even and >= 2; max_pos >= 0; theta > 0 (KCR_ERR_SHAPE
+ *   otherwise).
  */
 int kcr_rope_cos_sin(float* cos_tab, float* sin_tab, int64_t max_pos, int head_dim,
                      double theta, void* stream);
+
+/*
+ * kcr_rope_cos_sin_host -- the same tables, computed on the host into HOST
+ * memory (for callers that build them once and copy them to the device
+ * themselves): cos_tab[p, i] = cos(p * theta^(-2i/head_dim)), sin_tab
+ * likewise, in fp64 rounded once to fp32, with the precompute and fp32
+ * reasons of m.lsln.cn/news/61269, sections 2.3 and 1.1.
+ *
+ *   cos_tab, sin_tab [max_pos, head_dim/2] fp32 host outputs (caller-owned,
+ *   not overlapping); head_dim even and >= 2; max_pos >= 0; theta > 0
+ *   (KCR_ERR_SHAPE otherwise). Synchronous; touches no device.
+ */
+int kcr_rope_cos_sin_host(float* cos_tab, float* sin_tab, int64_t max_pos, int head_dim,
+                          double theta);
 
 /*
  * kcr_swiglu -- SwiGLU activation: out = silu(gate) * up, with

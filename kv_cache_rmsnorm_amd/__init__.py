@@ -14,6 +14,7 @@ Ops (names as in the C ABI):
                                            rotate-half RoPE of Q/K; q_out; K_rot, V -> cache
   swiglu(gate, up)                         silu(gate) * up
   rope_cos_sin(max_pos, head_dim, theta)   fp32 cos/sin tables built on the device
+  rope_cos_sin_host(max_pos, head_dim, theta)  the same tables built on the host
 """
 from __future__ import annotations
 
@@ -42,6 +43,7 @@ _SIGS = {
     "kcr_qknorm_rope_kvstore": [_P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _P, _P, _F, _P, _P,
                                 _P, _P, _I64, _P, _P, _I64, _I, _I, _I, _I, _I64, _I, _P],
     "kcr_rope_cos_sin": [_P, _P, _I64, _I, _D, _P],
+    "kcr_rope_cos_sin_host": [_P, _P, _I64, _I, _D],
     "kcr_swiglu": [_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I, _P],
     "kcr_reglu": [_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I, _P],
     "kcr_clip_norm": [_P, _I64, _I64, _P, _I64, _I64, _I64, _I, _I, _P, _I, _P, _I, _F, _F, _I, _P],
@@ -238,6 +240,16 @@ def _gated_args(gate: torch.Tensor, up: torch.Tensor, out: torch.Tensor | None, 
     _same(out, gate, f"{what} out")
     _, _, os_ = _rows(out)
     return dt, rows, cols, gs, us, out, os_
+
+
+def rope_cos_sin_host(max_pos: int, head_dim: int, theta: float):
+    """The cos/sin tables computed on the host: two CPU float32 tensors
+    [max_pos, head_dim / 2] (copy them to the device before use)."""
+    cos = torch.empty((max_pos, head_dim // 2), dtype=torch.float32)
+    sin = torch.empty_like(cos)
+    _check("rope_cos_sin_host", _lib.kcr_rope_cos_sin_host(cos.data_ptr(), sin.data_ptr(), max_pos,
+                                                           head_dim, float(theta)))
+    return cos, sin
 
 
 def swiglu(gate: torch.Tensor, up: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:

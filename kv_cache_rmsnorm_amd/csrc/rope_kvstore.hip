@@ -389,7 +389,7 @@ extern "C" int kcr_qknorm_rope_kvstore(const void* q, int64_t q_tok_stride, int6
 
 extern "C" int kcr_rope_cos_sin(float* cos_tab, float* sin_tab, int64_t max_pos, int head_dim,
                                 double theta, void* stream) {
-    if (max_pos < 0 || head_dim < 2 || head_dim % 2 != 0) return KCR_ERR_SHAPE;
+    if (max_pos < 0 || head_dim < 2 || head_dim % 2 != 0 || !(theta > 0.0)) return KCR_ERR_SHAPE;
     if (max_pos == 0) return KCR_OK;
     if (!cos_tab || !sin_tab) return KCR_ERR_NULL;
     if (!aligned16(cos_tab) || !aligned16(sin_tab)) return KCR_ERR_ALIGN;
@@ -399,4 +399,25 @@ extern "C" int kcr_rope_cos_sin(float* cos_tab, float* sin_tab, int64_t max_pos,
     if (device_cus() <= 0) return KCR_ERR_DEVICE;
     const TableArgs a{cos_tab, sin_tab, n, half, head_dim, theta};
     return launch(rope_table_kernel, dim3(grid_for(n, 256, device_cus(), 8)), dim3(256), stream, a);
+}
+
+// The host form of the same tables: one fp64 angle per (position,
+// frequency), its cos and sin each rounded once to fp32.
+extern "C" int kcr_rope_cos_sin_host(float* cos_tab, float* sin_tab, int64_t max_pos, int head_dim,
+                                     double theta) {
+    if (max_pos < 0 || head_dim < 2 || head_dim % 2 != 0 || !(theta > 0.0)) return KCR_ERR_SHAPE;
+    if (max_pos == 0) return KCR_OK;
+    if (!cos_tab || !sin_tab) return KCR_ERR_NULL;
+    const int half = head_dim / 2;
+    const int64_t n = max_pos * half;
+    if (overlap(span2d(cos_tab, 1, 0, n, 4), span2d(sin_tab, 1, 0, n, 4))) return KCR_ERR_ALIAS;
+    for (int i = 0; i < half; ++i) {
+        const double inv_freq = pow(theta, -2.0 * (double)i / (double)head_dim);
+        for (int64_t p = 0; p < max_pos; ++p) {
+            const double ang = (double)p * inv_freq;
+            cos_tab[p * half + i] = (float)cos(ang);
+            sin_tab[p * half + i] = (float)sin(ang);
+        }
+    }
+    return KCR_OK;
 }

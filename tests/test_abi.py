@@ -34,6 +34,7 @@ def lib():
     L.kcr_rope_kvstore.argtypes = [P, I64, I64, P, I64, I64, P, I64, I64, P, P, P, P, I64, P, P,
                                    I64, I, I, I, I, I64, I, P]
     L.kcr_rope_cos_sin.argtypes = [P, P, I64, I, D, P]
+    L.kcr_rope_cos_sin_host.argtypes = [P, P, I64, I, D]
     L.kcr_qknorm_rope_kvstore.argtypes = [P, I64, I64, P, I64, I64, P, I64, I64, P, P, F, P, P, P, P,
                                           I64, P, P, I64, I, I, I, I, I64, I, P]
     L.kcr_swiglu.argtypes = [P, I64, P, I64, P, I64, I64, I64, I, P]
@@ -241,3 +242,41 @@ def test_binding_refuses_missing_library(tmp_path):
     mod = importlib.util.module_from_spec(spec)
     with pytest.raises(ImportError):
         spec.loader.exec_module(mod)
+
+
+def test_rope_cos_sin_host_values(lib):
+    """The host table builder runs on the CPU: every entry is cos/sin of the
+    fp64 angle p * theta^(-2i/d) rounded once to fp32. Checked exactly
+    against Python's math module (the same fp64 operations) on a sample and
+    against numpy over the whole table to within one fp32 ulp."""
+    import math
+    import numpy as np
+    max_pos, hd, theta = 4097, 128, 1e6
+    half = hd // 2
+    c = np.empty((max_pos, half), dtype=np.float32)
+    s_ = np.empty_like(c)
+    assert lib.kcr_rope_cos_sin_host(c.ctypes.data, s_.ctypes.data, max_pos, hd, theta) == 0
+    assert np.all(c[0] == 1.0) and np.all(s_[0] == 0.0)          # position 0: the identity
+    for p in (1, 2, 37, 1000, 4096):
+        for i in (0, 1, 31, 63):
+            ang = p * math.pow(theta, -2.0 * i / hd)
+            assert c[p, i] == np.float32(math.cos(ang)) and s_[p, i] == np.float32(math.sin(ang)), (p, i)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * np.power(theta, -2.0 * np.arange(half) / hd)[None, :]
+    for got, ref in ((c, np.cos(ang).astype(np.float32)), (s_, np.sin(ang).astype(np.float32))):
+        ulp = np.abs(got.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+        assert ulp.max() <= 1 and (ulp > 0).mean() < 1e-4
+    assert np.allclose(c.astype(np.float64) ** 2 + s_.astype(np.float64) ** 2, 1.0, atol=3e-7)
+
+
+def test_rope_cos_sin_host_errors(lib):
+    import numpy as np
+    c = np.empty((8, 4), dtype=np.float32)
+    s_ = np.empty_like(c)
+    assert lib.kcr_rope_cos_sin_host(c.ctypes.data, s_.ctypes.data, -1, 8, 1e4) == SHAPE
+    assert lib.kcr_rope_cos_sin_host(c.ctypes.data, s_.ctypes.data, 8, 7, 1e4) == SHAPE
+    assert lib.kcr_rope_cos_sin_host(c.ctypes.data, s_.ctypes.data, 8, 8, 0.0) == SHAPE
+    assert lib.kcr_rope_cos_sin_host(c.ctypes.data, s_.ctypes.data, 8, 8, float("nan")) == SHAPE
+    assert lib.kcr_rope_cos_sin_host(None, s_.ctypes.data, 8, 8, 1e4) == NULL
+    assert lib.kcr_rope_cos_sin_host(c.ctypes.data, c.ctypes.data + 16, 8, 8, 1e4) == ALIAS
+    assert lib.kcr_rope_cos_sin_host(None, None, 0, 8, 1e4) == OK
+    assert lib.kcr_rope_cos_sin(None, None, 8, 8, -1.0, None) == SHAPE

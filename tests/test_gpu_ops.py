@@ -351,6 +351,13 @@ def test_rope_table(kcr):
             err = np.abs(got.cpu().double().numpy() - ref)
             # one fp32 rounding of an fp64 value (2^-24 relative) plus fp64 angle error
             assert np.all(err <= np.abs(ref) * 2.0 ** -24 + 1e-10), float(err.max())
+        # the host-built tables meet the same bound (their fp64 pow/cos/sin are
+        # the host's, which may differ from the device's in the last fp64 bit:
+        # an absolute error of up to ~1e-11 at position 70000, hence the floor)
+        ch, sh = kcr.rope_cos_sin_host(max_pos, dh, theta)
+        for got, ref in ((ch, c_ref), (sh, s_ref)):
+            err = np.abs(got.double().numpy() - ref)
+            assert np.all(err <= np.abs(ref) * 2.0 ** -24 + 1e-10), float(err.max())
 
 
 # ---------------------------------------------------------- paged KV gather
