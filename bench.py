@@ -469,11 +469,42 @@ def cpu_baseline_run(wl, bytes_per_step, budget_s: float):
         if el >= budget_s or el * (steps + 1) / steps > 3 * budget_s:
             break
     gbs = steps * bytes_per_step / el / 1e9
+    # the same oracle on one thread, over one layer-step slice (~1/16 of the time)
+    oracle.set_num_threads(1)
+    h1 = bits(wl["h"]).copy()
+    t1 = time.perf_counter()
+    n1 = 0
+    while True:
+        L = layers[n1 % len(layers)]
+        h1, _ = oracle.add_rmsnorm(h1, L["d_attn"], L["w_attn"], eps)
+        oracle.rope_kvstore(L["q"], L["k"], L["v"], pos, wl["theta"], cache, slots,
+                            block_size=wl["block_size"])
+        h1, _ = oracle.add_rmsnorm(h1, L["d_mlp"], L["w_mlp"], eps)
+        oracle.swiglu(L["gate"], L["up"])
+        n1 += 1
+        if time.perf_counter() - t1 >= budget_s / 4:
+            break
+    el1 = time.perf_counter() - t1
+    oracle.set_num_threads(threads)
+    gbs1 = n1 * (bytes_per_step / len(layers)) / el1 / 1e9
     return dict(value=round(gbs, 3), unit="GB/s", cores=threads, kind="oracle",
+                one_thread_value=round(gbs1, 3),
+                one_thread_sample=f"{n1} layer(s) of the same chain on 1 thread ({el1:.1f} s)",
+                cpu_model=cpu_model(),
                 sample=f"{steps} full step(s) of the same 28-layer, batch-256 chain "
                        f"({steps * 112} op calls, {el:.1f} s); one shared cache array stands in "
                        f"for the 28 per-layer caches (only the 256 named slots are touched)",
                 seconds=round(el, 2), ms_per_step=round(1e3 * el / steps, 1))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def pmc_pass():
