@@ -19,6 +19,7 @@ Prints ONE JSON line:
   kernels      each kernel at its large shape on cold, rotated buffers
   ceiling      1 GiB device copies: the library's copy kernel and hipMemcpy
   decode_token_b1  per-op latency of the batch-1 decode token
+  decode_chain_b1  the 28-layer chain at batch 1: graph of 112 launches vs one launch
 """
 from __future__ import annotations
 
@@ -377,6 +378,53 @@ def decode_token_latency(kcr, reps: int):
     return out
 
 
+def decode_chain_b1(kcr, reps: int):
+    """The 28-layer chain at batch 1 (the decode token of a single sequence
+    at position 4096): one step as a captured graph of the 112 separate
+    launches, and as the single launch of kcr_decode_chain_b1 (same ops,
+    same order, one workgroup), also replayed from a captured graph. Step
+    time from events over `reps` replays; the single launch's kernel
+    duration also from events stamped at its start and end."""
+    import torch
+    import workloads
+    from kv_cache_rmsnorm_amd.chain import DecodeChain
+    chain = DecodeChain(workloads.decode_chain(batch=1), "cuda", sentinel_cache=False)
+    nb = chain.bytes_per_step()["step"]
+    chain.capture()
+
+    def timed(fn):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = events(2)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    graph_us = timed(chain.step_graph)
+    chain.capture_b1()
+    one_us = timed(chain.graph_b1.replay)
+    ev = events(2)
+    samples = []
+    for _ in range(20):
+        kcr.time_next_launch(ev[0], ev[1])
+        chain.step_b1()
+        torch.cuda.synchronize()
+        samples.append(ev[0].elapsed_time(ev[1]) * 1e3)
+    res = dict(step_bytes=nb, graph_112_launches_us=round(graph_us, 2), one_launch_us=round(one_us, 2),
+               one_launch_kernel_median_us=round(statistics.median(samples), 2),
+               one_launch_gbs=round(nb / (one_us * 1e-6) / 1e9, 1),
+               speedup=round(graph_us / one_us, 2))
+    log(f"batch-1 chain: graph of 112 launches {graph_us:.1f} us/step, one launch {one_us:.1f} us/step "
+        f"({res['one_launch_gbs']} GB/s)")
+    del chain
+    torch.cuda.empty_cache()
+    return res
+
+
 def launch_floor(kcr, n_launch: int, reps: int):
     """Per-node time of a captured graph of n_launch minimal launches (a
     16-byte copy): what one graph node costs with (almost) no work."""
@@ -644,6 +692,7 @@ def main():
     chain.reset_residual()
     log("in-graph per-launch us: " + ", ".join(f"{k} {v:.2f}" for k, v in op_graph.items()))
     token = decode_token_latency(kcr, max(10, args.steps // 2))
+    chain_b1 = decode_chain_b1(kcr, max(20, args.steps))
     ceiling = copy_ceiling(kcr, args.kernel_iters)
     kernels = {} if args.skip_large else large_shapes(kcr, args.kernel_iters)
     sweep = {} if args.skip_sweep else rmsnorm_sweep(kcr, max(10, args.steps // 5))
@@ -681,6 +730,7 @@ def main():
         "op_event_stamped_mean_us": op_us,
         "op_in_graph_us": {k: round(v, 3) for k, v in op_graph.items()},
         "decode_token_b1": token,
+        "decode_chain_b1": chain_b1,
         "timed_wall_s": round(wall_s, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,

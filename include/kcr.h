@@ -315,6 +315,65 @@ int kcr_paged_kv_gather(const void* kv_cache, int64_t num_blocks, int block_size
                         void* v_out, int dtype, void* stream);
 
 /*
+ * kcr_decode_chain_b1 -- the whole per-layer chain of one batch-1 decode
+ * step in a single launch:
+ *
+ *   for each layer l < n_layers, in order:
+ *     h <- round(h + d_attn);  y_attn = rmsnorm(h) * w_attn      (kcr_add_rmsnorm)
+ *     rope + store of the token's q/k/v (from the layer's fused qkv) at
+ *       positions[0] into the layer's cache at slot_mapping[0]    (kcr_rope_kvstore)
+ *     h <- round(h + d_mlp);   y_mlp  = rmsnorm(h) * w_mlp       (kcr_add_rmsnorm)
+ *     act = silu(gate) * up, from the layer's fused gate_up     (kcr_swiglu)
+ *
+ * Each op is the one defined above (the koas-w.github.io 2026-03-31 post,
+ * sections 1, 2 and 4) and its results are those of the separate calls made
+ * in this order. One workgroup runs every op of every layer in turn with
+ * workgroup barriers only, keeping the residual h in registers; the
+ * launch-overhead elimination (one launch instead of four per layer) that
+ * m.lsln.cn/news/61269 section 4 seeks with CUDA Graph. Batch 1 only: the
+ * ops' GEMMs and attention (not part of this library) are not in between.
+ *
+ *   layers [n_layers]  HOST array of per-layer device pointers (read during
+ *        the call; 0 <= n_layers <= KCR_B1_MAX_LAYERS):
+ *          d_attn, w_attn, d_mlp, w_mlp [hidden]       inputs
+ *          y_attn, y_mlp [hidden]                      outputs
+ *          qkv [(n_head + 2 n_kv_head) * head_dim]     input, heads in that order
+ *          q_out [n_head * head_dim]                   output
+ *          kv_cache [2, num_blocks, block_size, n_kv_head, head_dim]  in/out
+ *          gate_up [2 * inter] (gate first)            input
+ *          act [inter]                                 output
+ *   h [hidden]                  device, input and output (the residual)
+ *   positions, slot_mapping [1] int64 device; cos_tab, sin_tab as for
+ *        kcr_rope_kvstore (slot < 0 or out of range: nothing stored)
+ *
+ * Limits (KCR_ERR_SHAPE): hidden and inter multiples of 16 bytes' worth of
+ * elements, hidden <= 1024 such vectors, inter <= 4096 of them, head_dim as
+ * for kcr_rope_kvstore with (n_head + 2 n_kv_head) heads of at most 1024
+ * lanes in all. Every pointer 16-byte aligned (KCR_ERR_ALIGN); outputs may
+ * not overlap the inputs of their layer or h (KCR_ERR_ALIAS).
+ */
+#define KCR_B1_MAX_LAYERS 32
+typedef struct kcr_chain_layer {
+    const void* d_attn;
+    const void* w_attn;
+    void* y_attn;
+    const void* qkv;
+    void* q_out;
+    void* kv_cache;
+    const void* d_mlp;
+    const void* w_mlp;
+    void* y_mlp;
+    const void* gate_up;
+    void* act;
+} kcr_chain_layer;
+
+int kcr_decode_chain_b1(const kcr_chain_layer* layers, int n_layers, void* h, int hidden,
+                        int inter, int n_head, int n_kv_head, int head_dim,
+                        const int64_t* positions, const int64_t* slot_mapping,
+                        const float* cos_tab, const float* sin_tab, int64_t max_pos,
+                        int block_size, int64_t num_blocks, float eps, int dtype, void* stream);
+
+/*
  * kcr_copy -- plain streaming copy of `bytes` bytes (a multiple of 16, both
  * pointers 16-byte aligned, no overlap). It moves data with the same 16-byte
  * vector loads and stores as the kernels above and serves as the measured

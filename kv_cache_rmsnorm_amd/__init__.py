@@ -49,6 +49,7 @@ _SIGS = {
     "kcr_clip_norm": [_P, _I64, _I64, _P, _I64, _I64, _I64, _I, _I, _P, _I, _P, _I, _F, _F, _I, _P],
     "kcr_paged_kv_gather": [_P, _I64, _I, _I, _I, _P, _I64, _P, _I64, _I64, _P, _P, _I, _P],
     "kcr_copy": [_P, _P, _I64, _P],
+    "kcr_decode_chain_b1": [_P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I64, _I, _I64, _F, _I, _P],
     "kcr_time_next_launch": [_P, _P],
     "kcr_device_cus": [],
     "kcr_selftest_host": [],
@@ -330,6 +331,76 @@ def paged_kv_gather(kv_cache: torch.Tensor, block_tables: torch.Tensor, seq_lens
         kv_cache.data_ptr(), nb, bs, hkv, hd, block_tables.data_ptr(), block_tables.shape[1],
         seq_lens.data_ptr(), n, max_len, k_out.data_ptr(), v_out.data_ptr(), dt, _stream(kv_cache)))
     return k_out, v_out
+
+
+class ChainLayer(ctypes.Structure):
+    """kcr_chain_layer: one layer's device pointers for decode_chain_b1."""
+    _fields_ = [(n, ctypes.c_void_p) for n in ("d_attn", "w_attn", "y_attn", "qkv", "q_out", "kv_cache",
+                                                "d_mlp", "w_mlp", "y_mlp", "gate_up", "act")]
+
+
+class DecodeChainB1:
+    """Marshalled arguments of kcr_decode_chain_b1 (one batch-1 decode
+    step's chain in one launch), checked and packed once; calling the object
+    launches the step on the current stream. `layers` is a list of dicts with
+    tensors d_attn, w_attn, y_attn, d_mlp, w_mlp, y_mlp [hidden],
+    qkv [(n_head + 2 n_kv_head) * head_dim], q_out [n_head, head_dim],
+    cache [2, blocks, block_size, n_kv_head, head_dim], gate_up [2 * inter],
+    act [inter] (a leading batch dimension of 1 is allowed); h [hidden] is
+    updated in place. The tensors must stay alive while the object is used."""
+
+    def __init__(self, layers: list, h: torch.Tensor, positions: torch.Tensor, slot_mapping: torch.Tensor,
+                 cos: torch.Tensor, sin: torch.Tensor, eps: float, n_head: int, n_kv_head: int):
+        hidden = h.shape[-1]
+        _expect(h.numel() == hidden and h.is_contiguous(), "h must be one contiguous row")
+        self.dt = _dt(h)
+        _expect(all(t.device == h.device for t in (positions, slot_mapping, cos, sin)),
+                "positions, slot_mapping and the tables must be on h's device")
+        n = len(layers)
+        _expect(0 <= n <= 32, "at most 32 layers")
+        _expect(cos.dim() == 2 and cos.dtype == torch.float32 and sin.dtype == torch.float32
+                and tuple(sin.shape) == tuple(cos.shape) and cos.is_contiguous() and sin.is_contiguous(),
+                "cos/sin must be contiguous float32 [max_pos, head_dim / 2]")
+        head_dim = cos.shape[1] * 2
+        _expect(positions.dtype == torch.int64 and slot_mapping.dtype == torch.int64
+                and positions.numel() == 1 and slot_mapping.numel() == 1,
+                "positions and slot_mapping must be int64 [1]")
+        self.table = (ChainLayer * max(n, 1))()
+        inter = nb = bs = 0
+        for i, L in enumerate(layers):
+            cache = L["cache"]
+            _expect(cache.dim() == 5 and cache.shape[0] == 2 and cache.shape[3] == n_kv_head
+                    and cache.shape[4] == head_dim and cache.is_contiguous() and cache.dtype == h.dtype
+                    and cache.device == h.device,
+                    "cache must be a contiguous [2, blocks, block_size, n_kv_head, head_dim] tensor like h")
+            if i and (cache.shape[1], cache.shape[2], L["act"].shape[-1]) != (nb, bs, inter):
+                raise ValueError("every layer must have the same cache shape and intermediate size")
+            nb, bs, inter = cache.shape[1], cache.shape[2], L["act"].shape[-1]
+            sizes = dict(d_attn=hidden, w_attn=hidden, y_attn=hidden, d_mlp=hidden, w_mlp=hidden,
+                         y_mlp=hidden, qkv=(n_head + 2 * n_kv_head) * head_dim, q_out=n_head * head_dim,
+                         gate_up=2 * inter, act=inter)
+            for name, size in sizes.items():
+                t = L[name]
+                _expect(t.numel() == size and t.is_contiguous() and t.dtype == h.dtype and t.device == h.device,
+                        f"layer {i} {name} must be a contiguous {size}-element tensor like h")
+            self.table[i] = ChainLayer(*[L[f].data_ptr() for f in ("d_attn", "w_attn", "y_attn", "qkv", "q_out")],
+                                       cache.data_ptr(),
+                                       *[L[f].data_ptr() for f in ("d_mlp", "w_mlp", "y_mlp", "gate_up", "act")])
+        self.h = h
+        self.args = (ctypes.cast(self.table, ctypes.c_void_p), n, h.data_ptr(), hidden, inter, n_head, n_kv_head,
+                     head_dim, positions.data_ptr(), slot_mapping.data_ptr(), cos.data_ptr(), sin.data_ptr(),
+                     cos.shape[0], bs, nb, float(eps), self.dt)
+        self.n = n
+
+    def __call__(self) -> None:
+        if self.n:
+            _check("decode_chain_b1", _lib.kcr_decode_chain_b1(*self.args, _stream(self.h)))
+
+
+def decode_chain_b1(layers: list, h: torch.Tensor, positions: torch.Tensor, slot_mapping: torch.Tensor,
+                    cos: torch.Tensor, sin: torch.Tensor, eps: float, n_head: int, n_kv_head: int) -> None:
+    """One call of kcr_decode_chain_b1 (see DecodeChainB1)."""
+    DecodeChainB1(layers, h, positions, slot_mapping, cos, sin, eps, n_head, n_kv_head)()
 
 
 def copy_(dst: torch.Tensor, src: torch.Tensor) -> torch.Tensor:

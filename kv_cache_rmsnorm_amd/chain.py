@@ -58,6 +58,8 @@ class DecodeChain:
                 q_out=torch.empty((B, hq, dh), dtype=wl["dtype"], device=dev),
                 act=torch.empty((B, self.inter), dtype=wl["dtype"], device=dev)))
         self.graph = None
+        self.graph_b1 = None
+        self._b1 = None
 
     def reset_residual(self):
         self.h.copy_(self.h0)
@@ -73,6 +75,29 @@ class DecodeChain:
     def step_eager(self):
         for L in self.layers:
             self.layer_ops(L)
+
+    def step_b1(self):
+        """Batch 1 only: the whole step's chain in one launch
+        (kcr_decode_chain_b1), same ops in the same order."""
+        if self._b1 is None:
+            self._b1 = kcr.DecodeChainB1(self.layers, self.h, self.positions, self.slot_mapping, self.cos,
+                                         self.sin, self.eps, self.hq, self.hkv)
+        self._b1()
+
+    def capture_b1(self):
+        """Capture the one-launch step into a HIP graph."""
+        s = torch.cuda.Stream(device=self.device)
+        s.wait_stream(torch.cuda.current_stream(self.device))
+        with torch.cuda.stream(s):
+            self.step_b1()
+        torch.cuda.current_stream(self.device).wait_stream(s)
+        torch.cuda.synchronize(self.device)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step_b1()
+        torch.cuda.synchronize(self.device)
+        self.graph_b1 = g
+        return g
 
     def capture(self):
         """Capture one step into a HIP graph (after one eager warm-up step on

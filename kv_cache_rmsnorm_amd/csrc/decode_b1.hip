@@ -1,0 +1,300 @@
+// decode_b1.hip -- the per-layer chain of one batch-1 decode step in a single
+// launch (kcr_decode_chain_b1): for every layer, in order, residual add +
+// RMSNorm (the koas-w.github.io 2026-03-31 post, section 4), RoPE + paged
+// store (section 1), residual add + RMSNorm, SwiGLU (section 2).
+//
+// gfx950 design
+//  * One workgroup of 1024 lanes runs every op of every layer in turn; ops
+//    are separated by workgroup barriers only, so the 4 launches per layer
+//    of the separate entry points (and their graph-node or host launch
+//    cost) become one launch per step.
+//  * The residual h lives in registers for the whole step: lane l owns
+//    16-byte vector l of the row, adds delta to it, stores the rounded sum
+//    (the in-place update of each add) and normalises it. The row's sum of
+//    squares is reduced in-wave with DPP, then across the 16 waves through
+//    two alternating LDS slot arrays (one barrier per norm).
+//  * Each layer's loads (both deltas and weights, the token's q/k/v chunks,
+//    the gate/up vectors) are issued together before its first op runs, so
+//    one memory latency per layer is exposed rather than one per op. The
+//    cos/sin rows of the token's position are the same for every layer and
+//    are read once.
+//  * RoPE lane mapping as in rope_kvstore.hip: a unit of LPU lanes per
+//    virtual head in KV-group order, lane c owning chunk c of both halves.
+#include "kcr_device.h"
+#include "kcr_host.h"
+
+namespace kcr {
+
+constexpr int kB1Threads = 1024;
+constexpr int kB1Waves = kB1Threads / 64;
+constexpr int kB1MaxSwigluIters = 4;  // inter <= 4096 vectors
+
+struct ChainB1Args {
+    kcr_chain_layer layers[KCR_B1_MAX_LAYERS];
+    void* h;
+    const int64_t* pos;
+    const int64_t* slots;
+    const float* cos_t;
+    const float* sin_t;
+    int64_t max_pos, n_slots;
+    int32_t n_layers, hidden, inter, hq, hkv, dh, group, lpu;
+    float eps;
+};
+
+// Sum over the workgroup's 1024 lanes, every lane gets the result. `slot`
+// alternates between the two norms of a layer: a lane rewrites slot s only
+// after passing the barrier of the other slot, which every lane reaches
+// after its last read of slot s.
+__device__ __forceinline__ float block_sum(float v, float (*part)[kB1Waves], int slot, int wave, int lane) {
+    v = wave_sum(v);
+    if (lane == 0) part[slot][wave] = v;
+    __syncthreads();
+    float t = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kB1Waves; ++i) t += part[slot][i];
+    return t;
+}
+
+template <typename T, int SWI>
+__global__ __launch_bounds__(kB1Threads) void decode_b1_kernel(const ChainB1Args a) {
+    using S = typename T::storage;
+    constexpr int kVec = T::kVec;
+    __shared__ float part[2][kB1Waves];
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+
+    // residual: lane tid owns vector tid of h
+    const int hv = a.hidden / kVec;
+    const bool own_h = tid < hv;
+    const int64_t he = (int64_t)tid * kVec;
+    const int64_t he_c = own_h ? he : 0;  // in-bounds load address for every lane
+    u32x4 hreg = ld16<T>(a.h, he_c);
+
+    // RoPE: unit = virtual head (KV-group order), lane c = chunk c of both halves
+    const int half = a.dh >> 1;
+    const int unit = tid / a.lpu, c = tid % a.lpu;
+    const int nvh = a.hkv * (a.group + 2);
+    const bool rope_on = unit < nvh && c * kVec < half;
+    const int g = rope_on ? unit / (a.group + 2) : 0;
+    const int r = rope_on ? unit - g * (a.group + 2) : 0;
+    const int kind = r < a.group ? 0 : (r == a.group ? 1 : 2);  // query, K, V
+    const int src_head = kind == 0 ? g * a.group + r : (kind == 1 ? a.hq + g : a.hq + a.hkv + g);
+    const int64_t c0 = rope_on ? (int64_t)c * kVec : 0;
+    const int64_t p = a.pos[0];
+    const int64_t slot = a.slots[0];
+    const bool p_ok = p >= 0 && p < a.max_pos;
+    const bool store_kv = p_ok && slot >= 0 && slot < a.n_slots;
+    float cs[kVec], sn[kVec];
+    if (rope_on) {
+        const float* cr = a.cos_t + (p_ok ? p : 0) * half + c0;
+        const float* sr = a.sin_t + (p_ok ? p : 0) * half + c0;
+#pragma unroll
+        for (int i = 0; i < kVec; i += 4) {
+            const u32x4 cv = *reinterpret_cast<const u32x4*>(cr + i);
+            const u32x4 sv = *reinterpret_cast<const u32x4*>(sr + i);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                cs[i + e] = __uint_as_float(cv[e]);
+                sn[i + e] = __uint_as_float(sv[e]);
+            }
+        }
+    }
+    const int iv = a.inter / kVec;
+
+    for (int l = 0; l < a.n_layers; ++l) {
+        const kcr_chain_layer& L = a.layers[l];
+        // Every load of the layer first, unconditionally: lanes with nothing to
+        // load read an in-bounds clamped address and ignore the result. In
+        // straight-line code the compiler waits for exactly the loads each op
+        // needs; loads under lane-dependent branches made it wait for all of
+        // them, and for earlier stores, before every op.
+        const u32x4 dA = ld16_nt<T>(L.d_attn, he_c);
+        const u32x4 wA = ld16<T>(L.w_attn, he_c);
+        const S* src = static_cast<const S*>(L.qkv) + (int64_t)src_head * a.dh;
+        const u32x4 x1 = ld16_nt<T>(src, c0);
+        const u32x4 x2 = ld16_nt<T>(src, half + c0);
+        const u32x4 dM = ld16_nt<T>(L.d_mlp, he_c);
+        const u32x4 wM = ld16<T>(L.w_mlp, he_c);
+        u32x4 gr[SWI], ur[SWI];
+#pragma unroll
+        for (int k = 0; k < SWI; ++k) {
+            const int v = tid + k * kB1Threads;
+            const int64_t e = v < iv ? (int64_t)v * kVec : 0;
+            gr[k] = ld16_nt<T>(L.gate_up, e);
+            ur[k] = ld16_nt<T>(L.gate_up, (int64_t)a.inter + e);
+        }
+        // The layer's output pointers, read while the loads are in flight
+        // (uniform; a per-lane choice between two fields of the argument
+        // block would be a vector load that every later wait must cover).
+        S* const q_out = static_cast<S*>(L.q_out);
+        S* const kv_cache = static_cast<S*>(L.kv_cache);
+        // Compiler-only barrier: keeps every load above issued here, ahead of
+        // the lane-dependent branches that use them (the compiler otherwise
+        // sinks a load into its only user and then waits for all loads).
+        asm volatile("" ::: "memory");
+
+        // 1. h <- round(h + d_attn); y_attn = rmsnorm(h) * w_attn
+        for (int n = 0; n < 2; ++n) {
+            const u32x4 dv = n == 0 ? dA : dM;
+            const u32x4 wv = n == 0 ? wA : wM;
+            float ss = 0.0f;
+            float xf[kVec];
+            if (own_h) {
+                float df[kVec];
+                unpack<T>(hreg, xf);
+                unpack<T>(dv, df);
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) xf[e] += df[e];
+                hreg = pack<T>(xf);
+                st16_nt<T>(a.h, he, hreg);
+                unpack<T>(hreg, xf);  // the rounded sum is what the norm sees
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) ss += xf[e] * xf[e];
+            }
+            const float tot = block_sum(ss, part, n, wave, lane);
+            if (own_h) {
+                const float rs = __builtin_amdgcn_rsqf(tot / (float)a.hidden + a.eps);
+                float wf[kVec], yf[kVec];
+                unpack<T>(wv, wf);
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) yf[e] = xf[e] * rs * wf[e];
+                st16_nt<T>(n == 0 ? L.y_attn : L.y_mlp, he, pack<T>(yf));
+            }
+            if (n == 1) break;
+
+            // 2. RoPE of the token's query and key heads, K_rot and V to the cache
+            if (rope_on && (kind == 0 || store_kv)) {
+                u32x4 o1 = x1, o2 = x2;
+                if (kind < 2 && p_ok) {
+                    float f1[kVec], f2[kVec], r1[kVec], r2[kVec];
+                    unpack<T>(x1, f1);
+                    unpack<T>(x2, f2);
+#pragma unroll
+                    for (int e = 0; e < kVec; ++e) {
+                        r1[e] = f1[e] * cs[e] - f2[e] * sn[e];
+                        r2[e] = f2[e] * cs[e] + f1[e] * sn[e];
+                    }
+                    o1 = pack<T>(r1);
+                    o2 = pack<T>(r2);
+                }
+                S* dst = kind == 0
+                             ? q_out + (int64_t)src_head * a.dh
+                             : kv_cache + (((int64_t)(kind - 1) * a.n_slots + slot) * a.hkv + g) * (int64_t)a.dh;
+                st16_nt<T>(dst, c0, o1);
+                st16_nt<T>(dst, half + c0, o2);
+            }
+        }
+
+        // 4. act = silu(gate) * up
+#pragma unroll
+        for (int k = 0; k < SWI; ++k) {
+            const int v = tid + k * kB1Threads;
+            if (v < iv) {
+                float gf[kVec], uf[kVec], of[kVec];
+                unpack<T>(gr[k], gf);
+                unpack<T>(ur[k], uf);
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) {
+                    const float ex = __builtin_amdgcn_exp2f(gf[e] * -1.4426950408889634f);
+                    of[e] = gf[e] * __builtin_amdgcn_rcpf(1.0f + ex) * uf[e];
+                }
+                st16_nt<T>(L.act, (int64_t)v * kVec, pack<T>(of));
+            }
+        }
+    }
+}
+
+template <typename T>
+static int launch_b1(const ChainB1Args& a, void* stream) {
+    const int iters = (a.inter / T::kVec + kB1Threads - 1) / kB1Threads;
+    switch (iters <= 1 ? 1 : (iters <= 2 ? 2 : 4)) {
+        case 1: return launch(decode_b1_kernel<T, 1>, dim3(1), dim3(kB1Threads), stream, a);
+        case 2: return launch(decode_b1_kernel<T, 2>, dim3(1), dim3(kB1Threads), stream, a);
+        default: return launch(decode_b1_kernel<T, kB1MaxSwigluIters>, dim3(1), dim3(kB1Threads), stream, a);
+    }
+}
+
+}  // namespace kcr
+
+using namespace kcr;
+
+extern "C" int kcr_decode_chain_b1(const kcr_chain_layer* layers, int n_layers, void* h, int hidden,
+                                   int inter, int n_head, int n_kv_head, int head_dim,
+                                   const int64_t* positions, const int64_t* slot_mapping,
+                                   const float* cos_tab, const float* sin_tab, int64_t max_pos,
+                                   int block_size, int64_t num_blocks, float eps, int dtype,
+                                   void* stream) {
+    if (!dtype_ok(dtype)) return KCR_ERR_DTYPE;
+    if (n_layers < 0 || n_layers > KCR_B1_MAX_LAYERS) return KCR_ERR_SHAPE;
+    if (n_kv_head < 1 || n_head < 1) return KCR_ERR_SHAPE;
+    if (n_head % n_kv_head != 0) return KCR_ERR_HEADS;
+    const size_t es = dtype_size(dtype);
+    const int vec = (int)(16 / es);
+    if (hidden < 1 || hidden % vec != 0 || hidden / vec > kB1Threads) return KCR_ERR_SHAPE;
+    if (inter < 1 || inter % vec != 0 || inter / vec > kB1MaxSwigluIters * kB1Threads) return KCR_ERR_SHAPE;
+    if (head_dim < 2 || head_dim % 2 != 0 || (head_dim / 2) % vec != 0 || head_dim > KCR_ROPE_MAX_HEAD_DIM)
+        return KCR_ERR_SHAPE;
+    if (block_size < 1 || num_blocks < 0 || max_pos < 1) return KCR_ERR_SHAPE;
+    const int group = n_head / n_kv_head;
+    int lpu = 1;
+    while (lpu * vec < head_dim / 2) lpu *= 2;
+    if ((int64_t)n_kv_head * (group + 2) * lpu > kB1Threads) return KCR_ERR_SHAPE;
+    if (n_layers == 0) return KCR_OK;
+    if (!layers || !h || !positions || !slot_mapping || !cos_tab || !sin_tab) return KCR_ERR_NULL;
+    if (!aligned16(h) || !aligned16(cos_tab) || !aligned16(sin_tab) ||
+        (reinterpret_cast<uintptr_t>(positions) & 7u) || (reinterpret_cast<uintptr_t>(slot_mapping) & 7u))
+        return KCR_ERR_ALIGN;
+
+    const int64_t n_slots = num_blocks * (int64_t)block_size;
+    const int64_t qkv_elems = (int64_t)(n_head + 2 * n_kv_head) * head_dim;
+    const Span sh = span2d(h, 1, 0, hidden, es);
+    const Span st = span2d(cos_tab, 1, 0, max_pos * (head_dim / 2), 4);
+    const Span ss = span2d(sin_tab, 1, 0, max_pos * (head_dim / 2), 4);
+    const Span sp = span2d(positions, 1, 0, 1, 8), sm = span2d(slot_mapping, 1, 0, 1, 8);
+    ChainB1Args a{};
+    for (int l = 0; l < n_layers; ++l) {
+        const kcr_chain_layer& L = layers[l];
+        const void* ptrs[] = {L.d_attn, L.w_attn, L.y_attn, L.qkv, L.q_out, L.d_mlp, L.w_mlp, L.y_mlp,
+                              L.gate_up, L.act};
+        for (const void* p : ptrs) {
+            if (!p) return KCR_ERR_NULL;
+            if (!aligned16(p)) return KCR_ERR_ALIGN;
+        }
+        if (!L.kv_cache && n_slots > 0) return KCR_ERR_NULL;
+        if (L.kv_cache && !aligned16(L.kv_cache)) return KCR_ERR_ALIGN;
+        const Span in[] = {span2d(L.d_attn, 1, 0, hidden, es), span2d(L.w_attn, 1, 0, hidden, es),
+                           span2d(L.qkv, 1, 0, qkv_elems, es), span2d(L.d_mlp, 1, 0, hidden, es),
+                           span2d(L.w_mlp, 1, 0, hidden, es), span2d(L.gate_up, 1, 0, 2 * (int64_t)inter, es),
+                           sh, st, ss, sp, sm};
+        const Span out[] = {span2d(L.y_attn, 1, 0, hidden, es),
+                            span2d(L.q_out, 1, 0, (int64_t)n_head * head_dim, es),
+                            span2d(L.kv_cache, 1, 0, 2 * n_slots * n_kv_head * (int64_t)head_dim, es),
+                            span2d(L.y_mlp, 1, 0, hidden, es), span2d(L.act, 1, 0, inter, es)};
+        constexpr int n_in = sizeof(in) / sizeof(in[0]), n_out = sizeof(out) / sizeof(out[0]);
+        for (int i = 0; i < n_out; ++i) {
+            for (int j = 0; j < n_in; ++j)
+                if (overlap(out[i], in[j])) return KCR_ERR_ALIAS;
+            for (int j = i + 1; j < n_out; ++j)
+                if (overlap(out[i], out[j])) return KCR_ERR_ALIAS;
+        }
+        a.layers[l] = L;
+    }
+    if (device_cus() <= 0) return KCR_ERR_DEVICE;
+    a.h = h;
+    a.pos = positions;
+    a.slots = slot_mapping;
+    a.cos_t = cos_tab;
+    a.sin_t = sin_tab;
+    a.max_pos = max_pos;
+    a.n_slots = n_slots;
+    a.n_layers = n_layers;
+    a.hidden = hidden;
+    a.inter = inter;
+    a.hq = n_head;
+    a.hkv = n_kv_head;
+    a.dh = head_dim;
+    a.group = group;
+    a.lpu = lpu;
+    a.eps = eps;
+    return by_dtype(dtype, [&](auto t) { return launch_b1<decltype(t)>(a, stream); });
+}

@@ -35,6 +35,7 @@ def lib():
                                    I64, I, I, I, I, I64, I, P]
     L.kcr_rope_cos_sin.argtypes = [P, P, I64, I, D, P]
     L.kcr_rope_cos_sin_host.argtypes = [P, P, I64, I, D]
+    L.kcr_decode_chain_b1.argtypes = [P, I, P, I, I, I, I, I, P, P, P, P, I64, I, I64, F, I, P]
     L.kcr_qknorm_rope_kvstore.argtypes = [P, I64, I64, P, I64, I64, P, I64, I64, P, P, F, P, P, P, P,
                                           I64, P, P, I64, I, I, I, I, I64, I, P]
     L.kcr_swiglu.argtypes = [P, I64, P, I64, P, I64, I64, I64, I, P]
@@ -280,3 +281,50 @@ def test_rope_cos_sin_host_errors(lib):
     assert lib.kcr_rope_cos_sin_host(c.ctypes.data, c.ctypes.data + 16, 8, 8, 1e4) == ALIAS
     assert lib.kcr_rope_cos_sin_host(None, None, 0, 8, 1e4) == OK
     assert lib.kcr_rope_cos_sin(None, None, 8, 8, -1.0, None) == SHAPE
+
+
+def test_decode_chain_b1_validation(lib):
+    """Host-side checks of the one-launch batch-1 chain: sizes, counts and the
+    layer table are refused before anything is launched (no device here, so
+    a call that passes every check reports DEVICE)."""
+    import ctypes
+    A = 1 << 20
+    f = lib.kcr_decode_chain_b1
+
+    class Layer(ctypes.Structure):
+        _fields_ = [(f"p{i}", ctypes.c_void_p) for i in range(11)]
+
+    def table(n, base=1 << 30, step=1 << 22):
+        arr = (Layer * n)()
+        for i in range(n):
+            arr[i] = Layer(*[base + (i * 11 + j) * step for j in range(11)])
+        return arr
+
+    H = 1 << 34  # far from every table pointer
+
+    def call(layers=None, n=2, h=H, hidden=1536, inter=8960, hq=12, hkv=2, hd=128, pos=H + A,
+             slot=H + A + 64, cos=H + 2 * A, sin=H + 8 * A, max_pos=4097, bs=16, nb=64, dt=BF16):
+        t = table(max(n, 1)) if layers is None else layers
+        return f(ctypes.cast(t, ctypes.c_void_p), n, h, hidden, inter, hq, hkv, hd, pos, slot, cos, sin,
+                 max_pos, bs, nb, 1e-6, dt, None)
+
+    assert call() == DEVICE
+    assert call(n=33) == SHAPE                       # more layers than the argument block holds
+    assert call(n=0, h=None) == OK                   # no work
+    assert call(hidden=1537) == SHAPE                # not whole 16-byte vectors
+    assert call(hidden=8 * 1025) == SHAPE            # more vectors than lanes
+    assert call(inter=8 * 4097) == SHAPE
+    assert call(hq=12, hkv=5) == HEADS
+    assert call(hd=120) == SHAPE                     # half a head not whole vectors
+    assert call(dt=7) == DTYPE
+    assert call(h=None) == NULL
+    assert call(h=H + 2) == ALIGN
+    bad = table(2)
+    bad[1].p3 = None                                 # layer 1 without qkv
+    assert call(layers=bad) == NULL
+    bad = table(2)
+    bad[0].p0 = (1 << 30) + 8                        # misaligned d_attn
+    assert call(layers=bad) == ALIGN
+    bad = table(2)
+    bad[0].p2 = bad[0].p0                            # y_attn on top of d_attn
+    assert call(layers=bad) == ALIAS

@@ -113,7 +113,32 @@ def test_config5_decode_chain_graph(kcr):
     torch.cuda.synchronize()
     chain.step_graph()
     torch.cuda.synchronize()
+    check_chain(wl, chain)
 
+
+def test_decode_chain_b1_one_launch(kcr):
+    """The batch-1 decode step's 28-layer chain in one launch
+    (kcr_decode_chain_b1) against the oracle run layer by layer, twice in a
+    row (the residual carries over)."""
+    from kv_cache_rmsnorm_amd.chain import DecodeChain
+    say("batch-1 decode chain, one launch")
+    wl = workloads.decode_chain(batch=1, seed=3)
+    chain = DecodeChain(wl, "cuda", sentinel_cache=True)
+    chain.step_b1()
+    torch.cuda.synchronize()
+    h_after = check_chain(wl, chain)
+    # a second step continues from the updated residual
+    for L in chain.layers:
+        L["cache"].view(torch.int16).fill_(-1)
+    wl2 = dict(wl, h=torch.from_numpy(h_after.view(np.int16).copy()).view(torch.bfloat16))
+    chain.step_b1()
+    torch.cuda.synchronize()
+    check_chain(wl2, chain)
+
+
+def check_chain(wl, chain):
+    """Every layer's outputs of one step of `chain` against the oracle run
+    layer by layer from wl["h"]; returns the oracle's final residual."""
     eps = f32eps(wl["eps"])
     hq, hkv, dh, inter = wl["hq"], wl["hkv"], wl["dh"], wl["inter"]
     h = np_bits(wl["h"]).copy()
@@ -140,6 +165,7 @@ def test_config5_decode_chain_graph(kcr):
         assert untouched == L["cache"].numel() - 2 * len(slots) * hkv * dh, f"layer {i} stray writes"
     # the residual after 56 fused adds is bit-exact
     assert np.array_equal(np_bits(chain.h.cpu()), h), "residual stream after the step"
+    return h
 
 
 def test_large_rmsnorm_sampled(kcr):
