@@ -110,3 +110,21 @@ def test_gather_shapes(kcr):
     with pytest.raises(ValueError):
         kcr.paged_kv_gather(cache, bt, lens, 8, v_out=t(2, 8, 2, 32)[..., :16])
     torch.cuda.synchronize()
+
+
+def test_decode_chain_b1_shapes(kcr):
+    import workloads
+    from kv_cache_rmsnorm_amd.chain import DecodeChain
+    wl = workloads.decode_chain(layers=2, batch=1, ctx=40, seed=1, hidden=256, inter=512, hq=4, hkv=2,
+                                dh=32, block_size=8)
+    chain = DecodeChain(wl, "cuda", sentinel_cache=False)
+    chain.step_b1()
+    args = (chain.h, chain.positions, chain.slot_mapping, chain.cos, chain.sin, chain.eps, chain.hq, chain.hkv)
+    for name, bad in (("act", t(1, 256)), ("q_out", t(1, 4, 16)), ("w_mlp", t(128)), ("qkv", t(1, 64))):
+        layers = [dict(L) for L in chain.layers]
+        layers[1][name] = bad
+        with pytest.raises(ValueError):
+            kcr.DecodeChainB1(layers, *args)
+    with pytest.raises(ValueError):
+        kcr.DecodeChainB1(chain.layers, chain.h, chain.positions.repeat(2), *args[2:])
+    torch.cuda.synchronize()

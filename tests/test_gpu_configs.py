@@ -130,15 +130,38 @@ def test_decode_chain_b1_one_launch(kcr):
     # a second step continues from the updated residual
     for L in chain.layers:
         L["cache"].view(torch.int16).fill_(-1)
-    wl2 = dict(wl, h=torch.from_numpy(h_after.view(np.int16).copy()).view(torch.bfloat16))
+    wl2 = dict(wl, h=bits_to_tensor(h_after, torch.bfloat16))
     chain.step_b1()
     torch.cuda.synchronize()
     check_chain(wl2, chain)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+def test_decode_chain_b1_dtypes_and_shapes(kcr, dt):
+    """The one-launch batch-1 chain in every dtype at other shapes: 5 layers,
+    hidden 512, intermediate 1408, 8 query / 2 KV heads of 64, block size 8."""
+    from kv_cache_rmsnorm_amd.chain import DecodeChain
+    say(f"batch-1 decode chain, one launch, {dt}")
+    wl = workloads.decode_chain(layers=5, batch=1, ctx=100, dtype=dt, seed=4, hidden=512, inter=1408,
+                                hq=8, hkv=2, dh=64, block_size=8)
+    chain = DecodeChain(wl, "cuda", sentinel_cache=True)
+    chain.step_b1()
+    torch.cuda.synchronize()
+    check_chain(wl, chain)
+
+
+def bits_to_tensor(bits: np.ndarray, dt) -> torch.Tensor:
+    """Inverse of np_bits: storage-convention numpy array -> CPU tensor."""
+    if dt == torch.bfloat16:
+        return torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16)
+    return torch.from_numpy(bits.copy())
+
+
 def check_chain(wl, chain):
     """Every layer's outputs of one step of `chain` against the oracle run
     layer by layer from wl["h"]; returns the oracle's final residual."""
+    dt = wl["dtype"]
+    ib = torch.int16 if dt.itemsize == 2 else torch.int32  # bit view; the sentinel is all ones
     eps = f32eps(wl["eps"])
     hq, hkv, dh, inter = wl["hq"], wl["hkv"], wl["dh"], wl["inter"]
     h = np_bits(wl["h"]).copy()
@@ -151,17 +174,17 @@ def check_chain(wl, chain):
                                            None, None)
         h, y_mlp = oracle.add_rmsnorm(h, np_bits(lw["d_mlp"]), np_bits(lw["w_mlp"]), eps)
         act = oracle.swiglu(np_bits(lw["gate_up"][:, :inter]), np_bits(lw["gate_up"][:, inter:]))
-        assert_close(L["y_attn"].cpu().double().numpy(), y_attn, torch.bfloat16, f"layer {i} y_attn")
-        assert_close(L["y_mlp"].cpu().double().numpy(), y_mlp, torch.bfloat16, f"layer {i} y_mlp")
-        assert_rope_close(L["q_out"].cpu().double().numpy(), q_rot, torch.bfloat16, f"layer {i} q_out")
-        assert_close(L["act"].cpu().double().numpy(), act, torch.bfloat16, f"layer {i} act")
+        assert_close(L["y_attn"].cpu().double().numpy(), y_attn, dt, f"layer {i} y_attn")
+        assert_close(L["y_mlp"].cpu().double().numpy(), y_mlp, dt, f"layer {i} y_mlp")
+        assert_rope_close(L["q_out"].cpu().double().numpy(), q_rot, dt, f"layer {i} q_out")
+        assert_close(L["act"].cpu().double().numpy(), act, dt, f"layer {i} act")
         # cache: the 256 named slots hold K_rot and V; every other slot the sentinel
         flat = L["cache"].view(2, n_slots, hkv, dh)
         s_dev = chain.slot_mapping
         k_got = flat[0][s_dev].cpu().double().numpy()
-        assert_rope_close(k_got, k_rot, torch.bfloat16, f"layer {i} K slots")
-        assert torch.equal(flat[1][s_dev].view(torch.int16).cpu(), v.contiguous().view(torch.int16))
-        untouched = int((L["cache"].view(torch.int16) == -1).sum())
+        assert_rope_close(k_got, k_rot, dt, f"layer {i} K slots")
+        assert torch.equal(flat[1][s_dev].view(ib).cpu(), v.contiguous().view(ib))
+        untouched = int((L["cache"].view(ib) == -1).sum())
         assert untouched == L["cache"].numel() - 2 * len(slots) * hkv * dh, f"layer {i} stray writes"
     # the residual after 56 fused adds is bit-exact
     assert np.array_equal(np_bits(chain.h.cpu()), h), "residual stream after the step"
