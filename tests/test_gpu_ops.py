@@ -157,14 +157,46 @@ def test_rmsnorm_tuned_in_place_strided(kcr):
 
 
 @pytest.mark.parametrize("dt", DTS, ids=DT_ID.get)
-def test_rmsnorm_many_rows_grid_stride(kcr, dt):
-    # more rows than the resident grid holds: every workgroup loops
+def test_rmsnorm_many_rows(kcr, dt):
+    # tens of thousands of one-pass workgroups; bf16 and fp16 stay in the
+    # small-call tier (32 MB streamed), fp32 takes the shape rule
     rows, d = 40000, 200
-    say(f"rmsnorm grid-stride rows={rows} dt={dt}")
+    say(f"rmsnorm many rows rows={rows} dt={dt}")
     wl = workloads.rmsnorm_rows(rows=rows, d=d, dtype=dt, seed=5)
     y = kcr.rmsnorm(dev(wl["x"]), dev(wl["w"]), wl["eps"])
     ref = oracle.rmsnorm(np_bits(wl["x"]), np_bits(wl["w"]), float(np.float32(wl["eps"])))
     assert_close(y.cpu().double().numpy(), ref, dt, "rmsnorm many rows")
+
+
+@pytest.mark.parametrize("add", [False, True], ids=["plain", "add"])
+def test_norm_launch_split(kcr, add):
+    # A grid holds at most 2^32 - 1 work-items, so a call with more rows than
+    # one launch covers is split into launches over consecutive row ranges.
+    # At one 16-byte vector per row that happens near 2^26 rows; the window
+    # checked here covers every row within 6000 of 2^26, the last rows, and a
+    # random sample.
+    rows, d = (1 << 26) + 6000, 8
+    say(f"norm launch split add={add} rows={rows} d={d}")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(31)
+    x = torch.randn((rows, d), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    w = (1 + 0.1 * torch.randn((d,), generator=g, device="cuda", dtype=torch.float32)).to(torch.bfloat16)
+    pick = torch.cat([torch.arange((1 << 26) - 6000, rows, device="cuda"),
+                      torch.randint(0, rows, (4000,), generator=g, device="cuda")])
+    x0 = x[pick].cpu()
+    eps = float(np.float32(1e-6))
+    if add:
+        dl = torch.randn((rows, d), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        y = kcr.add_rmsnorm(x, dl, w, eps)
+        x_ref, y_ref = oracle.add_rmsnorm(np_bits(x0), np_bits(dl[pick].cpu()), np_bits(w.cpu()), eps)
+        del dl
+        assert np.array_equal(np_bits(x[pick].cpu()).view(np.uint8), x_ref.view(np.uint8)), "residual"
+    else:
+        y = kcr.rmsnorm(x, w, eps)
+        y_ref = oracle.rmsnorm(np_bits(x0), np_bits(w.cpu()), eps)
+    assert_close(y[pick].cpu().double().numpy(), y_ref, torch.bfloat16, "rows around the split")
+    del x, y
+    torch.cuda.empty_cache()
 
 
 def test_rmsnorm_strided_and_in_place(kcr):
