@@ -165,33 +165,6 @@ __device__ __forceinline__ void st16_nt(void* base, int64_t elem, const u32x4& v
     __builtin_nontemporal_store(w, reinterpret_cast<u32x4_a4*>(static_cast<typename T::storage*>(base) + elem));
 }
 
-// Loads the vector that starts at element `elem` of a row of `n` elements:
-// a full 16-byte load when the whole vector is inside the row, element loads
-// for the `n - elem` (< kVec) valid elements of a ragged tail, zeros past the
-// end. Returns the floats in f[0..kVec).
-template <typename T, bool NT>
-__device__ __forceinline__ void load_vec(const void* base, int64_t elem, int64_t n, float* f) {
-    if (elem + T::kVec <= n) {
-        u32x4 v = NT ? ld16_nt<T>(base, elem) : ld16<T>(base, elem);
-        unpack<T>(v, f);
-    } else {
-#pragma unroll
-        for (int e = 0; e < T::kVec; ++e) f[e] = (elem + e < n) ? load_one<T>(base, elem + e) : 0.0f;
-    }
-}
-
-template <typename T, bool NT>
-__device__ __forceinline__ void store_vec(void* base, int64_t elem, int64_t n, const float* f) {
-    if (elem + T::kVec <= n) {
-        u32x4 v = pack<T>(f);
-        if (NT) st16_nt<T>(base, elem, v); else st16<T>(base, elem, v);
-    } else {
-#pragma unroll
-        for (int e = 0; e < T::kVec; ++e)
-            if (elem + e < n) store_one<T>(base, elem + e, f[e]);
-    }
-}
-
 // Raw-bit variants: the vector starting at element `elem` of a row of `n`
 // elements, as it sits in memory. `vec` says whether the row's base address
 // is dword aligned (vec_ok); when it is, every vector wholly inside the row
@@ -206,19 +179,72 @@ __host__ __device__ __forceinline__ bool vec_ok(const void* p) {
     return (reinterpret_cast<uintptr_t>(p) & 3u) == 0;
 }
 
-template <typename T, bool NT>
-__device__ __forceinline__ u32x4 load_raw(const void* base, int64_t elem, int64_t n, bool vec = true) {
-    if (vec && elem + T::kVec <= n) return NT ? ld16_nt<T>(base, elem) : ld16<T>(base, elem);
-    u32x4 v = {0u, 0u, 0u, 0u};
-    const typename T::storage* p = static_cast<const typename T::storage*>(base) + elem;
+// The elements [elem, min(elem + kVec, n)) one by one, zero bits past n.
+// Every element load is issued, from an in-bounds address (clamped to the
+// row's last element), before any is used.
+template <typename T>
+__device__ __forceinline__ u32x4 load_elems(const void* base, int64_t elem, int64_t n) {
+    const typename T::storage* p = static_cast<const typename T::storage*>(base);
+    uint32_t bits[T::kVec];
 #pragma unroll
     for (int e = 0; e < T::kVec; ++e) {
-        if (elem + e < n) {
-            if constexpr (T::kVec == 8) v[e >> 1] |= (uint32_t)p[e] << (16 * (e & 1));
-            else v[e] = __float_as_uint(p[e]);
-        }
+        const int64_t i = elem + e < n ? elem + e : n - 1;
+        if constexpr (T::kVec == 8) bits[e] = (uint32_t)p[i];
+        else bits[e] = __float_as_uint(p[i]);
+    }
+    u32x4 v = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < T::kVec; ++e) {
+        const uint32_t b = elem + e < n ? bits[e] : 0u;
+        if constexpr (T::kVec == 8) v[e >> 1] |= b << (16 * (e & 1));
+        else v[e] = b;
     }
     return v;
+}
+
+// EAGER (latency-bound calls): every load of a lane is in flight before any
+// is waited for. The result is zero bits in its registers before the vector
+// load is issued (the empty asm keeps the compiler from sinking the zeros
+// into the branches), so lanes past the end of the row write nothing; were
+// the zeros written on that path instead, they would overwrite the
+// destination of the vector load still in flight in other lanes, and the
+// compiler would wait there for every load in flight.
+//
+// Not EAGER (the throughput-bound large-call row-norm shapes, which were
+// tuned with it): lanes at or past the end of the row take the element path,
+// where the compiler waits for every load the wave has in flight before it
+// goes on, so each wave's requests are spaced out. Measured on MI355X, each
+// form wins its own regime: bf16 [131072, 2176] streams at 6.46-6.48 TB/s
+// this way against 6.31-6.33 eagerly, while a [512, 2176] bf16 call takes
+// 3.27 us per launch eagerly against 3.77 us this way (at widths with no
+// partial vector, such as [512, 2048], the zeroing moves cost about 0.05 us).
+template <typename T, bool NT, bool EAGER = true>
+__device__ __forceinline__ u32x4 load_raw(const void* base, int64_t elem, int64_t n, bool vec = true) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (!vec) {  // a row that is not dword aligned: element access throughout
+        if (elem < n) v = load_elems<T>(base, elem, n);
+        return v;
+    }
+    if constexpr (EAGER) {
+        asm volatile("" : "+v"(v));
+        if (elem + T::kVec <= n) {
+            v = NT ? ld16_nt<T>(base, elem) : ld16<T>(base, elem);
+        } else if (elem < n) {
+            v = load_elems<T>(base, elem, n);  // the vector that straddles the end
+        }
+        return v;
+    } else {
+        if (elem + T::kVec <= n) return NT ? ld16_nt<T>(base, elem) : ld16<T>(base, elem);
+        const typename T::storage* p = static_cast<const typename T::storage*>(base) + elem;
+#pragma unroll
+        for (int e = 0; e < T::kVec; ++e) {
+            if (elem + e < n) {
+                if constexpr (T::kVec == 8) v[e >> 1] |= (uint32_t)p[e] << (16 * (e & 1));
+                else v[e] = __float_as_uint(p[e]);
+            }
+        }
+        return v;
+    }
 }
 
 template <typename T, bool NT>

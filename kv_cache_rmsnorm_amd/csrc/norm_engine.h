@@ -54,10 +54,10 @@ __device__ __forceinline__ void* row_ptr(void* base, int64_t row, int64_t stride
 // per row, GROUPS row groups per workgroup, RPG rows per row group (all RPG
 // rows are read before any is written), nontemporal loads (NTL) and stores
 // (NTS) for the streamed rows.
-template <int VPT_, int WPR_, int GROUPS_, bool NTL_, bool NTS_, int RPG_ = 1>
+template <int VPT_, int WPR_, int GROUPS_, bool NTL_, bool NTS_, int RPG_ = 1, bool EAGER_ = false>
 struct NormCfg {
     static constexpr int VPT = VPT_, WPR = WPR_, GROUPS = GROUPS_, RPG = RPG_;
-    static constexpr bool NTL = NTL_, NTS = NTS_;
+    static constexpr bool NTL = NTL_, NTS = NTS_, EAGER = EAGER_;  // EAGER: see load_raw
     static constexpr int BLOCK = 64 * WPR * GROUPS;
 };
 
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(C::BLOCK) void row_norm_kernel(const NormArgs a) {
     const bool vw = VEC || vec_ok(a.w);
     u32x4 wr[VPT];
 #pragma unroll
-    for (int j = 0; j < VPT; ++j) wr[j] = load_raw<T, false>(a.w, (int64_t)(j * LANES + rl) * kVec, d, vw);
+    for (int j = 0; j < VPT; ++j) wr[j] = load_raw<T, false, C::EAGER>(a.w, (int64_t)(j * LANES + rl) * kVec, d, vw);
 
     // All RPG rows are read before any is written. `live[r]` is uniform per
     // row group; every wave reaches the barrier.
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(C::BLOCK) void row_norm_kernel(const NormArgs a) {
             vx[r] = VEC || vec_ok(xrow);  // row-uniform: vector or element access
 #pragma unroll
             for (int j = 0; j < VPT; ++j)
-                xr[r][j] = load_raw<T, C::NTL>(xrow, (int64_t)(j * LANES + rl) * kVec, d, vx[r]);
+                xr[r][j] = load_raw<T, C::NTL, C::EAGER>(xrow, (int64_t)(j * LANES + rl) * kVec, d, vx[r]);
         }
     }
     if constexpr (ADD) {
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(C::BLOCK) void row_norm_kernel(const NormArgs a) {
             const bool vd = VEC || vec_ok(drow);
 #pragma unroll
             for (int j = 0; j < VPT; ++j)
-                dr[r][j] = load_raw<T, C::NTL>(drow, (int64_t)(j * LANES + rl) * kVec, d, vd);
+                dr[r][j] = load_raw<T, C::NTL, C::EAGER>(drow, (int64_t)(j * LANES + rl) * kVec, d, vd);
         }
 #pragma unroll
         for (int r = 0; r < RPG; ++r) {
@@ -412,18 +412,19 @@ static int launch_unaligned(const NormArgs& a, void* stream) {
 // launches) this takes the step from 341 to 335 us against the two-group
 // shapes that win at large shapes. Loads and stores stay nontemporal: cached
 // ones measured 20-34 us slower per step there, since every kernel must
-// write its dirty L2 lines back before the next one starts.
+// write its dirty L2 lines back before the next one starts. Small calls are
+// latency-bound and issue every load before waiting (EAGER, load_raw).
 template <typename T, bool ADD, int WPR>
 static int launch_small_w(const NormArgs& a, void* stream, int vpt) {
     switch (vpt) {
-        case 1: return launch_norm<T, NormCfg<1, WPR, 1, true, true>, ADD>(a, stream);
-        case 2: return launch_norm<T, NormCfg<2, WPR, 1, true, true>, ADD>(a, stream);
-        case 3: return launch_norm<T, NormCfg<3, WPR, 1, true, true>, ADD>(a, stream);
-        case 4: return launch_norm<T, NormCfg<4, WPR, 1, true, true>, ADD>(a, stream);
-        case 5: return launch_norm<T, NormCfg<5, WPR, 1, true, true>, ADD>(a, stream);
-        case 6: return WPR == 8 ? launch_norm<T, NormCfg<6, WPR, 1, true, true>, ADD>(a, stream) : KCR_ERR_SHAPE;
-        case 7: return WPR == 8 ? launch_norm<T, NormCfg<7, WPR, 1, true, true>, ADD>(a, stream) : KCR_ERR_SHAPE;
-        case 8: return WPR == 8 ? launch_norm<T, NormCfg<8, WPR, 1, true, true>, ADD>(a, stream) : KCR_ERR_SHAPE;
+        case 1: return launch_norm<T, NormCfg<1, WPR, 1, true, true, 1, true>, ADD>(a, stream);
+        case 2: return launch_norm<T, NormCfg<2, WPR, 1, true, true, 1, true>, ADD>(a, stream);
+        case 3: return launch_norm<T, NormCfg<3, WPR, 1, true, true, 1, true>, ADD>(a, stream);
+        case 4: return launch_norm<T, NormCfg<4, WPR, 1, true, true, 1, true>, ADD>(a, stream);
+        case 5: return launch_norm<T, NormCfg<5, WPR, 1, true, true, 1, true>, ADD>(a, stream);
+        case 6: return WPR == 8 ? launch_norm<T, NormCfg<6, WPR, 1, true, true, 1, true>, ADD>(a, stream) : KCR_ERR_SHAPE;
+        case 7: return WPR == 8 ? launch_norm<T, NormCfg<7, WPR, 1, true, true, 1, true>, ADD>(a, stream) : KCR_ERR_SHAPE;
+        case 8: return WPR == 8 ? launch_norm<T, NormCfg<8, WPR, 1, true, true, 1, true>, ADD>(a, stream) : KCR_ERR_SHAPE;
     }
     return KCR_ERR_SHAPE;
 }
