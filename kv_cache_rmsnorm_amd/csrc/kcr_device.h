@@ -202,23 +202,25 @@ __device__ __forceinline__ u32x4 load_elems(const void* base, int64_t elem, int6
     return v;
 }
 
-// EAGER (latency-bound calls): every load of a lane is in flight before any
-// is waited for. The result is zero bits in its registers before the vector
-// load is issued (the empty asm keeps the compiler from sinking the zeros
-// into the branches), so lanes past the end of the row write nothing; were
-// the zeros written on that path instead, they would overwrite the
-// destination of the vector load still in flight in other lanes, and the
-// compiler would wait there for every load in flight.
+// EAGER (latency-bound row-norm calls whose shape leaves lanes past the
+// row's end): every load of a lane is in flight before any is waited for.
+// The result is zero bits in its registers before the vector load is issued
+// (the empty asm keeps the compiler from sinking the zeros into the
+// branches), so lanes past the end of the row write nothing. Were the zeros
+// written on that path instead, they would overwrite the destination of the
+// vector load still in flight in other lanes, and the compiler would wait
+// there for every load in flight.
 //
-// Not EAGER (the throughput-bound large-call row-norm shapes, which were
-// tuned with it): lanes at or past the end of the row take the element path,
-// where the compiler waits for every load the wave has in flight before it
-// goes on, so each wave's requests are spaced out. Measured on MI355X, each
-// form wins its own regime: bf16 [131072, 2176] streams at 6.46-6.48 TB/s
-// this way against 6.31-6.33 eagerly, while a [512, 2176] bf16 call takes
-// 3.27 us per launch eagerly against 3.77 us this way (at widths with no
-// partial vector, such as [512, 2048], the zeroing moves cost about 0.05 us).
-template <typename T, bool NT, bool EAGER = true>
+// Not EAGER (every other caller, and the throughput-bound large-call
+// row-norm shapes, which were tuned with it): lanes at or past the end of
+// the row take the element path, where the compiler waits for every load
+// the wave has in flight before it goes on, so each wave's requests are
+// spaced out. Measured on MI355X, each form wins its own regime: bf16
+// [131072, 2176] streams at 6.46-6.48 TB/s this way against 6.31-6.33
+// eagerly, while a [512, 2176] bf16 call takes 3.27 us per launch eagerly
+// against 3.77 us this way. Where every lane holds a whole vector the eager
+// form only adds the zeroing moves (about 0.05 us at [512, 2048]).
+template <typename T, bool NT, bool EAGER = false>
 __device__ __forceinline__ u32x4 load_raw(const void* base, int64_t elem, int64_t n, bool vec = true) {
     u32x4 v = {0u, 0u, 0u, 0u};
     if (!vec) {  // a row that is not dword aligned: element access throughout

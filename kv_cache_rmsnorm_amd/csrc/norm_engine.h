@@ -413,33 +413,49 @@ static int launch_unaligned(const NormArgs& a, void* stream) {
 // shapes that win at large shapes. Loads and stores stay nontemporal: cached
 // ones measured 20-34 us slower per step there, since every kernel must
 // write its dirty L2 lines back before the next one starts. Small calls are
-// latency-bound and issue every load before waiting (EAGER, load_raw).
-template <typename T, bool ADD, int WPR>
+// latency-bound: where the shape leaves lanes past the row's end, they issue
+// every load before waiting (EAGER, load_raw); where every lane holds a whole
+// vector, the plain form saves the zeroing moves.
+template <typename T, bool ADD, int WPR, bool EAGER>
 static int launch_small_w(const NormArgs& a, void* stream, int vpt) {
     switch (vpt) {
-        case 1: return launch_norm<T, NormCfg<1, WPR, 1, true, true, 1, true>, ADD>(a, stream);
-        case 2: return launch_norm<T, NormCfg<2, WPR, 1, true, true, 1, true>, ADD>(a, stream);
-        case 3: return launch_norm<T, NormCfg<3, WPR, 1, true, true, 1, true>, ADD>(a, stream);
-        case 4: return launch_norm<T, NormCfg<4, WPR, 1, true, true, 1, true>, ADD>(a, stream);
-        case 5: return launch_norm<T, NormCfg<5, WPR, 1, true, true, 1, true>, ADD>(a, stream);
-        case 6: return WPR == 8 ? launch_norm<T, NormCfg<6, WPR, 1, true, true, 1, true>, ADD>(a, stream) : KCR_ERR_SHAPE;
-        case 7: return WPR == 8 ? launch_norm<T, NormCfg<7, WPR, 1, true, true, 1, true>, ADD>(a, stream) : KCR_ERR_SHAPE;
-        case 8: return WPR == 8 ? launch_norm<T, NormCfg<8, WPR, 1, true, true, 1, true>, ADD>(a, stream) : KCR_ERR_SHAPE;
+        case 1: return launch_norm<T, NormCfg<1, WPR, 1, true, true, 1, EAGER>, ADD>(a, stream);
+        case 2: return launch_norm<T, NormCfg<2, WPR, 1, true, true, 1, EAGER>, ADD>(a, stream);
+        case 3: return launch_norm<T, NormCfg<3, WPR, 1, true, true, 1, EAGER>, ADD>(a, stream);
+        case 4: return launch_norm<T, NormCfg<4, WPR, 1, true, true, 1, EAGER>, ADD>(a, stream);
+        case 5: return launch_norm<T, NormCfg<5, WPR, 1, true, true, 1, EAGER>, ADD>(a, stream);
+        case 6: return WPR == 8 ? launch_norm<T, NormCfg<6, WPR, 1, true, true, 1, EAGER>, ADD>(a, stream) : KCR_ERR_SHAPE;
+        case 7: return WPR == 8 ? launch_norm<T, NormCfg<7, WPR, 1, true, true, 1, EAGER>, ADD>(a, stream) : KCR_ERR_SHAPE;
+        case 8: return WPR == 8 ? launch_norm<T, NormCfg<8, WPR, 1, true, true, 1, EAGER>, ADD>(a, stream) : KCR_ERR_SHAPE;
     }
     return KCR_ERR_SHAPE;
 }
 
 template <typename T, bool ADD>
 static int launch_small(const NormArgs& a, void* stream, const NormShape& s) {
+    const int64_t nvec = (a.d + T::kVec - 1) / T::kVec;
+    if ((int64_t)s.vpt * 64 * s.wpr > nvec) {
+        switch (s.wpr) {
+            case 1: return launch_small_w<T, ADD, 1, true>(a, stream, s.vpt);
+            case 2: return launch_small_w<T, ADD, 2, true>(a, stream, s.vpt);
+            case 3: return launch_small_w<T, ADD, 3, true>(a, stream, s.vpt);
+            case 4: return launch_small_w<T, ADD, 4, true>(a, stream, s.vpt);
+            case 5: return launch_small_w<T, ADD, 5, true>(a, stream, s.vpt);
+            case 6: return launch_small_w<T, ADD, 6, true>(a, stream, s.vpt);
+            case 7: return launch_small_w<T, ADD, 7, true>(a, stream, s.vpt);
+            case 8: return launch_small_w<T, ADD, 8, true>(a, stream, s.vpt);
+        }
+        return KCR_ERR_SHAPE;
+    }
     switch (s.wpr) {
-        case 1: return launch_small_w<T, ADD, 1>(a, stream, s.vpt);
-        case 2: return launch_small_w<T, ADD, 2>(a, stream, s.vpt);
-        case 3: return launch_small_w<T, ADD, 3>(a, stream, s.vpt);
-        case 4: return launch_small_w<T, ADD, 4>(a, stream, s.vpt);
-        case 5: return launch_small_w<T, ADD, 5>(a, stream, s.vpt);
-        case 6: return launch_small_w<T, ADD, 6>(a, stream, s.vpt);
-        case 7: return launch_small_w<T, ADD, 7>(a, stream, s.vpt);
-        case 8: return launch_small_w<T, ADD, 8>(a, stream, s.vpt);
+        case 1: return launch_small_w<T, ADD, 1, false>(a, stream, s.vpt);
+        case 2: return launch_small_w<T, ADD, 2, false>(a, stream, s.vpt);
+        case 3: return launch_small_w<T, ADD, 3, false>(a, stream, s.vpt);
+        case 4: return launch_small_w<T, ADD, 4, false>(a, stream, s.vpt);
+        case 5: return launch_small_w<T, ADD, 5, false>(a, stream, s.vpt);
+        case 6: return launch_small_w<T, ADD, 6, false>(a, stream, s.vpt);
+        case 7: return launch_small_w<T, ADD, 7, false>(a, stream, s.vpt);
+        case 8: return launch_small_w<T, ADD, 8, false>(a, stream, s.vpt);
     }
     return KCR_ERR_SHAPE;
 }
