@@ -167,7 +167,8 @@ int kcr_add_rmsnorm(void* x, int64_t x_stride, const void* delta, int64_t delta_
  * head_dim is even, head_dim/2 is a multiple of 16 bytes' worth of elements
  * (8 bf16, 4 fp32), head_dim <= KCR_ROPE_MAX_HEAD_DIM, n_kv_head >= 1,
  * block_size >= 1, num_blocks >= 0, max_pos >= 1; KCR_ERR_ALIAS when q_out
- * overlaps k, v, the tables or the cache, or the cache overlaps q, k or v.
+ * overlaps k, v, the tables, positions, slot_mapping or the cache, or the
+ * cache overlaps q, k, v, the tables, positions or slot_mapping.
  */
 int kcr_rope_kvstore(const void* q, int64_t q_tok_stride, int64_t q_head_stride,
                      const void* k, int64_t k_tok_stride, int64_t k_head_stride,

@@ -322,11 +322,13 @@ static int rope_prepare(const void* q, int64_t q_tok_stride, int64_t q_head_stri
     const Span sc = span2d(kv_cache, 1, 0, 2 * n_slots * n_kv_head * (int64_t)head_dim, es);
     const Span st = span2d(cos_tab, 1, 0, max_pos * (head_dim / 2), 4);
     const Span ss = span2d(sin_tab, 1, 0, max_pos * (head_dim / 2), 4);
+    const Span sp = span2d(positions, 1, 0, T, 8), sl = span2d(slot_mapping, 1, 0, T, 8);
     const bool q_contig = q_head_stride == head_dim && q_tok_stride == (int64_t)n_head * head_dim;
     const bool in_place = q == q_out && q_contig;
     if ((!in_place && overlap(so, sq)) || overlap(so, sk) || overlap(so, sv) || overlap(so, sc) ||
-        overlap(so, st) || overlap(so, ss) || overlap(sc, sq) || overlap(sc, sk) || overlap(sc, sv) ||
-        overlap(sc, st) || overlap(sc, ss))
+        overlap(so, st) || overlap(so, ss) || overlap(so, sp) || overlap(so, sl) || overlap(sc, sq) ||
+        overlap(sc, sk) || overlap(sc, sv) || overlap(sc, st) || overlap(sc, ss) || overlap(sc, sp) ||
+        overlap(sc, sl))
         return KCR_ERR_ALIAS;
     if (device_cus() <= 0) return KCR_ERR_DEVICE;
 

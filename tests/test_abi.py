@@ -130,6 +130,8 @@ def test_rope_validation(lib):
     assert _rope(lib, pos=A * 9 + 4) == ALIGN
     assert _rope(lib, qo=A + 64) == ALIAS        # q_out inside q's fused buffer
     assert _rope(lib, cache=A) == ALIAS          # cache over the inputs
+    assert _rope(lib, pos=A * 8 + 64) == ALIAS   # positions inside q_out
+    assert _rope(lib, slots=A * 16 + 1024) == ALIAS  # slot_mapping inside the cache
     # contiguous q may be rotated in place
     assert _rope(lib, qts=12 * 128, k=A * 3, kts=2 * 128, v=A * 4, vts=2 * 128,
                  qo=A) in (DEVICE, OK)
