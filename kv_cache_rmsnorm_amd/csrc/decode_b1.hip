@@ -61,7 +61,6 @@ __global__ __launch_bounds__(kB1Threads) void decode_b1_kernel(const ChainB1Args
     constexpr int kVec = T::kVec;
     __shared__ float part[2][kB1Waves];
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-    const u32x4 zero = {0u, 0u, 0u, 0u};
 
     // residual: lane tid owns vector tid of h
     const int hv = a.hidden / kVec;
