@@ -613,7 +613,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--kernel-iters", type=int, default=30)
+    ap.add_argument("--kernel-iters", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--skip-large", action="store_true", help="skip the per-kernel large shapes")
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
