@@ -363,6 +363,9 @@ static int launch_tuned(const NormArgs& a, void* stream) {
         }
     } else {
         if (a.d == 1024) return launch_norm<T, NormCfg<1, 4, 1, true, true, 1>, false>(a, stream);
+        // 2 waves x 5 vectors, 4 rows per workgroup: 6.25-6.28 TB/s at
+        // [131072, 2176] against 6.17-6.20 for the rule's 3 x 3 shape.
+        if (a.d == 2176) return launch_norm<T, NormCfg<5, 2, 4, true, true, 1>, false>(a, stream);
     }
     return 1;  // not in the table
 }

@@ -131,7 +131,7 @@ def test_rmsnorm_wide_row_loop(kcr):
 # rows leave the last group half empty.
 TUNED = [(torch.bfloat16, 1536), (torch.bfloat16, 2048), (torch.bfloat16, 2176),
          (torch.bfloat16, 4096), (torch.bfloat16, 5120), (torch.float16, 2176),
-         (torch.float16, 4096), (torch.float32, 1024)]
+         (torch.float16, 4096), (torch.float32, 1024), (torch.float32, 2176)]
 
 
 @pytest.mark.parametrize("dt,d", TUNED, ids=lambda v: DT_ID.get(v, str(v)))
