@@ -15,6 +15,12 @@ Ops (names as in the C ABI):
   swiglu(gate, up)                         silu(gate) * up
   rope_cos_sin(max_pos, head_dim, theta)   fp32 cos/sin tables built on the device
   rope_cos_sin_host(max_pos, head_dim, theta)  the same tables built on the host
+  qknorm_rope_kvstore(q, k, v, wq, wk, eps, ...)  per-head Q/K RMSNorm, then rope_kvstore
+  reglu(gate, up)                          relu(gate) * up
+  clip_norm(x, alpha, gamma, lo, hi)       clamp(alpha * x, lo, hi) * gamma (DyHT)
+  paged_kv_gather(kv_cache, block_tables, seq_lens, max_len)
+                                           K, V of each sequence, read back from the cache
+  DecodeChainB1(layers, h, ...)            batch-1 decode chain of every layer in one launch
 """
 from __future__ import annotations
 
