@@ -116,6 +116,52 @@ def test_config5_decode_chain_graph(kcr):
     check_chain(wl, chain)
 
 
+def _chain_outputs(chain):
+    """Bit views of everything one step writes: each layer's y_attn, q_out,
+    y_mlp and act, the K/V cache rows at the step's slots, and h."""
+    slots = chain.slot_mapping
+    out = []
+    for L in chain.layers:
+        cache = L["cache"]
+        rows = cache.view(2, -1, *cache.shape[3:])[:, slots]
+        for t in (L["y_attn"], L["q_out"], L["y_mlp"], L["act"], rows):
+            out.append(t.clone())
+    out.append(chain.h.clone())
+    return out
+
+
+def _reset_chain(chain):
+    for L in chain.layers:
+        L["cache"].view(torch.int16 if L["cache"].element_size() == 2 else torch.int32).fill_(-1)
+    chain.reset_residual()
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("batch", [256, 1], ids=["b256_graph_of_112", "b1_one_launch"])
+def test_graph_replays_match_eager(kcr, batch):
+    """A captured step replayed three times, with eager work (cache and
+    residual resets) and synchronizations between the replays: every replay
+    writes the same bits as the eager step."""
+    from kv_cache_rmsnorm_amd.chain import DecodeChain
+    say(f"graph replays against the eager step, batch {batch}")
+    wl = workloads.decode_chain(batch=batch, seed=7)
+    chain = DecodeChain(wl, "cuda", sentinel_cache=True)
+    eager = chain.step_eager if batch > 1 else chain.step_b1
+    (chain.capture if batch > 1 else chain.capture_b1)()
+    replay = chain.graph.replay if batch > 1 else chain.graph_b1.replay
+    _reset_chain(chain)
+    eager()
+    torch.cuda.synchronize()
+    ref = _chain_outputs(chain)
+    for rep in range(3):
+        _reset_chain(chain)
+        replay()
+        torch.cuda.synchronize()
+        got = _chain_outputs(chain)
+        for i, (a, b) in enumerate(zip(ref, got)):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep}: output {i} differs"
+
+
 def test_decode_chain_b1_one_launch(kcr):
     """The batch-1 decode step's 28-layer chain in one launch
     (kcr_decode_chain_b1) against the oracle run layer by layer, twice in a
