@@ -53,6 +53,24 @@ MUTANTS = {
     "f16_truncates": ("double r = rint(a / q) * q;", "double r = floor(a / q) * q;"),
     "f16_overflow_at_max": ("if (a >= 65520.0) return", "if (a >= 65504.0) return"),
     "gqa_modulo": ("return h / (hq / hkv);", "return h % hkv;"),
+    "add_norm_of_exact_sum": (
+        "            store(x, r * x_stride + j, s, dtype);\n"
+        "        }\n"
+        "        rmsnorm_row(x, r * x_stride, w, y + r * y_stride, d, eps, dtype);",
+        "            store(x, r * x_stride + j, s, dtype);\n"
+        "            y[r * y_stride + j] = s;\n"
+        "        }\n"
+        "        {\n"
+        "            double ss_ = 0.0;\n"
+        "            for (int64_t j = 0; j < d; ++j) ss_ += y[r * y_stride + j] * y[r * y_stride + j];\n"
+        "            for (int64_t j = 0; j < d; ++j)\n"
+        "                y[r * y_stride + j] *= load(w, j, dtype) / sqrt(ss_ / (double)d + eps);\n"
+        "        }"),
+    "swiglu_sigmoid_of_up": ("double sigmoid = 1.0 / (1.0 + exp(-g));", "double sigmoid = 1.0 / (1.0 + exp(-u));"),
+    "gather_reads_other_half": ("((((int64_t)which * num_blocks", "((((int64_t)(1 - which) * num_blocks"),
+    "clip_lower_bound_missing": ("                if (v < lo) v = lo;\n", ""),
+    "rope_position_off_by_one": ("int64_t p = positions[t];\n        for (int h = 0; h < hq; ++h)\n            rope_head(q",
+                                 "int64_t p = positions[t] + 1;\n        for (int h = 0; h < hq; ++h)\n            rope_head(q"),
     "gather_offset_from_block": ("int64_t block = block_table[t / block_size], offset = t % block_size;",
                                  "int64_t block = block_table[t / block_size], offset = (t + 1) % block_size;"),
 }
