@@ -71,6 +71,19 @@ MUTANTS = {
     "clip_lower_bound_missing": ("                if (v < lo) v = lo;\n", ""),
     "rope_position_off_by_one": ("int64_t p = positions[t];\n        for (int h = 0; h < hq; ++h)\n            rope_head(q",
                                  "int64_t p = positions[t] + 1;\n        for (int h = 0; h < hq; ++h)\n            rope_head(q"),
+    "silu_missing_g": ("out[r * out_stride + c] = g * sigmoid * u;", "out[r * out_stride + c] = sigmoid * u;"),
+    "clip_alpha_after_clamp": ("                double v = a * load(x, t * x_ts + h * x_hs + e, dtype);\n"
+                               "                if (v < lo) v = lo;\n"
+                               "                if (v > hi) v = hi;\n"
+                               "                y[(t * n_head + h) * d + e] = v * g;",
+                               "                double v = load(x, t * x_ts + h * x_hs + e, dtype);\n"
+                               "                if (v < lo) v = lo;\n"
+                               "                if (v > hi) v = hi;\n"
+                               "                y[(t * n_head + h) * d + e] = a * v * g;"),
+    "qknorm_mean_over_half": ("double r = 1.0 / sqrt(sum_sq / (double)d + eps);",
+                              "double r = 1.0 / sqrt(sum_sq / (double)(d / 2) + eps);"),
+    "scatter_offset_swapped": ("int64_t block = slot / block_size, offset = slot % block_size;",
+                               "int64_t block = slot % block_size, offset = slot / block_size;"),
     "gather_offset_from_block": ("int64_t block = block_table[t / block_size], offset = t % block_size;",
                                  "int64_t block = block_table[t / block_size], offset = (t + 1) % block_size;"),
 }
