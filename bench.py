@@ -15,7 +15,9 @@ Prints ONE JSON line:
                bytes per launch / its mean duration, measured with events
                stamped at kernel start and end (hipExtLaunchKernel) in whole
                steps that run back to back behind graph replays
-  cpu_baseline the CPU fp64 oracle on a bounded sample of the same workload
+  cpu_baseline the CPU fp64 oracle on a bounded sample of the same workload;
+               per_config: the oracle at each parity-shape config, with
+               every oracle thread and with one
   kernels      each kernel at its large shape on cold, rotated buffers
   ceiling      1 GiB device copies: the library's copy kernel and hipMemcpy
   decode_token_b1  per-op latency of the batch-1 decode token
@@ -545,6 +547,57 @@ def cpu_baseline_run(wl, bytes_per_step, budget_s: float):
                 seconds=round(el, 2), ms_per_step=round(1e3 * el / steps, 1))
 
 
+def cpu_configs_run():
+    """The oracle at each parity-shape config (the batch-1 decode token's
+    three ops; RMSNorm [512, 2176] in fp32 and bf16; the 8-sequence prefill
+    RoPE + store; SwiGLU [8192, 2 x 8960]), timed once with every oracle
+    thread and once with one thread."""
+    import numpy as np
+    import torch
+    import oracle
+    import workloads
+
+    def npb(t):
+        t = t.contiguous()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    tok = {k: (npb(v) if isinstance(v, torch.Tensor) else v)
+           for k, v in workloads.decode_token(seed=0).items()}
+    r32 = workloads.rmsnorm_rows(rows=512, d=2176, dtype="f32", seed=0)
+    r16 = workloads.rmsnorm_rows(rows=512, d=2176, dtype="bf16", seed=0)
+    x32, w32, x16, w16 = npb(r32["x"]), npb(r32["w"]), npb(r16["x"]), npb(r16["w"])
+    pf = workloads.prefill(n_seqs=8, dtype="bf16", seed=0)
+    qkv = [npb(t) for t in workloads.qkv_views(pf["qkv"], pf["hq"], pf["hkv"], pf["dh"])]
+    cache, pos, slots = npb(pf["cache"]).copy(), pf["positions"].numpy(), pf["slot_mapping"].numpy()
+    sw = workloads.swiglu_fused(rows=8192, inter=8960, dtype="bf16", seed=0)
+    gate, up = npb(sw["gate_up"][:, :8960]), npb(sw["gate_up"][:, 8960:])
+    eps = float(np.float32(1e-6))
+    cases = {
+        "decode_token_b1": lambda: (
+            oracle.rmsnorm(tok["x"], tok["w"], eps),
+            oracle.rope_kvstore(tok["q"], tok["k"], tok["v"], tok["positions"], tok["theta"],
+                                tok["cache"], tok["slot_mapping"]),
+            oracle.swiglu(tok["gate"], tok["up"])),
+        "rmsnorm_512x2176_f32": lambda: oracle.rmsnorm(x32, w32, eps),
+        "rmsnorm_512x2176_bf16": lambda: oracle.rmsnorm(x16, w16, eps),
+        "prefill_rope_kvstore_8_seqs": lambda: oracle.rope_kvstore(
+            *qkv, pos, pf["theta"], cache, slots, block_size=pf["block_size"]),
+        "swiglu_8192x8960": lambda: oracle.swiglu(gate, up),
+    }
+    threads = oracle.num_threads()
+    out = {}
+    for name, fn in cases.items():
+        row = {}
+        for n in (threads, 1):
+            oracle.set_num_threads(n)
+            t0 = time.perf_counter()
+            fn()
+            row["seconds" if n == threads else "one_thread_seconds"] = round(time.perf_counter() - t0, 4)
+        out[name] = row
+    oracle.set_num_threads(threads)
+    return dict(threads=threads, **out)
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -709,6 +762,7 @@ def main():
     cpu = None
     if not args.skip_cpu:
         cpu = cpu_baseline_run(wl, nbytes["step"], args.cpu_seconds)
+        cpu["per_config"] = cpu_configs_run()
         log(f"cpu oracle: {cpu['value']} GB/s on {cpu['cores']} threads ({cpu['sample']})")
 
     op_us = {k: round(1e3 * statistics.fmean(v), 3) for k, v in per_op.items()}
