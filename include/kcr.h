@@ -27,8 +27,14 @@
  *  - Data-dependent indices (positions, slots) are bounds-checked inside the
  *    kernels: an out-of-range index skips that token's writes instead of
  *    touching memory outside the caller's buffers.
- *  - Calls are thread-safe; the only library state is a per-device cache of
- *    the compute-unit count.
+ *  - Calls are thread-safe. The only library state is set once: per device,
+ *    the compute-unit count, the LDS per workgroup and whether the wide-row
+ *    kernel's LDS limit has been raised; per thread, the events armed by
+ *    kcr_time_next_launch.
+ *  - Debug mode: with the environment variable KCR_DEBUG set to a non-zero
+ *    integer when the library first launches, every call synchronizes its
+ *    stream after the launch (except while the stream is being captured into
+ *    a graph) and returns KCR_ERR_LAUNCH if the kernel failed.
  *
  * Citations name the web page and the section that defines each operation.
  */
@@ -55,7 +61,7 @@ enum kcr_status {
     KCR_ERR_ALIGN = -4,  /* a base pointer or a stride breaks 16-byte vector alignment */
     KCR_ERR_HEADS = -5,  /* n_head is not a multiple of n_kv_head */
     KCR_ERR_ALIAS = -6,  /* an output overlaps an input in a way the op does not allow */
-    KCR_ERR_LAUNCH = -7, /* the HIP runtime refused the launch (see hipGetLastError) */
+    KCR_ERR_LAUNCH = -7, /* the HIP runtime refused the launch, or (KCR_DEBUG) the kernel failed */
     KCR_ERR_DEVICE = -8  /* no usable HIP device is current */
 };
 

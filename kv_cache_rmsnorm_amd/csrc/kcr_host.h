@@ -96,6 +96,13 @@ struct TimingEvents {
 };
 TimingEvents& next_launch_events();
 
+// Debug mode (environment KCR_DEBUG set to a non-zero integer when the
+// library first launches): after every launch the stream is synchronized
+// and a kernel failure is reported as KCR_ERR_LAUNCH by the call that
+// launched it. A stream under graph capture is never synchronized.
+bool debug_sync();
+int debug_check(void* stream);
+
 // Launches `kern` with a single by-value argument struct and reports the
 // runtime's verdict for this launch. When the calling thread armed timing
 // events, the launch goes through hipExtLaunchKernel, which stamps them at
@@ -117,7 +124,8 @@ inline int launch(void (*kern)(Args), dim3 grid, dim3 block, void* stream, const
         e = hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, params, lds,
                             static_cast<hipStream_t>(stream));
     }
-    return e == hipSuccess ? KCR_OK : KCR_ERR_LAUNCH;
+    if (e != hipSuccess) return KCR_ERR_LAUNCH;
+    return debug_sync() ? debug_check(stream) : KCR_OK;
 }
 
 // Grid size for a grid-stride kernel: enough workgroups to cover `work`

@@ -1,6 +1,8 @@
 // runtime.hip -- library-wide pieces of the C ABI: device query, the plain
 // copy kernel used as the bandwidth ceiling, status strings and the host
 // self-test.
+#include <stdlib.h>
+
 #include <atomic>
 
 #include "kcr_device.h"
@@ -15,6 +17,23 @@ static std::atomic<int> g_cus[kMaxDevices];
 TimingEvents& next_launch_events() {
     static thread_local TimingEvents ev;
     return ev;
+}
+
+bool debug_sync() {
+    static const bool on = [] {
+        const char* v = getenv("KCR_DEBUG");
+        return v != nullptr && atoi(v) != 0;
+    }();
+    return on;
+}
+
+int debug_check(void* stream) {
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cap) != hipSuccess) return KCR_ERR_LAUNCH;
+    if (cap != hipStreamCaptureStatusNone) return KCR_OK;
+    if (hipStreamSynchronize(s) != hipSuccess || hipGetLastError() != hipSuccess) return KCR_ERR_LAUNCH;
+    return KCR_OK;
 }
 
 int device_cus() {

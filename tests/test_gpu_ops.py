@@ -556,3 +556,74 @@ def test_concurrent_host_threads(kcr):
     assert not any(th.is_alive() for th in threads), "a worker thread did not finish"
     torch.cuda.synchronize()
     assert not errors, errors[:3]
+
+
+def test_errors_launch_nothing(kcr):
+    """A refused call enqueues nothing: after each entry point below returns
+    its error code, the output (and, for the aliasing call, the input it
+    would have overwritten) keeps every byte."""
+    lib, s = kcr._lib, torch.cuda.current_stream().cuda_stream
+    g = torch.Generator().manual_seed(3)
+    xb = torch.randn((9, 64), generator=g).to(torch.bfloat16).cuda()  # one spare row
+    x = xb[:8]
+    w = torch.ones(64, dtype=torch.bfloat16, device="cuda")
+    y = torch.full((8, 64), -1, dtype=torch.int16, device="cuda")
+    x0, y0 = xb.clone(), y.clone()
+    assert lib.kcr_rmsnorm(x.data_ptr(), 64, w.data_ptr(), y.data_ptr(), 64, 8, 64, 1e-6, 9, s) == -3
+    assert lib.kcr_rmsnorm(x.data_ptr(), 64, w.data_ptr(), x.data_ptr() + 128, 64, 8, 64, 1e-6, 0, s) == -6
+    assert lib.kcr_swiglu(x.data_ptr(), 64, x.data_ptr(), 64, y.data_ptr(), 16, 8, 32, 0, s) == -2
+    q = torch.randn((2, 3, 128), generator=g).to(torch.bfloat16).cuda()
+    kv = torch.randn((2, 2, 128), generator=g).to(torch.bfloat16).cuda()
+    pos = torch.zeros(2, dtype=torch.int64, device="cuda")
+    cos = torch.ones((4, 64), device="cuda")
+    cache = torch.full((2, 4, 4, 2, 128), -1, dtype=torch.int16, device="cuda")
+    cache0 = cache.clone()
+    qo = torch.full((2, 3, 128), -1, dtype=torch.int16, device="cuda")
+    assert lib.kcr_rope_kvstore(q.data_ptr(), 384, 128, kv.data_ptr(), 256, 128, kv.data_ptr(), 256, 128,
+                                qo.data_ptr(), pos.data_ptr(), cos.data_ptr(), cos.data_ptr(), 4,
+                                cache.data_ptr(), pos.data_ptr(), 2, 3, 2, 128, 4, 4, 0, s) == -5
+    torch.cuda.synchronize()
+    assert torch.equal(xb, x0) and torch.equal(y, y0) and torch.equal(cache, cache0)
+    assert bool((qo == -1).all())
+
+
+def test_debug_mode(kcr):
+    """KCR_DEBUG=1: every call synchronizes and checks its kernel, and a
+    captured graph still records and replays; the results are the same bits
+    as without it."""
+    import hashlib
+    import os
+    import subprocess
+    import sys
+    code = (
+        "import hashlib, torch\n"
+        "import kv_cache_rmsnorm_amd as k\n"
+        "g = torch.Generator().manual_seed(5)\n"
+        "x = torch.randn((300, 2176), generator=g).to(torch.bfloat16).cuda()\n"
+        "w = (0.5 + torch.rand(2176, generator=g)).to(torch.bfloat16).cuda()\n"
+        "y = k.rmsnorm(x, w)\n"
+        "s = torch.cuda.Stream()\n"
+        "s.wait_stream(torch.cuda.current_stream())\n"
+        "with torch.cuda.stream(s):\n"
+        "    k.rmsnorm(x, w, out=y)\n"
+        "torch.cuda.current_stream().wait_stream(s)\n"
+        "torch.cuda.synchronize()\n"
+        "graph = torch.cuda.CUDAGraph()\n"
+        "with torch.cuda.graph(graph):\n"
+        "    k.rmsnorm(x, w, out=y)\n"
+        "y.zero_()\n"
+        "graph.replay()\n"
+        "torch.cuda.synchronize()\n"
+        "print(hashlib.sha256(y.cpu().view(torch.int16).numpy().tobytes()).hexdigest(), flush=True)\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    say("debug mode in a child process")
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, env=dict(os.environ, KCR_DEBUG="1"),
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    g = torch.Generator().manual_seed(5)
+    x = torch.randn((300, 2176), generator=g).to(torch.bfloat16).cuda()
+    w = (0.5 + torch.rand(2176, generator=g)).to(torch.bfloat16).cuda()
+    y = kcr.rmsnorm(x, w)
+    torch.cuda.synchronize()
+    want = hashlib.sha256(y.cpu().view(torch.int16).numpy().tobytes()).hexdigest()
+    assert r.stdout.strip().splitlines()[-1] == want
