@@ -22,6 +22,7 @@ Prints ONE JSON line:
   ceiling      1 GiB device copies: the library's copy kernel and hipMemcpy
   decode_token_b1  per-op latency of the batch-1 decode token
   decode_chain_b1  the 28-layer chain at batch 1: graph of 112 launches vs one launch
+  source_sha256    hash of the library's sources the line was measured with
 """
 from __future__ import annotations
 
@@ -661,6 +662,21 @@ def kernel_source_sha() -> str:
     return h.hexdigest()
 
 
+def library_source_sha() -> str:
+    """sha256 over the library's sources (C ABI header, kernels, binding),
+    file by file in name order: identifies the build a line was measured on
+    where no git metadata travels with the tree."""
+    h = hashlib.sha256()
+    for d in ("include", os.path.join("kv_cache_rmsnorm_amd", "csrc"), "kv_cache_rmsnorm_amd"):
+        full = os.path.join(ROOT, d)
+        for f in sorted(os.listdir(full)):
+            p = os.path.join(full, f)
+            if os.path.isfile(p) and f.endswith((".h", ".hip", ".py")):
+                h.update(f.encode())
+                h.update(open(p, "rb").read())
+    return h.hexdigest()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -792,6 +808,7 @@ def main():
         "kernels": kernels,
         "rmsnorm_sweep_512xD": sweep,
         "device": torch.cuda.get_device_name(0),
+        "source_sha256": library_source_sha(),
         "cus": kcr.device_cus(),
         "lds_per_block": torch.cuda.get_device_properties(0).shared_memory_per_block,
     }
