@@ -612,8 +612,8 @@ def cpu_model() -> str:
 def pmc_pass():
     """Eager launches only (no graphs), for hardware counter runs: the copy
     kernel on 1 GiB (the byte-counter reference), every op at the decode
-    chain's shape over its 28 layers, and each kernel once at its large
-    shape."""
+    chain's shape over its 28 layers, the batch-1 chain's one launch, and
+    each kernel at its large shape."""
     import torch
     import kv_cache_rmsnorm_amd as kcr
     import workloads
@@ -634,6 +634,12 @@ def pmc_pass():
     log(f"pmc pass: copy x3, chain steps x2 ({2 * 4 * len(chain.layers)} launches)")
     del chain
     torch.cuda.empty_cache()
+    b1 = DecodeChain(workloads.decode_chain(batch=1), "cuda", sentinel_cache=False)
+    for _ in range(3):
+        b1.step_b1()
+    torch.cuda.synchronize()
+    log("pmc pass: batch-1 one-launch chain x3")
+    del b1
     large_shapes(kcr, 3)
     torch.cuda.synchronize()
     log("pmc pass done")
