@@ -81,7 +81,7 @@ def norm_case(case: int):
     return tier, dt, d, rows, add, d + x_pad, d + y_pad, x_off, y_off, rng
 
 
-@pytest.mark.parametrize("case", range(36))
+@pytest.mark.parametrize("case", range(72))
 def test_fuzz_norms(kcr, case):
     tier, dt, d, rows, add, x_stride, y_stride, x_off, y_off, rng = norm_case(case)
     say(f"norm case {case} ({tier}): dt={dt} d={d} rows={rows} add={add} strides x={x_stride} "
@@ -105,7 +105,7 @@ def test_fuzz_norms(kcr, case):
     assert_close(y.cpu().double().numpy(), y_ref, dt, f"norm case {case}")
 
 
-@pytest.mark.parametrize("case", range(18))
+@pytest.mark.parametrize("case", range(36))
 def test_fuzz_gated(kcr, case):
     rng = np.random.default_rng(3000 + case)
     dt = DTS[case % 3]
@@ -128,7 +128,7 @@ def test_fuzz_gated(kcr, case):
     assert_close(out.cpu().double().numpy(), ref, dt, f"gated case {case}")
 
 
-@pytest.mark.parametrize("case", range(18))
+@pytest.mark.parametrize("case", range(36))
 def test_fuzz_rope(kcr, case):
     rng = np.random.default_rng(5000 + case)
     dt = DTS[case % 3]
@@ -177,7 +177,7 @@ def test_fuzz_rope(kcr, case):
     assert_rope_close(kg.view(dt).double().numpy(), k_rot[tok], dt, f"rope case {case}: K rows")
 
 
-@pytest.mark.parametrize("case", range(8))
+@pytest.mark.parametrize("case", range(16))
 def test_fuzz_gather(kcr, case):
     rng = np.random.default_rng(8000 + case)
     dt = DTS[case % 3]
