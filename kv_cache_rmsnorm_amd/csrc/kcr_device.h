@@ -202,51 +202,52 @@ __device__ __forceinline__ u32x4 load_elems(const void* base, int64_t elem, int6
     return v;
 }
 
-// EAGER (latency-bound row-norm calls whose shape leaves lanes past the
-// row's end): every load of a lane is in flight before any is waited for.
-// The result is zero bits in its registers before the vector load is issued
-// (the empty asm keeps the compiler from sinking the zeros into the
-// branches), so lanes past the end of the row write nothing. Were the zeros
-// written on that path instead, they would overwrite the destination of the
-// vector load still in flight in other lanes, and the compiler would wait
-// there for every load in flight.
-//
-// Not EAGER (every other caller, and the throughput-bound large-call
-// row-norm shapes, which were tuned with it): lanes at or past the end of
-// the row take the element path, where the compiler waits for every load
-// the wave has in flight before it goes on, so each wave's requests are
-// spaced out. Measured on MI355X, each form wins its own regime: bf16
-// [131072, 2176] streams at 6.46-6.48 TB/s this way against 6.31-6.33
-// eagerly, while a [512, 2176] bf16 call takes 3.27 us per launch eagerly
-// against 3.77 us this way. Where every lane holds a whole vector the eager
-// form only adds the zeroing moves (about 0.05 us at [512, 2048]).
-template <typename T, bool NT, bool EAGER = false>
+// Lanes at or past the end of the row take the element path, where the
+// compiler waits for every load the wave has in flight before it goes on,
+// so each wave's requests are spaced out. The throughput-bound large-call
+// row-norm shapes were tuned with this form and measured faster with it on
+// MI355X: bf16 [131072, 2176] streams at 6.46-6.48 TB/s this way against
+// 6.31-6.33 with every load issued first. Latency-bound small calls whose
+// shape leaves lanes past the row's end take load_whole and load_tail below
+// instead ([512, 2176] bf16: 3.22 against 3.77 us per launch).
+template <typename T, bool NT>
 __device__ __forceinline__ u32x4 load_raw(const void* base, int64_t elem, int64_t n, bool vec = true) {
     u32x4 v = {0u, 0u, 0u, 0u};
     if (!vec) {  // a row that is not dword aligned: element access throughout
         if (elem < n) v = load_elems<T>(base, elem, n);
         return v;
     }
-    if constexpr (EAGER) {
-        asm volatile("" : "+v"(v));
-        if (elem + T::kVec <= n) {
-            v = NT ? ld16_nt<T>(base, elem) : ld16<T>(base, elem);
-        } else if (elem < n) {
-            v = load_elems<T>(base, elem, n);  // the vector that straddles the end
-        }
-        return v;
-    } else {
-        if (elem + T::kVec <= n) return NT ? ld16_nt<T>(base, elem) : ld16<T>(base, elem);
-        const typename T::storage* p = static_cast<const typename T::storage*>(base) + elem;
+    if (elem + T::kVec <= n) return NT ? ld16_nt<T>(base, elem) : ld16<T>(base, elem);
+    const typename T::storage* p = static_cast<const typename T::storage*>(base) + elem;
 #pragma unroll
-        for (int e = 0; e < T::kVec; ++e) {
-            if (elem + e < n) {
-                if constexpr (T::kVec == 8) v[e >> 1] |= (uint32_t)p[e] << (16 * (e & 1));
-                else v[e] = __float_as_uint(p[e]);
-            }
+    for (int e = 0; e < T::kVec; ++e) {
+        if (elem + e < n) {
+            if constexpr (T::kVec == 8) v[e >> 1] |= (uint32_t)p[e] << (16 * (e & 1));
+            else v[e] = __float_as_uint(p[e]);
         }
-        return v;
     }
+    return v;
+}
+
+// Whole 16-byte vectors only: lanes whose vector is not wholly inside the
+// row read zero bits, and the vector that straddles the end is left to
+// load_tail, which the caller runs once every load of the wave is in flight
+// (so the wait its element loads need delays nothing). The result is zero
+// bits in its registers before the vector load is issued (the empty asm
+// keeps the compiler from sinking the zeros into a branch): were the zeros
+// written on their own path, they would overwrite the destination of the
+// vector load still in flight in other lanes, and the compiler would wait
+// there for every load in flight.
+template <typename T, bool NT>
+__device__ __forceinline__ u32x4 load_whole(const void* base, int64_t elem, int64_t n) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    asm volatile("" : "+v"(v));
+    if (elem + T::kVec <= n) v = NT ? ld16_nt<T>(base, elem) : ld16<T>(base, elem);
+    return v;
+}
+template <typename T>
+__device__ __forceinline__ void load_tail(const void* base, int64_t elem, int64_t n, u32x4& v) {
+    if (elem < n && elem + T::kVec > n) v = load_elems<T>(base, elem, n);
 }
 
 template <typename T, bool NT>

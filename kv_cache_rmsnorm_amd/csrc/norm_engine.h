@@ -57,7 +57,7 @@ __device__ __forceinline__ void* row_ptr(void* base, int64_t row, int64_t stride
 template <int VPT_, int WPR_, int GROUPS_, bool NTL_, bool NTS_, int RPG_ = 1, bool EAGER_ = false>
 struct NormCfg {
     static constexpr int VPT = VPT_, WPR = WPR_, GROUPS = GROUPS_, RPG = RPG_;
-    static constexpr bool NTL = NTL_, NTS = NTS_, EAGER = EAGER_;  // EAGER: see load_raw
+    static constexpr bool NTL = NTL_, NTS = NTS_, EAGER = EAGER_;  // EAGER: see load_whole
     static constexpr int BLOCK = 64 * WPR * GROUPS;
 };
 
@@ -80,9 +80,19 @@ __global__ __launch_bounds__(C::BLOCK) void row_norm_kernel(const NormArgs a) {
 
     // The weight, once per workgroup (an L2 hit), in registers.
     const bool vw = VEC || vec_ok(a.w);
+    // EAGER (small calls whose shape leaves lanes past the row's end; the
+    // host sends only dword-aligned rows there): whole vectors first, and
+    // the one vector that straddles the end once every load is in flight.
+    constexpr bool kTail = C::EAGER && VEC;
+    const bool ragged = kTail && d % kVec != 0;
     u32x4 wr[VPT];
+    if constexpr (kTail) {
 #pragma unroll
-    for (int j = 0; j < VPT; ++j) wr[j] = load_raw<T, false, C::EAGER>(a.w, (int64_t)(j * LANES + rl) * kVec, d, vw);
+        for (int j = 0; j < VPT; ++j) wr[j] = load_whole<T, false>(a.w, (int64_t)(j * LANES + rl) * kVec, d);
+    } else {
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) wr[j] = load_raw<T, false>(a.w, (int64_t)(j * LANES + rl) * kVec, d, vw);
+    }
 
     // All RPG rows are read before any is written. `live[r]` is uniform per
     // row group; every wave reaches the barrier.
@@ -97,11 +107,32 @@ __global__ __launch_bounds__(C::BLOCK) void row_norm_kernel(const NormArgs a) {
         if (live[r]) {
             const void* xrow = row_ptr<T>(a.x, row0 + r, a.x_stride);
             vx[r] = VEC || vec_ok(xrow);  // row-uniform: vector or element access
+            if constexpr (kTail) {
 #pragma unroll
-            for (int j = 0; j < VPT; ++j)
-                xr[r][j] = load_raw<T, C::NTL, C::EAGER>(xrow, (int64_t)(j * LANES + rl) * kVec, d, vx[r]);
+                for (int j = 0; j < VPT; ++j)
+                    xr[r][j] = load_whole<T, C::NTL>(xrow, (int64_t)(j * LANES + rl) * kVec, d);
+            } else {
+#pragma unroll
+                for (int j = 0; j < VPT; ++j)
+                    xr[r][j] = load_raw<T, C::NTL>(xrow, (int64_t)(j * LANES + rl) * kVec, d, vx[r]);
+            }
         }
     }
+    // The straddling vectors of the weight and of x (for the add variant,
+    // after its delta loads below are issued too).
+    auto tails = [&]() {
+        if (!ragged) return;
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) load_tail<T>(a.w, (int64_t)(j * LANES + rl) * kVec, d, wr[j]);
+#pragma unroll
+        for (int r = 0; r < RPG; ++r) {
+            if (!live[r]) continue;
+            const void* xrow = row_ptr<T>(a.x, row0 + r, a.x_stride);
+#pragma unroll
+            for (int j = 0; j < VPT; ++j) load_tail<T>(xrow, (int64_t)(j * LANES + rl) * kVec, d, xr[r][j]);
+        }
+    };
+    if constexpr (kTail && !ADD) tails();
     if constexpr (ADD) {
         u32x4 dr[RPG][VPT];
 #pragma unroll
@@ -109,9 +140,28 @@ __global__ __launch_bounds__(C::BLOCK) void row_norm_kernel(const NormArgs a) {
             if (!live[r]) continue;
             const void* drow = row_ptr<T>(a.delta, row0 + r, a.delta_stride);
             const bool vd = VEC || vec_ok(drow);
+            if constexpr (kTail) {
 #pragma unroll
-            for (int j = 0; j < VPT; ++j)
-                dr[r][j] = load_raw<T, C::NTL, C::EAGER>(drow, (int64_t)(j * LANES + rl) * kVec, d, vd);
+                for (int j = 0; j < VPT; ++j)
+                    dr[r][j] = load_whole<T, C::NTL>(drow, (int64_t)(j * LANES + rl) * kVec, d);
+            } else {
+#pragma unroll
+                for (int j = 0; j < VPT; ++j)
+                    dr[r][j] = load_raw<T, C::NTL>(drow, (int64_t)(j * LANES + rl) * kVec, d, vd);
+            }
+        }
+        if constexpr (kTail) {
+            tails();
+            if (ragged) {
+#pragma unroll
+                for (int r = 0; r < RPG; ++r) {
+                    if (!live[r]) continue;
+                    const void* drow = row_ptr<T>(a.delta, row0 + r, a.delta_stride);
+#pragma unroll
+                    for (int j = 0; j < VPT; ++j)
+                        load_tail<T>(drow, (int64_t)(j * LANES + rl) * kVec, d, dr[r][j]);
+                }
+            }
         }
 #pragma unroll
         for (int r = 0; r < RPG; ++r) {
@@ -417,7 +467,7 @@ static int launch_unaligned(const NormArgs& a, void* stream) {
 // ones measured 20-34 us slower per step there, since every kernel must
 // write its dirty L2 lines back before the next one starts. Small calls are
 // latency-bound: where the shape leaves lanes past the row's end, they issue
-// every load before waiting (EAGER, load_raw); where every lane holds a whole
+// every load before waiting (EAGER, load_whole); where every lane holds a whole
 // vector, the plain form saves the zeroing moves.
 template <typename T, bool ADD, int WPR, bool EAGER>
 static int launch_small_w(const NormArgs& a, void* stream, int vpt) {
