@@ -22,6 +22,8 @@ Prints ONE JSON line:
   ceiling      1 GiB device copies: the library's copy kernel and hipMemcpy
   decode_token_b1  per-op latency of the batch-1 decode token
   decode_chain_b1  the 28-layer chain at batch 1: graph of 112 launches vs one launch
+  decode_chain_b256_one_launch  the timed step's chain (batch 256) as one launch,
+               one workgroup per token, beside the graph of 112 launches
   source_sha256    hash of the library's sources the line was measured with
 """
 from __future__ import annotations
@@ -381,6 +383,42 @@ def decode_token_latency(kcr, reps: int):
     return out
 
 
+def decode_chain_one_launch(kcr, chain, graph_us: float, reps: int):
+    """The benchmark's step (batch 256) as one launch of
+    kcr_decode_chain_batch: one workgroup per token runs all 28 layers' ops
+    in order, on the same buffers as the graph of 112 launches. Step time
+    from events over `reps` replays of a captured one-node graph; the
+    kernel's own duration from events stamped at its start and end."""
+    import torch
+    nb = chain.bytes_per_step()["step"]
+    chain.capture_one_launch()
+    for _ in range(5):
+        chain.graph_one.replay()
+    torch.cuda.synchronize()
+    e0, e1 = events(2)
+    e0.record()
+    for _ in range(reps):
+        chain.graph_one.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    one_us = e0.elapsed_time(e1) * 1e3 / reps
+    ev = events(2)
+    samples = []
+    for _ in range(20):
+        kcr.time_next_launch(ev[0], ev[1])
+        chain.step_one_launch()
+        torch.cuda.synchronize()
+        samples.append(ev[0].elapsed_time(ev[1]) * 1e3)
+    res = dict(step_bytes=nb, graph_112_launches_us=round(graph_us, 2), one_launch_us=round(one_us, 2),
+               one_launch_kernel_median_us=round(statistics.median(samples), 2),
+               one_launch_gbs=round(nb / (one_us * 1e-6) / 1e9, 1),
+               one_launch_frac_of_peak=round(nb / (one_us * 1e-6) / 1e9 / PEAK_GBS, 4),
+               speedup=round(graph_us / one_us, 2))
+    log(f"batch-256 chain in one launch: {one_us:.1f} us/step ({res['one_launch_gbs']} GB/s), "
+        f"graph of 112 launches {graph_us:.1f} us/step")
+    return res
+
+
 def decode_chain_b1(kcr, reps: int):
     """The 28-layer chain at batch 1 (the decode token of a single sequence
     at position 4096): one step as a captured graph of the 112 separate
@@ -612,7 +650,8 @@ def cpu_model() -> str:
 def pmc_pass():
     """Eager launches only (no graphs), for hardware counter runs: the copy
     kernel on 1 GiB (the byte-counter reference), every op at the decode
-    chain's shape over its 28 layers, the batch-1 chain's one launch, and
+    chain's shape over its 28 layers, the batch-256 and batch-1 chains' one
+    launch, and
     each kernel at its large shape."""
     import torch
     import kv_cache_rmsnorm_amd as kcr
@@ -632,6 +671,10 @@ def pmc_pass():
         chain.step_eager()
     torch.cuda.synchronize()
     log(f"pmc pass: copy x3, chain steps x2 ({2 * 4 * len(chain.layers)} launches)")
+    for _ in range(3):
+        chain.step_one_launch()
+    torch.cuda.synchronize()
+    log("pmc pass: batch-256 one-launch chain x3")
     del chain
     torch.cuda.empty_cache()
     b1 = DecodeChain(workloads.decode_chain(batch=1), "cuda", sentinel_cache=False)
@@ -770,6 +813,8 @@ def main():
     op_graph = graph_op_us(kcr, chain, max(10, args.steps // 2))
     chain.reset_residual()
     log("in-graph per-launch us: " + ", ".join(f"{k} {v:.2f}" for k, v in op_graph.items()))
+    chain_one = decode_chain_one_launch(kcr, chain, ms * 1e3, max(20, args.steps))
+    chain.reset_residual()
     token = decode_token_latency(kcr, max(10, args.steps // 2))
     chain_b1 = decode_chain_b1(kcr, max(20, args.steps))
     ceiling = copy_ceiling(kcr, args.kernel_iters)
@@ -810,6 +855,7 @@ def main():
         "op_in_graph_us": {k: round(v, 3) for k, v in op_graph.items()},
         "decode_token_b1": token,
         "decode_chain_b1": chain_b1,
+        "decode_chain_b256_one_launch": chain_one,
         "timed_wall_s": round(wall_s, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,

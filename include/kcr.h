@@ -356,8 +356,9 @@ int kcr_paged_kv_gather(const void* kv_cache, int64_t num_blocks, int block_size
  * Limits (KCR_ERR_SHAPE): hidden and inter multiples of 16 bytes' worth of
  * elements, hidden <= 1024 such vectors, inter <= 4096 of them, head_dim as
  * for kcr_rope_kvstore with (n_head + 2 n_kv_head) heads of at most 1024
- * lanes in all. Every pointer 16-byte aligned (KCR_ERR_ALIGN); outputs may
- * not overlap the inputs of their layer or h (KCR_ERR_ALIAS).
+ * lanes in all. Every pointer 16-byte aligned (KCR_ERR_ALIGN); a layer's
+ * outputs and h may not overlap one another or that layer's inputs, the
+ * tables, positions or slot_mapping (KCR_ERR_ALIAS).
  */
 #define KCR_B1_MAX_LAYERS 32
 typedef struct kcr_chain_layer {
@@ -379,6 +380,36 @@ int kcr_decode_chain_b1(const kcr_chain_layer* layers, int n_layers, void* h, in
                         const int64_t* positions, const int64_t* slot_mapping,
                         const float* cos_tab, const float* sin_tab, int64_t max_pos,
                         int block_size, int64_t num_blocks, float eps, int dtype, void* stream);
+
+/*
+ * kcr_decode_chain_batch -- the same chain for `batch` tokens in one launch:
+ * kcr_decode_chain_b1 is this call with batch = 1. Every op of the chain is
+ * row-wise, so token b's outputs depend on token b's inputs alone (and on
+ * the shared weights and tables); one workgroup per token runs the whole
+ * chain, and the tokens' workgroups never wait for one another. The results
+ * are those of the separate calls, each over the whole batch, in the order
+ * above.
+ *
+ *   batch        0 <= batch < 2^22 tokens (0: nothing is launched)
+ *   layers       as for kcr_decode_chain_b1, each per-token tensor with
+ *        `batch` contiguous rows (token b's row at b times the row width):
+ *        d_attn, y_attn, d_mlp, y_mlp [batch, hidden];
+ *        qkv [batch, (n_head + 2 n_kv_head) * head_dim];
+ *        q_out [batch, n_head * head_dim]; gate_up [batch, 2 * inter];
+ *        act [batch, inter]. w_attn, w_mlp [hidden] and the cache are shared.
+ *   h [batch, hidden]           device, input and output (the residual)
+ *   positions, slot_mapping [batch] int64 device. Two tokens with the same
+ *        valid slot store into one cache row; which one lands there is
+ *        unspecified (as for kcr_rope_kvstore).
+ *
+ * Limits, alignment and aliasing as for kcr_decode_chain_b1, over the
+ * batch's whole rows; batch out of range is KCR_ERR_SHAPE.
+ */
+int kcr_decode_chain_batch(const kcr_chain_layer* layers, int n_layers, int64_t batch, void* h,
+                           int hidden, int inter, int n_head, int n_kv_head, int head_dim,
+                           const int64_t* positions, const int64_t* slot_mapping,
+                           const float* cos_tab, const float* sin_tab, int64_t max_pos,
+                           int block_size, int64_t num_blocks, float eps, int dtype, void* stream);
 
 /*
  * kcr_copy -- plain streaming copy of `bytes` bytes (a multiple of 16, both

@@ -21,6 +21,7 @@ Ops (names as in the C ABI):
   paged_kv_gather(kv_cache, block_tables, seq_lens, max_len)
                                            K, V of each sequence, read back from the cache
   DecodeChainB1(layers, h, ...)            batch-1 decode chain of every layer in one launch
+  DecodeChainBatch(layers, h, ...)         the same chain for a batch, one workgroup per token
 """
 from __future__ import annotations
 
@@ -56,6 +57,7 @@ _SIGS = {
     "kcr_paged_kv_gather": [_P, _I64, _I, _I, _I, _P, _I64, _P, _I64, _I64, _P, _P, _I, _P],
     "kcr_copy": [_P, _P, _I64, _P],
     "kcr_decode_chain_b1": [_P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I64, _I, _I64, _F, _I, _P],
+    "kcr_decode_chain_batch": [_P, _I, _I64, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I64, _I, _I64, _F, _I, _P],
     "kcr_time_next_launch": [_P, _P],
     "kcr_device_cus": [],
     "kcr_selftest_host": [],
@@ -340,25 +342,31 @@ def paged_kv_gather(kv_cache: torch.Tensor, block_tables: torch.Tensor, seq_lens
 
 
 class ChainLayer(ctypes.Structure):
-    """kcr_chain_layer: one layer's device pointers for decode_chain_b1."""
+    """kcr_chain_layer: one layer's device pointers for the one-launch chain."""
     _fields_ = [(n, ctypes.c_void_p) for n in ("d_attn", "w_attn", "y_attn", "qkv", "q_out", "kv_cache",
                                                 "d_mlp", "w_mlp", "y_mlp", "gate_up", "act")]
 
 
-class DecodeChainB1:
-    """Marshalled arguments of kcr_decode_chain_b1 (one batch-1 decode
-    step's chain in one launch), checked and packed once; calling the object
-    launches the step on the current stream. `layers` is a list of dicts with
-    tensors d_attn, w_attn, y_attn, d_mlp, w_mlp, y_mlp [hidden],
-    qkv [(n_head + 2 n_kv_head) * head_dim], q_out [n_head, head_dim],
-    cache [2, blocks, block_size, n_kv_head, head_dim], gate_up [2 * inter],
-    act [inter] (a leading batch dimension of 1 is allowed); h [hidden] is
-    updated in place. The tensors must stay alive while the object is used."""
+class DecodeChainBatch:
+    """Marshalled arguments of kcr_decode_chain_batch (one decode step's
+    chain for a batch of tokens in one launch), checked and packed once;
+    calling the object launches the step on the current stream. `h` is the
+    residual [batch, hidden] (or [hidden] for one token), updated in place.
+    `layers` is a list of dicts with tensors of `batch` contiguous rows:
+    d_attn, y_attn, d_mlp, y_mlp [batch, hidden],
+    qkv [batch, (n_head + 2 n_kv_head) * head_dim], q_out [batch, n_head, head_dim],
+    gate_up [batch, 2 * inter], act [batch, inter]; and the shared
+    w_attn, w_mlp [hidden] and cache [2, blocks, block_size, n_kv_head, head_dim].
+    The tensors must stay alive while the object is used."""
+
+    _op = "decode_chain_batch"
 
     def __init__(self, layers: list, h: torch.Tensor, positions: torch.Tensor, slot_mapping: torch.Tensor,
                  cos: torch.Tensor, sin: torch.Tensor, eps: float, n_head: int, n_kv_head: int):
         hidden = h.shape[-1]
-        _expect(h.numel() == hidden and h.is_contiguous(), "h must be one contiguous row")
+        batch = h.numel() // hidden if hidden else 0
+        _expect(h.dim() in (1, 2) and h.is_contiguous(), "h must be a contiguous [batch, hidden] tensor")
+        self._check_batch(batch)
         self.dt = _dt(h)
         _expect(all(t.device == h.device for t in (positions, slot_mapping, cos, sin)),
                 "positions, slot_mapping and the tables must be on h's device")
@@ -369,8 +377,9 @@ class DecodeChainB1:
                 "cos/sin must be contiguous float32 [max_pos, head_dim / 2]")
         head_dim = cos.shape[1] * 2
         _expect(positions.dtype == torch.int64 and slot_mapping.dtype == torch.int64
-                and positions.numel() == 1 and slot_mapping.numel() == 1,
-                "positions and slot_mapping must be int64 [1]")
+                and positions.numel() == batch and slot_mapping.numel() == batch
+                and positions.is_contiguous() and slot_mapping.is_contiguous(),
+                f"positions and slot_mapping must be contiguous int64 [{batch}]")
         self.table = (ChainLayer * max(n, 1))()
         inter = nb = bs = 0
         for i, L in enumerate(layers):
@@ -382,9 +391,10 @@ class DecodeChainB1:
             if i and (cache.shape[1], cache.shape[2], L["act"].shape[-1]) != (nb, bs, inter):
                 raise ValueError("every layer must have the same cache shape and intermediate size")
             nb, bs, inter = cache.shape[1], cache.shape[2], L["act"].shape[-1]
-            sizes = dict(d_attn=hidden, w_attn=hidden, y_attn=hidden, d_mlp=hidden, w_mlp=hidden,
-                         y_mlp=hidden, qkv=(n_head + 2 * n_kv_head) * head_dim, q_out=n_head * head_dim,
-                         gate_up=2 * inter, act=inter)
+            per_tok = dict(d_attn=hidden, y_attn=hidden, d_mlp=hidden, y_mlp=hidden,
+                           qkv=(n_head + 2 * n_kv_head) * head_dim, q_out=n_head * head_dim,
+                           gate_up=2 * inter, act=inter)
+            sizes = dict(w_attn=hidden, w_mlp=hidden, **{k: batch * v for k, v in per_tok.items()})
             for name, size in sizes.items():
                 t = L[name]
                 _expect(t.numel() == size and t.is_contiguous() and t.dtype == h.dtype and t.device == h.device,
@@ -393,20 +403,49 @@ class DecodeChainB1:
                                        cache.data_ptr(),
                                        *[L[f].data_ptr() for f in ("d_mlp", "w_mlp", "y_mlp", "gate_up", "act")])
         self.h = h
+        self.batch = batch
         self.args = (ctypes.cast(self.table, ctypes.c_void_p), n, h.data_ptr(), hidden, inter, n_head, n_kv_head,
                      head_dim, positions.data_ptr(), slot_mapping.data_ptr(), cos.data_ptr(), sin.data_ptr(),
                      cos.shape[0], bs, nb, float(eps), self.dt)
         self.n = n
 
+    @staticmethod
+    def _check_batch(batch: int) -> None:
+        pass
+
+    def _launch(self) -> int:
+        return _lib.kcr_decode_chain_batch(self.args[0], self.args[1], self.batch, *self.args[2:],
+                                           _stream(self.h))
+
     def __call__(self) -> None:
-        if self.n:
-            _check("decode_chain_b1", _lib.kcr_decode_chain_b1(*self.args, _stream(self.h)))
+        if self.n and self.batch:
+            _check(self._op, self._launch())
+
+
+class DecodeChainB1(DecodeChainBatch):
+    """The batch-1 form through kcr_decode_chain_b1: h is one row ([hidden]
+    or [1, hidden]) and every per-token tensor holds one token."""
+
+    _op = "decode_chain_b1"
+
+    @staticmethod
+    def _check_batch(batch: int) -> None:
+        _expect(batch == 1, "h must be one contiguous row")
+
+    def _launch(self) -> int:
+        return _lib.kcr_decode_chain_b1(*self.args, _stream(self.h))
 
 
 def decode_chain_b1(layers: list, h: torch.Tensor, positions: torch.Tensor, slot_mapping: torch.Tensor,
                     cos: torch.Tensor, sin: torch.Tensor, eps: float, n_head: int, n_kv_head: int) -> None:
     """One call of kcr_decode_chain_b1 (see DecodeChainB1)."""
     DecodeChainB1(layers, h, positions, slot_mapping, cos, sin, eps, n_head, n_kv_head)()
+
+
+def decode_chain_batch(layers: list, h: torch.Tensor, positions: torch.Tensor, slot_mapping: torch.Tensor,
+                       cos: torch.Tensor, sin: torch.Tensor, eps: float, n_head: int, n_kv_head: int) -> None:
+    """One call of kcr_decode_chain_batch (see DecodeChainBatch)."""
+    DecodeChainBatch(layers, h, positions, slot_mapping, cos, sin, eps, n_head, n_kv_head)()
 
 
 def copy_(dst: torch.Tensor, src: torch.Tensor) -> torch.Tensor:

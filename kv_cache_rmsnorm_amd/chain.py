@@ -59,7 +59,9 @@ class DecodeChain:
                 act=torch.empty((B, self.inter), dtype=wl["dtype"], device=dev)))
         self.graph = None
         self.graph_b1 = None
+        self.graph_one = None
         self._b1 = None
+        self._one = None
 
     def reset_residual(self):
         self.h.copy_(self.h0)
@@ -84,20 +86,37 @@ class DecodeChain:
                                          self.sin, self.eps, self.hq, self.hkv)
         self._b1()
 
-    def capture_b1(self):
-        """Capture the one-launch step into a HIP graph."""
+    def step_one_launch(self):
+        """Any batch: the whole step's chain in one launch
+        (kcr_decode_chain_batch, one workgroup per token), same ops in the
+        same order."""
+        if self._one is None:
+            self._one = kcr.DecodeChainBatch(self.layers, self.h, self.positions, self.slot_mapping, self.cos,
+                                             self.sin, self.eps, self.hq, self.hkv)
+        self._one()
+
+    def _capture(self, step):
         s = torch.cuda.Stream(device=self.device)
         s.wait_stream(torch.cuda.current_stream(self.device))
         with torch.cuda.stream(s):
-            self.step_b1()
+            step()
         torch.cuda.current_stream(self.device).wait_stream(s)
         torch.cuda.synchronize(self.device)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            self.step_b1()
+            step()
         torch.cuda.synchronize(self.device)
-        self.graph_b1 = g
         return g
+
+    def capture_b1(self):
+        """Capture the batch-1 one-launch step into a HIP graph."""
+        self.graph_b1 = self._capture(self.step_b1)
+        return self.graph_b1
+
+    def capture_one_launch(self):
+        """Capture the one-launch step of any batch into a HIP graph."""
+        self.graph_one = self._capture(self.step_one_launch)
+        return self.graph_one
 
     def capture(self):
         """Capture one step into a HIP graph (after one eager warm-up step on

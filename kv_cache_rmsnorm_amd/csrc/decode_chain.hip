@@ -1,13 +1,18 @@
-// decode_b1.hip -- the per-layer chain of one batch-1 decode step in a single
-// launch (kcr_decode_chain_b1): for every layer, in order, residual add +
-// RMSNorm (the koas-w.github.io 2026-03-31 post, section 4), RoPE + paged
-// store (section 1), residual add + RMSNorm, SwiGLU (section 2).
+// decode_chain.hip -- the per-layer chain of one decode step in a single
+// launch (kcr_decode_chain_batch, and kcr_decode_chain_b1 for one token):
+// for every layer, in order, residual add + RMSNorm (the koas-w.github.io
+// 2026-03-31 post, section 4), RoPE + paged store (section 1), residual
+// add + RMSNorm, SwiGLU (section 2).
 //
 // gfx950 design
-//  * One workgroup of 1024 lanes runs every op of every layer in turn; ops
-//    are separated by workgroup barriers only, so the 4 launches per layer
-//    of the separate entry points (and their graph-node or host launch
-//    cost) become one launch per step.
+//  * One workgroup of 1024 lanes per token runs every op of every layer in
+//    turn; ops are separated by workgroup barriers only, so the 4 launches
+//    per layer of the separate entry points (and their graph-node or host
+//    launch cost) become one launch per step. Every op of the chain is
+//    row-wise (a token's outputs depend on that token's inputs alone), so
+//    the tokens' workgroups never wait for one another: no device-wide
+//    barrier is needed at any batch size. A batch of 256 fills the 256 CUs
+//    with one workgroup each.
 //  * The residual h lives in registers for the whole step: lane l owns
 //    16-byte vector l of the row, adds delta to it, stores the rounded sum
 //    (the in-place update of each add) and normalises it. The row's sum of
@@ -28,16 +33,19 @@ namespace kcr {
 constexpr int kB1Threads = 1024;
 constexpr int kB1Waves = kB1Threads / 64;
 constexpr int kB1MaxSwigluIters = 4;  // inter <= 4096 vectors
+// Tokens per launch: batch * 1024 lanes must stay below 2^32.
+constexpr int64_t kChainMaxBatch = (int64_t(1) << 22) - 1;
 
-struct ChainB1Args {
+struct ChainArgs {
     kcr_chain_layer layers[KCR_B1_MAX_LAYERS];
-    void* h;
+    void* h;  // [batch, hidden]; token b's rows of every per-token tensor at b * width
     const int64_t* pos;
     const int64_t* slots;
     const float* cos_t;
     const float* sin_t;
     int64_t max_pos, n_slots;
     int32_t n_layers, hidden, inter, hq, hkv, dh, group, lpu;
+    int64_t qkv_w;  // (hq + 2 hkv) * dh
     float eps;
 };
 
@@ -56,18 +64,22 @@ __device__ __forceinline__ float block_sum(float v, float (*part)[kB1Waves], int
 }
 
 template <typename T, int SWI>
-__global__ __launch_bounds__(kB1Threads) void decode_b1_kernel(const ChainB1Args a) {
+__global__ __launch_bounds__(kB1Threads) void decode_chain_kernel(const ChainArgs a) {
     using S = typename T::storage;
     constexpr int kVec = T::kVec;
     __shared__ float part[2][kB1Waves];
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    // This workgroup's token and its row offsets (uniform).
+    const int64_t tok = blockIdx.x;
+    const int64_t hrow = tok * a.hidden;
 
-    // residual: lane tid owns vector tid of h
+    // residual: lane tid owns vector tid of the token's row of h
     const int hv = a.hidden / kVec;
     const bool own_h = tid < hv;
     const int64_t he = (int64_t)tid * kVec;
     const int64_t he_c = own_h ? he : 0;  // in-bounds load address for every lane
-    u32x4 hreg = ld16<T>(a.h, he_c);
+    S* const h = static_cast<S*>(a.h) + hrow;
+    u32x4 hreg = ld16<T>(h, he_c);
 
     // RoPE: unit = virtual head (KV-group order), lane c = chunk c of both halves
     const int half = a.dh >> 1;
@@ -79,8 +91,8 @@ __global__ __launch_bounds__(kB1Threads) void decode_b1_kernel(const ChainB1Args
     const int kind = r < a.group ? 0 : (r == a.group ? 1 : 2);  // query, K, V
     const int src_head = kind == 0 ? g * a.group + r : (kind == 1 ? a.hq + g : a.hq + a.hkv + g);
     const int64_t c0 = rope_on ? (int64_t)c * kVec : 0;
-    const int64_t p = a.pos[0];
-    const int64_t slot = a.slots[0];
+    const int64_t p = a.pos[tok];
+    const int64_t slot = a.slots[tok];
     const bool p_ok = p >= 0 && p < a.max_pos;
     const bool store_kv = p_ok && slot >= 0 && slot < a.n_slots;
     float cs[kVec], sn[kVec];
@@ -102,31 +114,39 @@ __global__ __launch_bounds__(kB1Threads) void decode_b1_kernel(const ChainB1Args
 
     for (int l = 0; l < a.n_layers; ++l) {
         const kcr_chain_layer& L = a.layers[l];
+        // The token's rows of the layer's per-token tensors (uniform).
+        const S* const d_attn = static_cast<const S*>(L.d_attn) + hrow;
+        const S* const d_mlp = static_cast<const S*>(L.d_mlp) + hrow;
+        const S* const qkv = static_cast<const S*>(L.qkv) + tok * a.qkv_w;
+        const S* const gate_up = static_cast<const S*>(L.gate_up) + tok * 2 * (int64_t)a.inter;
         // Every load of the layer first, unconditionally: lanes with nothing to
         // load read an in-bounds clamped address and ignore the result. In
         // straight-line code the compiler waits for exactly the loads each op
         // needs; loads under lane-dependent branches made it wait for all of
         // them, and for earlier stores, before every op.
-        const u32x4 dA = ld16_nt<T>(L.d_attn, he_c);
+        const u32x4 dA = ld16_nt<T>(d_attn, he_c);
         const u32x4 wA = ld16<T>(L.w_attn, he_c);
-        const S* src = static_cast<const S*>(L.qkv) + (int64_t)src_head * a.dh;
+        const S* src = qkv + (int64_t)src_head * a.dh;
         const u32x4 x1 = ld16_nt<T>(src, c0);
         const u32x4 x2 = ld16_nt<T>(src, half + c0);
-        const u32x4 dM = ld16_nt<T>(L.d_mlp, he_c);
+        const u32x4 dM = ld16_nt<T>(d_mlp, he_c);
         const u32x4 wM = ld16<T>(L.w_mlp, he_c);
         u32x4 gr[SWI], ur[SWI];
 #pragma unroll
         for (int k = 0; k < SWI; ++k) {
             const int v = tid + k * kB1Threads;
             const int64_t e = v < iv ? (int64_t)v * kVec : 0;
-            gr[k] = ld16_nt<T>(L.gate_up, e);
-            ur[k] = ld16_nt<T>(L.gate_up, (int64_t)a.inter + e);
+            gr[k] = ld16_nt<T>(gate_up, e);
+            ur[k] = ld16_nt<T>(gate_up, (int64_t)a.inter + e);
         }
         // The layer's output pointers, read while the loads are in flight
         // (uniform; a per-lane choice between two fields of the argument
         // block would be a vector load that every later wait must cover).
-        S* const q_out = static_cast<S*>(L.q_out);
+        S* const q_out = static_cast<S*>(L.q_out) + tok * (int64_t)a.hq * a.dh;
         S* const kv_cache = static_cast<S*>(L.kv_cache);
+        S* const y_attn = static_cast<S*>(L.y_attn) + hrow;
+        S* const y_mlp = static_cast<S*>(L.y_mlp) + hrow;
+        S* const act = static_cast<S*>(L.act) + tok * (int64_t)a.inter;
         // Compiler-only barrier: keeps every load above issued here, ahead of
         // the lane-dependent branches that use them (the compiler otherwise
         // sinks a load into its only user and then waits for all loads).
@@ -145,7 +165,7 @@ __global__ __launch_bounds__(kB1Threads) void decode_b1_kernel(const ChainB1Args
 #pragma unroll
                 for (int e = 0; e < kVec; ++e) xf[e] += df[e];
                 hreg = pack<T>(xf);
-                st16_nt<T>(a.h, he, hreg);
+                st16_nt<T>(h, he, hreg);
                 unpack<T>(hreg, xf);  // the rounded sum is what the norm sees
 #pragma unroll
                 for (int e = 0; e < kVec; ++e) ss += xf[e] * xf[e];
@@ -157,7 +177,7 @@ __global__ __launch_bounds__(kB1Threads) void decode_b1_kernel(const ChainB1Args
                 unpack<T>(wv, wf);
 #pragma unroll
                 for (int e = 0; e < kVec; ++e) yf[e] = xf[e] * rs * wf[e];
-                st16_nt<T>(n == 0 ? L.y_attn : L.y_mlp, he, pack<T>(yf));
+                st16_nt<T>(n == 0 ? y_attn : y_mlp, he, pack<T>(yf));
             }
             if (n == 1) break;
 
@@ -197,19 +217,20 @@ __global__ __launch_bounds__(kB1Threads) void decode_b1_kernel(const ChainB1Args
                     const float ex = __builtin_amdgcn_exp2f(gf[e] * -1.4426950408889634f);
                     of[e] = gf[e] * __builtin_amdgcn_rcpf(1.0f + ex) * uf[e];
                 }
-                st16_nt<T>(L.act, (int64_t)v * kVec, pack<T>(of));
+                st16_nt<T>(act, (int64_t)v * kVec, pack<T>(of));
             }
         }
     }
 }
 
 template <typename T>
-static int launch_b1(const ChainB1Args& a, void* stream) {
+static int launch_chain(const ChainArgs& a, int64_t batch, void* stream) {
     const int iters = (a.inter / T::kVec + kB1Threads - 1) / kB1Threads;
+    const dim3 grid((uint32_t)batch);
     switch (iters <= 1 ? 1 : (iters <= 2 ? 2 : 4)) {
-        case 1: return launch(decode_b1_kernel<T, 1>, dim3(1), dim3(kB1Threads), stream, a);
-        case 2: return launch(decode_b1_kernel<T, 2>, dim3(1), dim3(kB1Threads), stream, a);
-        default: return launch(decode_b1_kernel<T, kB1MaxSwigluIters>, dim3(1), dim3(kB1Threads), stream, a);
+        case 1: return launch(decode_chain_kernel<T, 1>, grid, dim3(kB1Threads), stream, a);
+        case 2: return launch(decode_chain_kernel<T, 2>, grid, dim3(kB1Threads), stream, a);
+        default: return launch(decode_chain_kernel<T, kB1MaxSwigluIters>, grid, dim3(kB1Threads), stream, a);
     }
 }
 
@@ -217,14 +238,15 @@ static int launch_b1(const ChainB1Args& a, void* stream) {
 
 using namespace kcr;
 
-extern "C" int kcr_decode_chain_b1(const kcr_chain_layer* layers, int n_layers, void* h, int hidden,
-                                   int inter, int n_head, int n_kv_head, int head_dim,
-                                   const int64_t* positions, const int64_t* slot_mapping,
-                                   const float* cos_tab, const float* sin_tab, int64_t max_pos,
-                                   int block_size, int64_t num_blocks, float eps, int dtype,
-                                   void* stream) {
+extern "C" int kcr_decode_chain_batch(const kcr_chain_layer* layers, int n_layers, int64_t batch, void* h,
+                                      int hidden, int inter, int n_head, int n_kv_head, int head_dim,
+                                      const int64_t* positions, const int64_t* slot_mapping,
+                                      const float* cos_tab, const float* sin_tab, int64_t max_pos,
+                                      int block_size, int64_t num_blocks, float eps, int dtype,
+                                      void* stream) {
     if (!dtype_ok(dtype)) return KCR_ERR_DTYPE;
     if (n_layers < 0 || n_layers > KCR_B1_MAX_LAYERS) return KCR_ERR_SHAPE;
+    if (batch < 0 || batch > kChainMaxBatch) return KCR_ERR_SHAPE;
     if (n_kv_head < 1 || n_head < 1) return KCR_ERR_SHAPE;
     if (n_head % n_kv_head != 0) return KCR_ERR_HEADS;
     const size_t es = dtype_size(dtype);
@@ -238,7 +260,7 @@ extern "C" int kcr_decode_chain_b1(const kcr_chain_layer* layers, int n_layers, 
     int lpu = 1;
     while (lpu * vec < head_dim / 2) lpu *= 2;
     if ((int64_t)n_kv_head * (group + 2) * lpu > kB1Threads) return KCR_ERR_SHAPE;
-    if (n_layers == 0) return KCR_OK;
+    if (n_layers == 0 || batch == 0) return KCR_OK;
     if (!layers || !h || !positions || !slot_mapping || !cos_tab || !sin_tab) return KCR_ERR_NULL;
     if (!aligned16(h) || !aligned16(cos_tab) || !aligned16(sin_tab) ||
         (reinterpret_cast<uintptr_t>(positions) & 7u) || (reinterpret_cast<uintptr_t>(slot_mapping) & 7u))
@@ -246,11 +268,12 @@ extern "C" int kcr_decode_chain_b1(const kcr_chain_layer* layers, int n_layers, 
 
     const int64_t n_slots = num_blocks * (int64_t)block_size;
     const int64_t qkv_elems = (int64_t)(n_head + 2 * n_kv_head) * head_dim;
-    const Span sh = span2d(h, 1, 0, hidden, es);
+    const int64_t B = batch;
+    const Span sh = span2d(h, B, hidden, hidden, es);
     const Span st = span2d(cos_tab, 1, 0, max_pos * (head_dim / 2), 4);
     const Span ss = span2d(sin_tab, 1, 0, max_pos * (head_dim / 2), 4);
-    const Span sp = span2d(positions, 1, 0, 1, 8), sm = span2d(slot_mapping, 1, 0, 1, 8);
-    ChainB1Args a{};
+    const Span sp = span2d(positions, 1, 0, B, 8), sm = span2d(slot_mapping, 1, 0, B, 8);
+    ChainArgs a{};
     for (int l = 0; l < n_layers; ++l) {
         const kcr_chain_layer& L = layers[l];
         const void* ptrs[] = {L.d_attn, L.w_attn, L.y_attn, L.qkv, L.q_out, L.d_mlp, L.w_mlp, L.y_mlp,
@@ -261,14 +284,16 @@ extern "C" int kcr_decode_chain_b1(const kcr_chain_layer* layers, int n_layers, 
         }
         if (!L.kv_cache && n_slots > 0) return KCR_ERR_NULL;
         if (L.kv_cache && !aligned16(L.kv_cache)) return KCR_ERR_ALIGN;
-        const Span in[] = {span2d(L.d_attn, 1, 0, hidden, es), span2d(L.w_attn, 1, 0, hidden, es),
-                           span2d(L.qkv, 1, 0, qkv_elems, es), span2d(L.d_mlp, 1, 0, hidden, es),
-                           span2d(L.w_mlp, 1, 0, hidden, es), span2d(L.gate_up, 1, 0, 2 * (int64_t)inter, es),
-                           sh, st, ss, sp, sm};
-        const Span out[] = {span2d(L.y_attn, 1, 0, hidden, es),
-                            span2d(L.q_out, 1, 0, (int64_t)n_head * head_dim, es),
+        const Span in[] = {span2d(L.d_attn, B, hidden, hidden, es), span2d(L.w_attn, 1, 0, hidden, es),
+                           span2d(L.qkv, B, qkv_elems, qkv_elems, es), span2d(L.d_mlp, B, hidden, hidden, es),
+                           span2d(L.w_mlp, 1, 0, hidden, es),
+                           span2d(L.gate_up, B, 2 * (int64_t)inter, 2 * (int64_t)inter, es),
+                           st, ss, sp, sm};
+        // h is read and written: it may overlap neither an input nor an output.
+        const Span out[] = {sh, span2d(L.y_attn, B, hidden, hidden, es),
+                            span2d(L.q_out, B, (int64_t)n_head * head_dim, (int64_t)n_head * head_dim, es),
                             span2d(L.kv_cache, 1, 0, 2 * n_slots * n_kv_head * (int64_t)head_dim, es),
-                            span2d(L.y_mlp, 1, 0, hidden, es), span2d(L.act, 1, 0, inter, es)};
+                            span2d(L.y_mlp, B, hidden, hidden, es), span2d(L.act, B, inter, inter, es)};
         constexpr int n_in = sizeof(in) / sizeof(in[0]), n_out = sizeof(out) / sizeof(out[0]);
         for (int i = 0; i < n_out; ++i) {
             for (int j = 0; j < n_in; ++j)
@@ -295,5 +320,17 @@ extern "C" int kcr_decode_chain_b1(const kcr_chain_layer* layers, int n_layers, 
     a.group = group;
     a.lpu = lpu;
     a.eps = eps;
-    return by_dtype(dtype, [&](auto t) { return launch_b1<decltype(t)>(a, stream); });
+    a.qkv_w = qkv_elems;
+    return by_dtype(dtype, [&](auto t) { return launch_chain<decltype(t)>(a, batch, stream); });
+}
+
+extern "C" int kcr_decode_chain_b1(const kcr_chain_layer* layers, int n_layers, void* h, int hidden,
+                                   int inter, int n_head, int n_kv_head, int head_dim,
+                                   const int64_t* positions, const int64_t* slot_mapping,
+                                   const float* cos_tab, const float* sin_tab, int64_t max_pos,
+                                   int block_size, int64_t num_blocks, float eps, int dtype,
+                                   void* stream) {
+    return kcr_decode_chain_batch(layers, n_layers, 1, h, hidden, inter, n_head, n_kv_head, head_dim,
+                                  positions, slot_mapping, cos_tab, sin_tab, max_pos, block_size,
+                                  num_blocks, eps, dtype, stream);
 }

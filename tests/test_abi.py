@@ -36,6 +36,7 @@ def lib():
     L.kcr_rope_cos_sin.argtypes = [P, P, I64, I, D, P]
     L.kcr_rope_cos_sin_host.argtypes = [P, P, I64, I, D]
     L.kcr_decode_chain_b1.argtypes = [P, I, P, I, I, I, I, I, P, P, P, P, I64, I, I64, F, I, P]
+    L.kcr_decode_chain_batch.argtypes = [P, I, I64, P, I, I, I, I, I, P, P, P, P, I64, I, I64, F, I, P]
     L.kcr_qknorm_rope_kvstore.argtypes = [P, I64, I64, P, I64, I64, P, I64, I64, P, P, F, P, P, P, P,
                                           I64, P, P, I64, I, I, I, I, I64, I, P]
     L.kcr_swiglu.argtypes = [P, I64, P, I64, P, I64, I64, I64, I, P]
@@ -330,3 +331,40 @@ def test_decode_chain_b1_validation(lib):
     bad = table(2)
     bad[0].p2 = bad[0].p0                            # y_attn on top of d_attn
     assert call(layers=bad) == ALIAS
+
+
+def test_decode_chain_batch_validation(lib):
+    """Host-side checks of the one-launch chain over a batch: the batch's
+    range, and aliasing over the whole batch's rows (a y_attn on row 3 of
+    d_attn is refused at batch 4 and accepted at batch 2)."""
+    import ctypes
+    A = 1 << 20
+    f = lib.kcr_decode_chain_batch
+
+    class Layer(ctypes.Structure):
+        _fields_ = [(f"p{i}", ctypes.c_void_p) for i in range(11)]
+
+    def table(n, base=1 << 30, step=1 << 22):
+        arr = (Layer * n)()
+        for i in range(n):
+            arr[i] = Layer(*[base + (i * 11 + j) * step for j in range(11)])
+        return arr
+
+    H = 1 << 34
+
+    def call(batch, layers=None, n=2, h=H, hidden=1536):
+        t = table(max(n, 1)) if layers is None else layers
+        return f(ctypes.cast(t, ctypes.c_void_p), n, batch, h, hidden, 8960, 12, 2, 128, H + A, H + A + 64,
+                 H + 2 * A, H + 8 * A, 4097, 16, 64, 1e-6, BF16, None)
+
+    assert call(4) == DEVICE
+    assert call(1) == DEVICE
+    assert call(-1) == SHAPE
+    assert call(1 << 22) == SHAPE                     # batch * 1024 lanes past 2^32
+    assert call(0, h=None) == OK                      # no tokens, no work
+    assert call(4, hidden=1537) == SHAPE
+    bad = table(2)
+    bad[0].p2 = bad[0].p0 + 3 * 1536 * 2              # y_attn = row 3 of d_attn
+    assert call(4, layers=bad) == ALIAS
+    assert call(2, layers=bad) == DEVICE
+    assert call(4, h=H + A - 2 * 1536 * 2) == ALIAS   # h's last rows over positions

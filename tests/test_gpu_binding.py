@@ -128,3 +128,26 @@ def test_decode_chain_b1_shapes(kcr):
     with pytest.raises(ValueError):
         kcr.DecodeChainB1(chain.layers, chain.h, chain.positions.repeat(2), *args[2:])
     torch.cuda.synchronize()
+
+
+def test_decode_chain_batch_shapes(kcr):
+    import workloads
+    from kv_cache_rmsnorm_amd.chain import DecodeChain
+    wl = workloads.decode_chain(layers=2, batch=3, ctx=40, seed=1, hidden=256, inter=512, hq=4, hkv=2,
+                                dh=32, block_size=8)
+    chain = DecodeChain(wl, "cuda", sentinel_cache=False)
+    chain.step_one_launch()
+    args = (chain.h, chain.positions, chain.slot_mapping, chain.cos, chain.sin, chain.eps, chain.hq, chain.hkv)
+    for name, bad in (("d_attn", t(2, 256)), ("q_out", t(3, 4, 16)), ("gate_up", t(3, 1000)),
+                      ("y_mlp", t(6, 256)[::2])):
+        layers = [dict(L) for L in chain.layers]
+        layers[0][name] = bad
+        with pytest.raises(ValueError):
+            kcr.DecodeChainBatch(layers, *args)
+    with pytest.raises(ValueError):                     # one position for three tokens
+        kcr.DecodeChainBatch(chain.layers, chain.h, chain.positions[:1], *args[2:])
+    with pytest.raises(ValueError):                     # a batch-1 entry given three tokens
+        kcr.DecodeChainB1(chain.layers, *args)
+    with pytest.raises(ValueError):
+        kcr.DecodeChainBatch(chain.layers, t(6, 256)[::2], *args[1:])
+    torch.cuda.synchronize()

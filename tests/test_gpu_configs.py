@@ -137,18 +137,19 @@ def _reset_chain(chain):
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("batch", [256, 1], ids=["b256_graph_of_112", "b1_one_launch"])
-def test_graph_replays_match_eager(kcr, batch):
+@pytest.mark.parametrize("batch,form", [(256, "graph"), (1, "b1"), (256, "one")],
+                         ids=["b256_graph_of_112", "b1_one_launch", "b256_one_launch"])
+def test_graph_replays_match_eager(kcr, batch, form):
     """A captured step replayed three times, with eager work (cache and
     residual resets) and synchronizations between the replays: every replay
     writes the same bits as the eager step."""
     from kv_cache_rmsnorm_amd.chain import DecodeChain
-    say(f"graph replays against the eager step, batch {batch}")
+    say(f"graph replays against the eager step, batch {batch}, {form}")
     wl = workloads.decode_chain(batch=batch, seed=7)
     chain = DecodeChain(wl, "cuda", sentinel_cache=True)
-    eager = chain.step_eager if batch > 1 else chain.step_b1
-    (chain.capture if batch > 1 else chain.capture_b1)()
-    replay = chain.graph.replay if batch > 1 else chain.graph_b1.replay
+    eager = {"graph": chain.step_eager, "b1": chain.step_b1, "one": chain.step_one_launch}[form]
+    capture = {"graph": chain.capture, "b1": chain.capture_b1, "one": chain.capture_one_launch}[form]
+    replay = capture().replay
     _reset_chain(chain)
     eager()
     torch.cuda.synchronize()
@@ -160,6 +161,76 @@ def test_graph_replays_match_eager(kcr, batch):
         got = _chain_outputs(chain)
         for i, (a, b) in enumerate(zip(ref, got)):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep}: output {i} differs"
+
+
+def test_decode_chain_batch_one_launch(kcr):
+    """The benchmark's decode step (28 layers, batch 256) in one launch of
+    kcr_decode_chain_batch, one workgroup per token, against the oracle run
+    layer by layer."""
+    from kv_cache_rmsnorm_amd.chain import DecodeChain
+    say("batch-256 decode chain, one launch")
+    wl = workloads.decode_chain(seed=0)
+    assert wl["h"].shape[0] == 256
+    chain = DecodeChain(wl, "cuda", sentinel_cache=True)
+    chain.step_one_launch()
+    torch.cuda.synchronize()
+    check_chain(wl, chain)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+def test_decode_chain_batch_ragged(kcr, dt):
+    """The one-launch chain at an odd batch (37 tokens) with two padding
+    tokens (slot -1), at other shapes (5 layers, hidden 512, intermediate
+    1408, 8 query / 2 KV heads of 64, block size 8), two steps in a row
+    (the residual carries over)."""
+    from kv_cache_rmsnorm_amd.chain import DecodeChain
+    say(f"batch-37 decode chain with padding tokens, one launch, {dt}")
+    wl = workloads.decode_chain(layers=5, batch=37, ctx=100, dtype=dt, seed=5, hidden=512, inter=1408,
+                                hq=8, hkv=2, dh=64, block_size=8)
+    wl["slot_mapping"][[3, 36]] = -1
+    wl["positions"] = torch.randint(0, wl["max_pos"], (37,), generator=workloads.gen(6))
+    chain = DecodeChain(wl, "cuda", sentinel_cache=True)
+    chain.step_one_launch()
+    torch.cuda.synchronize()
+    h_after = check_chain(wl, chain)
+    _reset_cache(chain)
+    chain.step_one_launch()
+    torch.cuda.synchronize()
+    check_chain(dict(wl, h=bits_to_tensor(h_after, workloads.as_dtype(dt))), chain)
+
+
+def test_decode_chain_batch_matches_b1(kcr):
+    """Token b of a batched one-launch step writes the same bits as a
+    batch-1 one-launch step of token b alone (no token's result depends on
+    another's)."""
+    from kv_cache_rmsnorm_amd.chain import DecodeChain
+    say("batched one-launch chain against per-token batch-1 launches")
+    wl = workloads.decode_chain(layers=3, batch=6, ctx=64, seed=11)
+    wl["positions"] = torch.randint(0, wl["max_pos"], (6,), generator=workloads.gen(12))
+    full = DecodeChain(wl, "cuda", sentinel_cache=True)
+    full.step_one_launch()
+    torch.cuda.synchronize()
+    for b in (0, 5):
+        one = dict(wl, h=wl["h"][b:b + 1], positions=wl["positions"][b:b + 1],
+                   slot_mapping=wl["slot_mapping"][b:b + 1],
+                   layers=[{k: (t[b:b + 1] if k in ("d_attn", "d_mlp", "qkv", "gate_up") else t)
+                            for k, t in lw.items()} for lw in wl["layers"]])
+        single = DecodeChain(one, "cuda", sentinel_cache=True)
+        single.step_b1()
+        torch.cuda.synchronize()
+        assert torch.equal(single.h.view(torch.int16), full.h[b:b + 1].view(torch.int16)), f"token {b} h"
+        s = int(wl["slot_mapping"][b])
+        for i, (Lf, Ls) in enumerate(zip(full.layers, single.layers)):
+            for name in ("y_attn", "q_out", "y_mlp", "act"):
+                assert torch.equal(Ls[name].view(torch.int16), Lf[name][b:b + 1].view(torch.int16)), \
+                    f"token {b} layer {i} {name}"
+            cf, cs = (L["cache"].view(2, -1, *L["cache"].shape[3:]) for L in (Lf, Ls))
+            assert torch.equal(cf[:, s].view(torch.int16), cs[:, s].view(torch.int16)), f"token {b} layer {i} cache"
+
+
+def _reset_cache(chain):
+    for L in chain.layers:
+        L["cache"].view(torch.int16 if L["cache"].element_size() == 2 else torch.int32).fill_(-1)
 
 
 def test_decode_chain_b1_one_launch(kcr):
@@ -213,6 +284,7 @@ def check_chain(wl, chain):
     h = np_bits(wl["h"]).copy()
     pos, slots = wl["positions"].numpy(), wl["slot_mapping"].numpy()
     n_slots = wl["num_blocks"] * wl["block_size"]
+    live = slots >= 0
     for i, (lw, L) in enumerate(zip(wl["layers"], chain.layers)):
         h, y_attn = oracle.add_rmsnorm(h, np_bits(lw["d_attn"]), np_bits(lw["w_attn"]), eps)
         q, k, v = workloads.qkv_views(lw["qkv"], hq, hkv, dh)
@@ -224,14 +296,15 @@ def check_chain(wl, chain):
         assert_close(L["y_mlp"].cpu().double().numpy(), y_mlp, dt, f"layer {i} y_mlp")
         assert_rope_close(L["q_out"].cpu().double().numpy(), q_rot, dt, f"layer {i} q_out")
         assert_close(L["act"].cpu().double().numpy(), act, dt, f"layer {i} act")
-        # cache: the 256 named slots hold K_rot and V; every other slot the sentinel
+        # cache: the named slots hold K_rot and V (padding tokens, slot < 0,
+        # store nothing); every other slot keeps the sentinel
         flat = L["cache"].view(2, n_slots, hkv, dh)
-        s_dev = chain.slot_mapping
+        s_dev = chain.slot_mapping[chain.slot_mapping >= 0]
         k_got = flat[0][s_dev].cpu().double().numpy()
-        assert_rope_close(k_got, k_rot, dt, f"layer {i} K slots")
-        assert torch.equal(flat[1][s_dev].view(ib).cpu(), v.contiguous().view(ib))
+        assert_rope_close(k_got, k_rot[live], dt, f"layer {i} K slots")
+        assert torch.equal(flat[1][s_dev].view(ib).cpu(), v[torch.from_numpy(live)].contiguous().view(ib))
         untouched = int((L["cache"].view(ib) == -1).sum())
-        assert untouched == L["cache"].numel() - 2 * len(slots) * hkv * dh, f"layer {i} stray writes"
+        assert untouched == L["cache"].numel() - 2 * int(live.sum()) * hkv * dh, f"layer {i} stray writes"
     # the residual after 56 fused adds is bit-exact
     assert np.array_equal(np_bits(chain.h.cpu()), h), "residual stream after the step"
     return h
