@@ -402,6 +402,11 @@ int kcr_decode_chain_b1(const kcr_chain_layer* layers, int n_layers, void* h, in
  *        valid slot store into one cache row; which one lands there is
  *        unspecified (as for kcr_rope_kvstore).
  *
+ * For both entry points, a buffer that one layer writes may not overlap any
+ * buffer of another layer (weights may be shared between layers). This is
+ * not checked: each layer's inputs are read ahead of the previous layer's
+ * ops, so such an overlap gives unspecified results.
+ *
  * Limits, alignment and aliasing as for kcr_decode_chain_b1, over the
  * batch's whole rows; batch out of range is KCR_ERR_SHAPE.
  */

@@ -18,9 +18,12 @@
 //    (the in-place update of each add) and normalises it. The row's sum of
 //    squares is reduced in-wave with DPP, then across the 16 waves through
 //    two alternating LDS slot arrays (one barrier per norm).
-//  * Each layer's loads (both deltas and weights, the token's q/k/v chunks,
-//    the gate/up vectors) are issued together before its first op runs, so
-//    one memory latency per layer is exposed rather than one per op. The
+//  * Loads are software-pipelined by half layers. The MLP half's inputs
+//    (delta, weight, the gate/up vectors) are issued together before the
+//    layer's first op; the attention half's (delta, weight, the token's
+//    q/k/v chunks) one layer ahead, as soon as the previous layer's RoPE has
+//    consumed its own. Each half's loads are therefore in flight while the
+//    other half computes, in the registers the layer already holds. The
 //    cos/sin rows of the token's position are the same for every layer and
 //    are read once.
 //  * RoPE lane mapping as in rope_kvstore.hip: a unit of LPU lanes per
@@ -112,23 +115,31 @@ __global__ __launch_bounds__(kB1Threads) void decode_chain_kernel(const ChainArg
     }
     const int iv = a.inter / kVec;
 
+    // The attention half's inputs of layer l (delta, weight, the token's
+    // q/k/v chunks). They are loaded one layer ahead: layer l + 1's are
+    // issued once layer l's RoPE has consumed its own, so they are in flight
+    // during layer l's MLP half. Every load is unconditional: lanes with
+    // nothing to load read an in-bounds clamped address and ignore the
+    // result. In straight-line code the compiler waits for exactly the loads
+    // each op needs; loads under lane-dependent branches made it wait for all
+    // of them, and for earlier stores, before every op.
+    u32x4 dA, wA, x1, x2;
+    auto load_attn = [&](int l) {
+        const kcr_chain_layer& L = a.layers[l];
+        dA = ld16_nt<T>(static_cast<const S*>(L.d_attn) + hrow, he_c);
+        wA = ld16<T>(L.w_attn, he_c);
+        const S* src = static_cast<const S*>(L.qkv) + tok * a.qkv_w + (int64_t)src_head * a.dh;
+        x1 = ld16_nt<T>(src, c0);
+        x2 = ld16_nt<T>(src, half + c0);
+    };
+    load_attn(0);
+
     for (int l = 0; l < a.n_layers; ++l) {
         const kcr_chain_layer& L = a.layers[l];
         // The token's rows of the layer's per-token tensors (uniform).
-        const S* const d_attn = static_cast<const S*>(L.d_attn) + hrow;
         const S* const d_mlp = static_cast<const S*>(L.d_mlp) + hrow;
-        const S* const qkv = static_cast<const S*>(L.qkv) + tok * a.qkv_w;
         const S* const gate_up = static_cast<const S*>(L.gate_up) + tok * 2 * (int64_t)a.inter;
-        // Every load of the layer first, unconditionally: lanes with nothing to
-        // load read an in-bounds clamped address and ignore the result. In
-        // straight-line code the compiler waits for exactly the loads each op
-        // needs; loads under lane-dependent branches made it wait for all of
-        // them, and for earlier stores, before every op.
-        const u32x4 dA = ld16_nt<T>(d_attn, he_c);
-        const u32x4 wA = ld16<T>(L.w_attn, he_c);
-        const S* src = qkv + (int64_t)src_head * a.dh;
-        const u32x4 x1 = ld16_nt<T>(src, c0);
-        const u32x4 x2 = ld16_nt<T>(src, half + c0);
+        // The MLP half's inputs, issued together before the layer's first op.
         const u32x4 dM = ld16_nt<T>(d_mlp, he_c);
         const u32x4 wM = ld16<T>(L.w_mlp, he_c);
         u32x4 gr[SWI], ur[SWI];
@@ -202,6 +213,10 @@ __global__ __launch_bounds__(kB1Threads) void decode_chain_kernel(const ChainArg
                 st16_nt<T>(dst, c0, o1);
                 st16_nt<T>(dst, half + c0, o2);
             }
+            // The next layer's attention-half inputs (the last layer reads its
+            // own again and ignores them).
+            load_attn(l + 1 < a.n_layers ? l + 1 : l);
+            asm volatile("" ::: "memory");
         }
 
         // 4. act = silu(gate) * up
