@@ -755,10 +755,13 @@ def main():
     if args.pmc_pass:
         pmc_pass()
         return
-    # The [512, D] sweep first, while the process holds nothing else: run
-    # after the chain (its 30 GB of caches and captured graphs alive), its
-    # smallest bf16 launches read 0.3 us slower.
+    # The small workloads first, while the process holds nothing else: run
+    # after the chain (its 30 GB of caches and captured graphs alive), the
+    # [512, D] sweep's smallest bf16 launches read 0.3 us slower, and the
+    # batch-1 chain's one launch 63 -> 75 us per step.
     sweep = {} if args.skip_sweep else rmsnorm_sweep(kcr, max(10, args.steps // 5))
+    token = decode_token_latency(kcr, max(10, args.steps // 2))
+    chain_b1 = decode_chain_b1(kcr, max(20, args.steps))
     t0 = time.perf_counter()
     wl = workloads.decode_chain()
     log(f"generated workload in {time.perf_counter() - t0:.1f} s")
@@ -815,8 +818,6 @@ def main():
     log("in-graph per-launch us: " + ", ".join(f"{k} {v:.2f}" for k, v in op_graph.items()))
     chain_one = decode_chain_one_launch(kcr, chain, ms * 1e3, max(20, args.steps))
     chain.reset_residual()
-    token = decode_token_latency(kcr, max(10, args.steps // 2))
-    chain_b1 = decode_chain_b1(kcr, max(20, args.steps))
     ceiling = copy_ceiling(kcr, args.kernel_iters)
     kernels = {} if args.skip_large else large_shapes(kcr, args.kernel_iters)
 
