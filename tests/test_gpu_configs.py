@@ -180,15 +180,17 @@ def test_decode_chain_batch_one_launch(kcr):
 @pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
 def test_decode_chain_batch_ragged(kcr, dt):
     """The one-launch chain at an odd batch (37 tokens) with two padding
-    tokens (slot -1), at other shapes (5 layers, hidden 512, intermediate
-    1408, 8 query / 2 KV heads of 64, block size 8), two steps in a row
-    (the residual carries over)."""
+    tokens (slot -1) and two positions outside the tables (-1 and max_pos),
+    at other shapes (5 layers, hidden 512, intermediate 1408, 8 query / 2 KV
+    heads of 64, block size 8), two steps in a row (the residual carries
+    over)."""
     from kv_cache_rmsnorm_amd.chain import DecodeChain
     say(f"batch-37 decode chain with padding tokens, one launch, {dt}")
     wl = workloads.decode_chain(layers=5, batch=37, ctx=100, dtype=dt, seed=5, hidden=512, inter=1408,
                                 hq=8, hkv=2, dh=64, block_size=8)
     wl["slot_mapping"][[3, 36]] = -1
     wl["positions"] = torch.randint(0, wl["max_pos"], (37,), generator=workloads.gen(6))
+    wl["positions"][[10, 20]] = torch.tensor([-1, wl["max_pos"]])
     chain = DecodeChain(wl, "cuda", sentinel_cache=True)
     chain.step_one_launch()
     torch.cuda.synchronize()
@@ -284,12 +286,16 @@ def check_chain(wl, chain):
     h = np_bits(wl["h"]).copy()
     pos, slots = wl["positions"].numpy(), wl["slot_mapping"].numpy()
     n_slots = wl["num_blocks"] * wl["block_size"]
-    live = slots >= 0
+    # a position outside the tables copies the token's query heads unrotated
+    # and stores nothing; a negative slot (padding) stores nothing
+    in_range = (pos >= 0) & (pos < wl["max_pos"])
+    live = (slots >= 0) & in_range
     for i, (lw, L) in enumerate(zip(wl["layers"], chain.layers)):
         h, y_attn = oracle.add_rmsnorm(h, np_bits(lw["d_attn"]), np_bits(lw["w_attn"]), eps)
         q, k, v = workloads.qkv_views(lw["qkv"], hq, hkv, dh)
         q_rot, k_rot = oracle.rope_kvstore(np_bits(q), np_bits(k), np_bits(v), pos, wl["theta"],
                                            None, None)
+        q_rot[~in_range] = q[torch.from_numpy(~in_range)].double().numpy()
         h, y_mlp = oracle.add_rmsnorm(h, np_bits(lw["d_mlp"]), np_bits(lw["w_mlp"]), eps)
         act = oracle.swiglu(np_bits(lw["gate_up"][:, :inter]), np_bits(lw["gate_up"][:, inter:]))
         assert_close(L["y_attn"].cpu().double().numpy(), y_attn, dt, f"layer {i} y_attn")
@@ -299,7 +305,7 @@ def check_chain(wl, chain):
         # cache: the named slots hold K_rot and V (padding tokens, slot < 0,
         # store nothing); every other slot keeps the sentinel
         flat = L["cache"].view(2, n_slots, hkv, dh)
-        s_dev = chain.slot_mapping[chain.slot_mapping >= 0]
+        s_dev = chain.slot_mapping[torch.from_numpy(live).to(chain.slot_mapping.device)]
         k_got = flat[0][s_dev].cpu().double().numpy()
         assert_rope_close(k_got, k_rot[live], dt, f"layer {i} K slots")
         assert torch.equal(flat[1][s_dev].view(ib).cpu(), v[torch.from_numpy(live)].contiguous().view(ib))
