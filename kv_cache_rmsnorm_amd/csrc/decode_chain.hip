@@ -33,9 +33,9 @@
 
 namespace kcr {
 
-constexpr int kB1Threads = 1024;
-constexpr int kB1Waves = kB1Threads / 64;
-constexpr int kB1MaxSwigluIters = 4;  // inter <= 4096 vectors
+constexpr int kChainThreads = 1024;
+constexpr int kChainWaves = kChainThreads / 64;
+constexpr int kChainMaxSwigluIters = 4;  // inter <= 4096 vectors
 // Tokens per launch: batch * 1024 lanes must stay below 2^32.
 constexpr int64_t kChainMaxBatch = (int64_t(1) << 22) - 1;
 
@@ -56,21 +56,21 @@ struct ChainArgs {
 // alternates between the two norms of a layer: a lane rewrites slot s only
 // after passing the barrier of the other slot, which every lane reaches
 // after its last read of slot s.
-__device__ __forceinline__ float block_sum(float v, float (*part)[kB1Waves], int slot, int wave, int lane) {
+__device__ __forceinline__ float block_sum(float v, float (*part)[kChainWaves], int slot, int wave, int lane) {
     v = wave_sum(v);
     if (lane == 0) part[slot][wave] = v;
     __syncthreads();
     float t = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kB1Waves; ++i) t += part[slot][i];
+    for (int i = 0; i < kChainWaves; ++i) t += part[slot][i];
     return t;
 }
 
 template <typename T, int SWI>
-__global__ __launch_bounds__(kB1Threads) void decode_chain_kernel(const ChainArgs a) {
+__global__ __launch_bounds__(kChainThreads) void decode_chain_kernel(const ChainArgs a) {
     using S = typename T::storage;
     constexpr int kVec = T::kVec;
-    __shared__ float part[2][kB1Waves];
+    __shared__ float part[2][kChainWaves];
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     // This workgroup's token and its row offsets (uniform).
     const int64_t tok = blockIdx.x;
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(kB1Threads) void decode_chain_kernel(const ChainArg
         u32x4 gr[SWI], ur[SWI];
 #pragma unroll
         for (int k = 0; k < SWI; ++k) {
-            const int v = tid + k * kB1Threads;
+            const int v = tid + k * kChainThreads;
             const int64_t e = v < iv ? (int64_t)v * kVec : 0;
             gr[k] = ld16_nt<T>(gate_up, e);
             ur[k] = ld16_nt<T>(gate_up, (int64_t)a.inter + e);
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(kB1Threads) void decode_chain_kernel(const ChainArg
         // 4. act = silu(gate) * up
 #pragma unroll
         for (int k = 0; k < SWI; ++k) {
-            const int v = tid + k * kB1Threads;
+            const int v = tid + k * kChainThreads;
             if (v < iv) {
                 float gf[kVec], uf[kVec], of[kVec];
                 unpack<T>(gr[k], gf);
@@ -240,12 +240,12 @@ __global__ __launch_bounds__(kB1Threads) void decode_chain_kernel(const ChainArg
 
 template <typename T>
 static int launch_chain(const ChainArgs& a, int64_t batch, void* stream) {
-    const int iters = (a.inter / T::kVec + kB1Threads - 1) / kB1Threads;
+    const int iters = (a.inter / T::kVec + kChainThreads - 1) / kChainThreads;
     const dim3 grid((uint32_t)batch);
     switch (iters <= 1 ? 1 : (iters <= 2 ? 2 : 4)) {
-        case 1: return launch(decode_chain_kernel<T, 1>, grid, dim3(kB1Threads), stream, a);
-        case 2: return launch(decode_chain_kernel<T, 2>, grid, dim3(kB1Threads), stream, a);
-        default: return launch(decode_chain_kernel<T, kB1MaxSwigluIters>, grid, dim3(kB1Threads), stream, a);
+        case 1: return launch(decode_chain_kernel<T, 1>, grid, dim3(kChainThreads), stream, a);
+        case 2: return launch(decode_chain_kernel<T, 2>, grid, dim3(kChainThreads), stream, a);
+        default: return launch(decode_chain_kernel<T, kChainMaxSwigluIters>, grid, dim3(kChainThreads), stream, a);
     }
 }
 
@@ -266,15 +266,15 @@ extern "C" int kcr_decode_chain_batch(const kcr_chain_layer* layers, int n_layer
     if (n_head % n_kv_head != 0) return KCR_ERR_HEADS;
     const size_t es = dtype_size(dtype);
     const int vec = (int)(16 / es);
-    if (hidden < 1 || hidden % vec != 0 || hidden / vec > kB1Threads) return KCR_ERR_SHAPE;
-    if (inter < 1 || inter % vec != 0 || inter / vec > kB1MaxSwigluIters * kB1Threads) return KCR_ERR_SHAPE;
+    if (hidden < 1 || hidden % vec != 0 || hidden / vec > kChainThreads) return KCR_ERR_SHAPE;
+    if (inter < 1 || inter % vec != 0 || inter / vec > kChainMaxSwigluIters * kChainThreads) return KCR_ERR_SHAPE;
     if (head_dim < 2 || head_dim % 2 != 0 || (head_dim / 2) % vec != 0 || head_dim > KCR_ROPE_MAX_HEAD_DIM)
         return KCR_ERR_SHAPE;
     if (block_size < 1 || num_blocks < 0 || max_pos < 1) return KCR_ERR_SHAPE;
     const int group = n_head / n_kv_head;
     int lpu = 1;
     while (lpu * vec < head_dim / 2) lpu *= 2;
-    if ((int64_t)n_kv_head * (group + 2) * lpu > kB1Threads) return KCR_ERR_SHAPE;
+    if ((int64_t)n_kv_head * (group + 2) * lpu > kChainThreads) return KCR_ERR_SHAPE;
     if (n_layers == 0 || batch == 0) return KCR_OK;
     if (!layers || !h || !positions || !slot_mapping || !cos_tab || !sin_tab) return KCR_ERR_NULL;
     if (!aligned16(h) || !aligned16(cos_tab) || !aligned16(sin_tab) ||
