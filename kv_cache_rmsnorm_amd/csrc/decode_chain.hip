@@ -52,6 +52,11 @@ struct ChainArgs {
     float eps;
 };
 
+// The argument-block warm-up in the kernel relies on this entry layout.
+static_assert(sizeof(kcr_chain_layer) == 88 && offsetof(kcr_chain_layer, kv_cache) == 40 &&
+                  offsetof(kcr_chain_layer, act) == 80,
+              "kcr_chain_layer: 11 pointers");
+
 // Sum over the workgroup's 1024 lanes, every lane gets the result. `slot`
 // alternates between the two norms of a layer: a lane rewrites slot s only
 // after passing the barrier of the other slot, which every lane reaches
@@ -133,6 +138,24 @@ __global__ __launch_bounds__(kChainThreads) void decode_chain_kernel(const Chain
         x2 = ld16_nt<T>(src, half + c0);
     };
     load_attn(0);
+    // The layer table sits in the kernel's argument block and each layer's
+    // pointers are first read at that layer's start, where a scalar-cache
+    // miss stalls every wave. Bring the whole table into the scalar cache
+    // now, behind the first layer's loads: the fields read here (bytes 0,
+    // 40 and 80 of each 88-byte, 8-byte-aligned entry) leave no gap of 64
+    // bytes, so every 64-byte line of the table holds one of them. The
+    // block always holds KCR_B1_MAX_LAYERS entries (unused ones zero), so
+    // every read is in bounds.
+    {
+        uintptr_t acc = 0;
+#pragma unroll
+        for (int l = 0; l < KCR_B1_MAX_LAYERS; ++l) {
+            const kcr_chain_layer& E = a.layers[l];
+            acc |= reinterpret_cast<uintptr_t>(E.d_attn) | reinterpret_cast<uintptr_t>(E.kv_cache) |
+                   reinterpret_cast<uintptr_t>(E.act);
+        }
+        asm volatile("" ::"s"(acc));
+    }
 
     for (int l = 0; l < a.n_layers; ++l) {
         const kcr_chain_layer& L = a.layers[l];
