@@ -204,3 +204,36 @@ def test_fuzz_gather(kcr, case):
             got = np_bits(out[b].cpu())
             assert np.array_equal(got[:L].view(np.uint8), ref.view(np.uint8)), f"seq {b} half {half}"
             assert not got[L:].any(), f"seq {b}: rows past the length were written"
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_fuzz_chain_one_launch(kcr, case):
+    """The one-launch decode chain (kcr_decode_chain_batch) at random
+    batches, layer counts, widths, head layouts and block sizes in every
+    dtype, with padding tokens and random positions, against the oracle run
+    layer by layer (the same check as the benchmark's chain)."""
+    from kv_cache_rmsnorm_amd.chain import DecodeChain
+    from test_gpu_configs import check_chain
+    rng = np.random.default_rng(10000 + case)
+    dt = DTS[case % 3]
+    vec = 16 // dt.itemsize
+    hidden = vec * int(rng.integers(1, 1025))
+    inter = vec * int(rng.choice([int(rng.integers(1, 1025)), int(rng.integers(1025, 4097))]))
+    hkv = int(rng.choice([1, 2, 4]))
+    hq = hkv * int(rng.choice([1, 2, 4, 6]))
+    dh = int(rng.choice([d for d in (16, 32, 64, 128, 256) if (d // 2) % vec == 0]))
+    batch = int(rng.choice([1, int(rng.integers(2, 40)), int(rng.integers(200, 300))]))
+    layers = int(rng.integers(1, 5))
+    bs = int(rng.choice([1, 8, 16]))
+    say(f"chain case {case}: dt={dt} batch={batch} layers={layers} hidden={hidden} inter={inter} "
+        f"hq={hq} hkv={hkv} dh={dh} block_size={bs}")
+    wl = workloads.decode_chain(layers=layers, batch=batch, ctx=int(rng.integers(1, 60)), dtype=dt,
+                                seed=11000 + case, hidden=hidden, inter=inter, hq=hq, hkv=hkv, dh=dh,
+                                block_size=bs)
+    wl["positions"] = torch.from_numpy(rng.integers(0, wl["max_pos"], batch))
+    pad = rng.random(batch) < 0.1
+    wl["slot_mapping"][torch.from_numpy(pad)] = -1
+    chain = DecodeChain(wl, "cuda", sentinel_cache=True)
+    chain.step_one_launch()
+    torch.cuda.synchronize()
+    check_chain(wl, chain)
