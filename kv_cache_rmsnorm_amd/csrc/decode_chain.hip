@@ -26,6 +26,9 @@
 //    other half computes, in the registers the layer already holds. The
 //    cos/sin rows of the token's position are the same for every layer and
 //    are read once.
+//  * The per-layer pointer table travels in the argument block; it is read
+//    into the scalar cache at kernel start, so no layer's start waits on a
+//    scalar-cache miss for its pointers.
 //  * RoPE lane mapping as in rope_kvstore.hip: a unit of LPU lanes per
 //    virtual head in KV-group order, lane c owning chunk c of both halves.
 #include "kcr_device.h"
