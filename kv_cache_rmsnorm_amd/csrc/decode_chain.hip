@@ -5,7 +5,8 @@
 // add + RMSNorm, SwiGLU (section 2).
 //
 // gfx950 design
-//  * One workgroup of 1024 lanes per token runs every op of every layer in
+//  * One workgroup per token (512 lanes where the token's row, RoPE units
+//    and SwiGLU vectors fit, else 1024) runs every op of every layer in
 //    turn; ops are separated by workgroup barriers only, so the 4 launches
 //    per layer of the separate entry points (and their graph-node or host
 //    launch cost) become one launch per step. Every op of the chain is
@@ -16,7 +17,7 @@
 //  * The residual h lives in registers for the whole step: lane l owns
 //    16-byte vector l of the row, adds delta to it, stores the rounded sum
 //    (the in-place update of each add) and normalises it. The row's sum of
-//    squares is reduced in-wave with DPP, then across the 16 waves through
+//    squares is reduced in-wave with DPP, then across the waves through
 //    two alternating LDS slot arrays (one barrier per norm).
 //  * Loads are software-pipelined by half layers. The MLP half's inputs
 //    (delta, weight, the gate/up vectors) are issued together before the
@@ -36,9 +37,12 @@
 
 namespace kcr {
 
+// Lanes per token: 1024 at most (the shape limits below), 512 where the
+// row, the RoPE units and the SwiGLU fit (fewer waves per barrier; measured
+// faster at every batch).
 constexpr int kChainThreads = 1024;
-constexpr int kChainWaves = kChainThreads / 64;
-constexpr int kChainMaxSwigluIters = 4;  // inter <= 4096 vectors
+constexpr int kChainSmallThreads = 512;
+constexpr int kChainMaxSwigluIters = 4;  // inter <= 4096 vectors at 1024 lanes
 // Tokens per launch: batch * 1024 lanes must stay below 2^32.
 constexpr int64_t kChainMaxBatch = (int64_t(1) << 22) - 1;
 
@@ -60,25 +64,27 @@ static_assert(sizeof(kcr_chain_layer) == 88 && offsetof(kcr_chain_layer, kv_cach
                   offsetof(kcr_chain_layer, act) == 80,
               "kcr_chain_layer: 11 pointers");
 
-// Sum over the workgroup's 1024 lanes, every lane gets the result. `slot`
+// Sum over the workgroup's lanes, every lane gets the result. `slot`
 // alternates between the two norms of a layer: a lane rewrites slot s only
 // after passing the barrier of the other slot, which every lane reaches
 // after its last read of slot s.
-__device__ __forceinline__ float block_sum(float v, float (*part)[kChainWaves], int slot, int wave, int lane) {
+template <int WAVES>
+__device__ __forceinline__ float block_sum(float v, float (*part)[WAVES], int slot, int wave, int lane) {
     v = wave_sum(v);
     if (lane == 0) part[slot][wave] = v;
     __syncthreads();
     float t = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kChainWaves; ++i) t += part[slot][i];
+    for (int i = 0; i < WAVES; ++i) t += part[slot][i];
     return t;
 }
 
-template <typename T, int SWI>
-__global__ __launch_bounds__(kChainThreads) void decode_chain_kernel(const ChainArgs a) {
+template <typename T, int SWI, int THREADS>
+__global__ __launch_bounds__(THREADS) void decode_chain_kernel(const ChainArgs a) {
     using S = typename T::storage;
     constexpr int kVec = T::kVec;
-    __shared__ float part[2][kChainWaves];
+    constexpr int kWaves = THREADS / 64;
+    __shared__ float part[2][kWaves];
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     // This workgroup's token and its row offsets (uniform).
     const int64_t tok = blockIdx.x;
@@ -171,7 +177,7 @@ __global__ __launch_bounds__(kChainThreads) void decode_chain_kernel(const Chain
         u32x4 gr[SWI], ur[SWI];
 #pragma unroll
         for (int k = 0; k < SWI; ++k) {
-            const int v = tid + k * kChainThreads;
+            const int v = tid + k * THREADS;
             const int64_t e = v < iv ? (int64_t)v * kVec : 0;
             gr[k] = ld16_nt<T>(gate_up, e);
             ur[k] = ld16_nt<T>(gate_up, (int64_t)a.inter + e);
@@ -207,7 +213,7 @@ __global__ __launch_bounds__(kChainThreads) void decode_chain_kernel(const Chain
 #pragma unroll
                 for (int e = 0; e < kVec; ++e) ss += xf[e] * xf[e];
             }
-            const float tot = block_sum(ss, part, n, wave, lane);
+            const float tot = block_sum<kWaves>(ss, part, n, wave, lane);
             if (own_h) {
                 const float rs = __builtin_amdgcn_rsqf(tot / (float)a.hidden + a.eps);
                 float wf[kVec], yf[kVec];
@@ -248,7 +254,7 @@ __global__ __launch_bounds__(kChainThreads) void decode_chain_kernel(const Chain
         // 4. act = silu(gate) * up
 #pragma unroll
         for (int k = 0; k < SWI; ++k) {
-            const int v = tid + k * kChainThreads;
+            const int v = tid + k * THREADS;
             if (v < iv) {
                 float gf[kVec], uf[kVec], of[kVec];
                 unpack<T>(gr[k], gf);
@@ -264,15 +270,27 @@ __global__ __launch_bounds__(kChainThreads) void decode_chain_kernel(const Chain
     }
 }
 
+template <typename T, int THREADS>
+static int launch_chain_t(const ChainArgs& a, int64_t batch, void* stream) {
+    const int iters = (a.inter / T::kVec + THREADS - 1) / THREADS;
+    const dim3 grid((uint32_t)batch), block(THREADS);
+    switch (iters) {
+        case 1: return launch(decode_chain_kernel<T, 1, THREADS>, grid, block, stream, a);
+        case 2: return launch(decode_chain_kernel<T, 2, THREADS>, grid, block, stream, a);
+        case 3: return launch(decode_chain_kernel<T, 3, THREADS>, grid, block, stream, a);
+        default: return launch(decode_chain_kernel<T, kChainMaxSwigluIters, THREADS>, grid, block, stream, a);
+    }
+}
+
+// 512 lanes when the token's row, its RoPE units and its SwiGLU vectors (at
+// most 4 per lane) fit, else 1024.
 template <typename T>
 static int launch_chain(const ChainArgs& a, int64_t batch, void* stream) {
-    const int iters = (a.inter / T::kVec + kChainThreads - 1) / kChainThreads;
-    const dim3 grid((uint32_t)batch);
-    switch (iters <= 1 ? 1 : (iters <= 2 ? 2 : 4)) {
-        case 1: return launch(decode_chain_kernel<T, 1>, grid, dim3(kChainThreads), stream, a);
-        case 2: return launch(decode_chain_kernel<T, 2>, grid, dim3(kChainThreads), stream, a);
-        default: return launch(decode_chain_kernel<T, kChainMaxSwigluIters>, grid, dim3(kChainThreads), stream, a);
-    }
+    const bool small = a.hidden / T::kVec <= kChainSmallThreads &&
+                       a.hkv * (a.group + 2) * a.lpu <= kChainSmallThreads &&
+                       a.inter / T::kVec <= kChainMaxSwigluIters * kChainSmallThreads;
+    return small ? launch_chain_t<T, kChainSmallThreads>(a, batch, stream)
+                 : launch_chain_t<T, kChainThreads>(a, batch, stream);
 }
 
 }  // namespace kcr
