@@ -273,8 +273,9 @@ def graph_op_us(kcr, chain, reps: int):
 
 
 def rmsnorm_sweep(kcr, reps: int):
-    """RMSNorm over [2 x 256, D] rows, the microbenchmark shape of the Zhihu
-    "RMSNorm in Triton" page (D = 128 ... 8196; FP32, FP16, BF16). Each point
+    """RMSNorm over [2 x 256, D] rows, the microbenchmark shape of the csdn
+    page "Qwen3 from scratch (4-2): RMSNorm with Triton", section
+    "performance comparison" (D = 128 ... 8196; FP32, FP16, BF16). Each point
     is the per-launch time inside a captured graph of 64 launches over 16
     rotated buffer sets, so it includes the graph's per-node launch cost;
     GB/s counts the algorithmic bytes (x read, y written, w once)."""

@@ -403,9 +403,12 @@ int kcr_decode_chain_b1(const kcr_chain_layer* layers, int n_layers, void* h, in
  *        unspecified (as for kcr_rope_kvstore).
  *
  * For both entry points, a buffer that one layer writes may not overlap any
- * buffer of another layer (weights may be shared between layers). This is
- * not checked: each layer's inputs are read ahead of the previous layer's
- * ops, so such an overlap gives unspecified results.
+ * buffer of another layer, since each layer's inputs are read ahead of the
+ * previous layer's ops (KCR_ERR_ALIAS, checked before anything is launched).
+ * Inputs may be shared between layers (e.g. one weight), and so may a
+ * cache when the layers name exactly the same cache range: the chain never
+ * reads the cache, and the last layer's K/V rows land there, as with the
+ * separate calls.
  *
  * Limits, alignment and aliasing as for kcr_decode_chain_b1, over the
  * batch's whole rows; batch out of range is KCR_ERR_SHAPE.
@@ -420,7 +423,10 @@ int kcr_decode_chain_batch(const kcr_chain_layer* layers, int n_layers, int64_t 
  * kcr_copy -- plain streaming copy of `bytes` bytes (a multiple of 16, both
  * pointers 16-byte aligned, no overlap). It moves data with the same 16-byte
  * vector loads and stores as the kernels above and serves as the measured
- * bandwidth ceiling and as the reference for hardware byte counters.
+ * bandwidth ceiling and as the reference for hardware byte counters. A copy
+ * of more than 2^32 - 64 vectors (64 GiB) runs as several launches over
+ * consecutive ranges; a timing arming (kcr_time_next_launch) then stamps
+ * the first of them only.
  */
 int kcr_copy(void* dst, const void* src, int64_t bytes, void* stream);
 

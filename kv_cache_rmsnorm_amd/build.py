@@ -34,10 +34,18 @@ CXXFLAGS = [
 NORM_VARIANTS = [(t, add) for t in ("Bf16", "F16", "F32") for add in (0, 1)]
 
 
+def _headers_mtime() -> float:
+    hdrs = glob.glob(os.path.join(CSRC, "*.h")) + glob.glob(os.path.join(INCLUDE, "*.h"))
+    return max(os.path.getmtime(h) for h in hdrs)
+
+
 def _compile(job) -> str:
-    src, defines = job
+    src, defines, incremental = job
     tag = "".join(f"_{v}" for _, v in defines)
     obj = os.path.join(OUT_DIR, os.path.basename(src) + tag + ".o")
+    if incremental and os.path.exists(obj) and \
+            os.path.getmtime(obj) > max(os.path.getmtime(src), _headers_mtime()):
+        return obj
     cmd = [HIPCC, *CXXFLAGS, *[f"-D{k}={v}" for k, v in defines], "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -50,13 +58,15 @@ def _compile(job) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every csrc/*.hip for gfx950 and link libkcr.so (always rebuilds)."""
+def build(verbose: bool = True, incremental: bool = False) -> str:
+    """Compile every csrc/*.hip for gfx950 and link libkcr.so. Always
+    rebuilds every object unless `incremental`, which keeps objects newer
+    than their source and every header."""
     os.makedirs(OUT_DIR, exist_ok=True)
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     inst = os.path.join(CSRC, "norm_inst.hip")
-    work = [(s, ()) for s in sources if s != inst]
-    work += [(inst, (("KCR_NORM_T", t), ("KCR_NORM_ADD", add))) for t, add in NORM_VARIANTS]
+    work = [(s, (), incremental) for s in sources if s != inst]
+    work += [(inst, (("KCR_NORM_T", t), ("KCR_NORM_ADD", add)), incremental) for t, add in NORM_VARIANTS]
     # the norm instantiations are the slowest; start them first
     work.sort(key=lambda j: j[0] != inst)
     jobs = min(len(work), max(1, min(8, os.cpu_count() or 1)))
@@ -71,4 +81,4 @@ def build(verbose: bool = True) -> str:
 
 
 if __name__ == "__main__":
-    build()
+    build(incremental="--incremental" in sys.argv)

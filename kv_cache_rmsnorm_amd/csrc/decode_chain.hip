@@ -32,6 +32,8 @@
 //    scalar-cache miss for its pointers.
 //  * RoPE lane mapping as in rope_kvstore.hip: a unit of LPU lanes per
 //    virtual head in KV-group order, lane c owning chunk c of both halves.
+#include <algorithm>
+
 #include "kcr_device.h"
 #include "kcr_host.h"
 
@@ -293,6 +295,41 @@ static int launch_chain(const ChainArgs& a, int64_t batch, void* stream) {
                  : launch_chain_t<T, kChainThreads>(a, batch, stream);
 }
 
+// One per-layer buffer of a chain call: its byte range, its layer, its
+// role (the order of the span lists in kcr_decode_chain_batch: d_attn,
+// w_attn, qkv, d_mlp, w_mlp, gate_up, then y_attn, q_out, kv_cache, y_mlp,
+// act) and whether the chain writes it.
+struct LayerSpan {
+    Span s;
+    int layer, role;
+    bool written;
+};
+constexpr int kLayerInputs = 6, kLayerBufs = 11, kRoleCache = 8;
+
+// Cross-layer rule of the one-launch chain: each layer's inputs are read
+// ahead of the previous layer's ops, so a buffer one layer writes may not
+// overlap any buffer of another layer. Inputs may be shared (e.g. one
+// weight for several layers), and so may a cache, when the layers name the
+// same cache range: the chain never reads the cache, and each token's cache
+// rows are written by the same lanes layer after layer, so the last layer's
+// rows land there, as with the separate calls. Overlaps within a layer are
+// checked by the caller. Sort-and-sweep over the ranges, O(n log n) plus the
+// overlapping pairs.
+static bool layers_disjoint(LayerSpan* v, int n) {
+    std::sort(v, v + n, [](const LayerSpan& x, const LayerSpan& y) { return x.s.lo < y.s.lo; });
+    for (int i = 0; i < n; ++i) {
+        if (v[i].s.lo == v[i].s.hi) continue;
+        for (int j = i + 1; j < n && v[j].s.lo < v[i].s.hi; ++j) {
+            if (v[j].s.lo == v[j].s.hi || v[i].layer == v[j].layer) continue;
+            if (!v[i].written && !v[j].written) continue;
+            const bool same_cache = v[i].role == kRoleCache && v[j].role == kRoleCache &&
+                                    v[i].s.lo == v[j].s.lo && v[i].s.hi == v[j].s.hi;
+            if (!same_cache) return false;
+        }
+    }
+    return true;
+}
+
 }  // namespace kcr
 
 using namespace kcr;
@@ -333,6 +370,9 @@ extern "C" int kcr_decode_chain_batch(const kcr_chain_layer* layers, int n_layer
     const Span ss = span2d(sin_tab, 1, 0, max_pos * (head_dim / 2), 4);
     const Span sp = span2d(positions, 1, 0, B, 8), sm = span2d(slot_mapping, 1, 0, B, 8);
     ChainArgs a{};
+    // Every layer's buffers, for the cross-layer check below.
+    LayerSpan all[KCR_B1_MAX_LAYERS * kLayerBufs];
+    int n_all = 0;
     for (int l = 0; l < n_layers; ++l) {
         const kcr_chain_layer& L = layers[l];
         const void* ptrs[] = {L.d_attn, L.w_attn, L.y_attn, L.qkv, L.q_out, L.d_mlp, L.w_mlp, L.y_mlp,
@@ -360,8 +400,13 @@ extern "C" int kcr_decode_chain_batch(const kcr_chain_layer* layers, int n_layer
             for (int j = i + 1; j < n_out; ++j)
                 if (overlap(out[i], out[j])) return KCR_ERR_ALIAS;
         }
+        const Span mine[kLayerBufs] = {in[0], in[1], in[2], in[3], in[4], in[5],
+                                       out[1], out[2], out[3], out[4], out[5]};
+        for (int i = 0; i < kLayerBufs; ++i)
+            all[n_all++] = LayerSpan{mine[i], l, i, i >= kLayerInputs};
         a.layers[l] = L;
     }
+    if (!layers_disjoint(all, n_all)) return KCR_ERR_ALIAS;
     if (device_cus() <= 0) return KCR_ERR_DEVICE;
     a.h = h;
     a.pos = positions;

@@ -238,6 +238,113 @@ static int dispatch_rope_lpu(const RopeArgs& a, int64_t T_tokens, void* stream) 
     return KCR_ERR_SHAPE;
 }
 
+// Decode batches: one workgroup per token, LPU = the chunks of half a head
+// (a power of two), lanes u * LPU .. u * LPU + LPU - 1 on virtual head u in
+// KV-group order. The token index is the workgroup index, so its position
+// and slot are scalar loads and every lane's addresses follow from the
+// lane number alone; lanes past the token's last head (the workgroup is a
+// whole number of waves) repeat its last head and store nothing. Straight-
+// line code with no early exit: in the 28-layer, batch-256 decode chain on
+// MI355X this took the step 5-7 us below the unit kernel above at the same
+// work split.
+template <typename T, int LPU, bool QKN>
+__global__ __launch_bounds__(1024) void rope_token_kernel(const RopeArgs a) {
+    using S = typename T::storage;
+    constexpr int kVec = T::kVec;
+    const int tid = threadIdx.x, c = tid % LPU, u0 = tid / LPU;
+    const bool on = u0 < a.nvh;
+    const int u = on ? u0 : a.nvh - 1;
+    const int half = a.dh >> 1;
+    const int64_t t = blockIdx.x;
+    const int g = (int)fastdiv((uint32_t)u, a.gsize);
+    const int r = u - g * (int)a.gsize.d;
+    const int kind = r < a.group ? 0 : (r == a.group ? 1 : 2);  // query, K, V
+    const int hh = g * a.group + r;
+    const S* base = static_cast<const S*>(kind == 0 ? a.q : (kind == 1 ? a.k : a.v));
+    const int64_t ts = kind == 0 ? a.q_ts : (kind == 1 ? a.k_ts : a.v_ts);
+    const int64_t hs = kind == 0 ? a.q_hs : (kind == 1 ? a.k_hs : a.v_hs);
+    const S* src = base + t * ts + (int64_t)(kind == 0 ? hh : g) * hs;
+    const int64_t p = a.pos[t], slot = a.slots[t];
+    const int c0 = c * kVec;
+    const u32x4 x1 = ld16_nt<T>(src, c0), x2 = ld16_nt<T>(src, half + c0);
+    // Compiler-only barrier: the head loads stay ahead of everything that
+    // waits for the position.
+    asm volatile("" ::: "memory");
+    float w1[kVec], w2[kVec];
+    if constexpr (QKN) {
+        const void* wp = kind == 1 ? a.k_w : a.q_w;
+        unpack<T>(ld16<T>(wp, c0), w1);
+        unpack<T>(ld16<T>(wp, half + c0), w2);
+    }
+    const bool p_ok = p >= 0 && p < a.max_pos;
+    const int64_t pc = p_ok ? p : 0;
+    const float* cr = a.cos_t + pc * half + c0;
+    const float* sr = a.sin_t + pc * half + c0;
+    float cs[kVec], sn[kVec];
+#pragma unroll
+    for (int i = 0; i < kVec; i += 4) {
+        const u32x4 cv = *reinterpret_cast<const u32x4*>(cr + i);
+        const u32x4 sv = *reinterpret_cast<const u32x4*>(sr + i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            cs[i + e] = __uint_as_float(cv[e]);
+            sn[i + e] = __uint_as_float(sv[e]);
+        }
+    }
+    float f1[kVec], f2[kVec], r1[kVec], r2[kVec];
+    unpack<T>(x1, f1);
+    unpack<T>(x2, f2);
+    if constexpr (QKN) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) ss += f1[e] * f1[e] + f2[e] * f2[e];
+        ss = group_sum<LPU>(ss);
+        const float rs = __builtin_amdgcn_rsqf(ss / (float)a.dh + a.eps);
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+            f1[e] = f1[e] * rs * w1[e];
+            f2[e] = f2[e] * rs * w2[e];
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) {
+        r1[e] = f1[e] * cs[e] - f2[e] * sn[e];
+        r2[e] = f2[e] * cs[e] + f1[e] * sn[e];
+    }
+    // Q and K rotate; V (and Q at an out-of-range position) keep their bits.
+    const bool rot = kind < 2 && p_ok;
+    const u32x4 o1 = rot ? pack<T>(r1) : x1, o2 = rot ? pack<T>(r2) : x2;
+    const bool store_kv = p_ok && slot >= 0 && slot < a.n_slots;
+    S* dst = kind == 0 ? static_cast<S*>(a.q_out) + (t * a.hq + hh) * a.dh
+                       : static_cast<S*>(a.cache) +
+                             (((int64_t)(kind - 1) * a.n_slots + (store_kv ? slot : 0)) * a.hkv + g) * (int64_t)a.dh;
+    if (on && (kind == 0 || store_kv)) {
+        st16_nt<T>(dst, c0, o1);
+        st16_nt<T>(dst, half + c0, o2);
+    }
+}
+
+// One workgroup per token when half a head is a power-of-two number of
+// chunks and the token's virtual heads fit one workgroup; returns 1 when the
+// call does not qualify.
+template <typename T, bool QKN>
+static int launch_rope_token(const RopeArgs& a, int64_t T_tokens, void* stream) {
+    const int chunks = (a.dh / 2) / T::kVec;
+    const int lanes = a.nvh * chunks;
+    if ((chunks & (chunks - 1)) != 0 || lanes > 1024) return 1;
+    const dim3 grid((uint32_t)T_tokens), block((uint32_t)((lanes + 63) / 64 * 64));
+    switch (chunks) {
+        case 1: return launch(rope_token_kernel<T, 1, QKN>, grid, block, stream, a);
+        case 2: return launch(rope_token_kernel<T, 2, QKN>, grid, block, stream, a);
+        case 4: return launch(rope_token_kernel<T, 4, QKN>, grid, block, stream, a);
+        case 8: return launch(rope_token_kernel<T, 8, QKN>, grid, block, stream, a);
+        case 16: return launch(rope_token_kernel<T, 16, QKN>, grid, block, stream, a);
+        case 32: return launch(rope_token_kernel<T, 32, QKN>, grid, block, stream, a);
+        case 64: return launch(rope_token_kernel<T, 64, QKN>, grid, block, stream, a);
+    }
+    return 1;
+}
+
 // Decode batches (up to 4096 tokens): one virtual head per unit spreads the
 // work over the most workgroups, and 128-lane workgroups measured 2.8 us
 // faster per step than 256-lane ones in the 28-layer, batch-256 decode chain
@@ -250,8 +357,10 @@ constexpr int64_t kRopeSmallBatch = 4096;
 
 template <typename T, bool QKN>
 static int dispatch_rope(const RopeArgs& a, int64_t T_tokens, void* stream) {
-    return T_tokens <= kRopeSmallBatch ? dispatch_rope_lpu<T, 1, QKN, 128>(a, T_tokens, stream)
-                                       : dispatch_rope_lpu<T, 2, QKN, 256>(a, T_tokens, stream);
+    if (T_tokens > kRopeSmallBatch) return dispatch_rope_lpu<T, 2, QKN, 256>(a, T_tokens, stream);
+    const int rc = launch_rope_token<T, QKN>(a, T_tokens, stream);
+    if (rc <= 0) return rc;
+    return dispatch_rope_lpu<T, 1, QKN, 128>(a, T_tokens, stream);
 }
 
 // ---------------------------------------------------------- cos/sin tables

@@ -74,9 +74,17 @@ extern "C" int kcr_copy(void* dst, const void* src, int64_t bytes, void* stream)
     if (overlap(span2d(dst, 1, 0, bytes, 1), span2d(src, 1, 0, bytes, 1))) return KCR_ERR_ALIAS;
     const int cus = device_cus();
     if (cus <= 0) return KCR_ERR_DEVICE;
-    CopyArgs a{static_cast<u32x4*>(dst), static_cast<const u32x4*>(src), bytes / 16};
-    if (a.n > (int64_t)0x7FFFFFFF * 64) return KCR_ERR_SHAPE;
-    return launch(copy_kernel, dim3((uint32_t)((a.n + 63) / 64)), dim3(64), stream, a);
+    // A grid holds at most 2^32 - 1 work-items: a copy of more vectors than
+    // that (64 GiB) is split into launches over consecutive ranges.
+    constexpr int64_t kPerLaunch = (int64_t)(0xFFFFFFFFu / 64) * 64;
+    const int64_t n = bytes / 16;
+    for (int64_t off = 0; off < n; off += kPerLaunch) {
+        const CopyArgs a{static_cast<u32x4*>(dst) + off, static_cast<const u32x4*>(src) + off,
+                         n - off < kPerLaunch ? n - off : kPerLaunch};
+        const int rc = launch(copy_kernel, dim3((uint32_t)((a.n + 63) / 64)), dim3(64), stream, a);
+        if (rc != KCR_OK) return rc;
+    }
+    return KCR_OK;
 }
 
 extern "C" int kcr_device_cus(void) { return device_cus(); }

@@ -368,3 +368,65 @@ def test_decode_chain_batch_validation(lib):
     assert call(4, layers=bad) == ALIAS
     assert call(2, layers=bad) == DEVICE
     assert call(4, h=H + A - 2 * 1536 * 2) == ALIAS   # h's last rows over positions
+
+
+def test_decode_chain_cross_layer_alias(lib):
+    """A buffer one layer of the one-launch chain writes may not overlap any
+    buffer of another layer (the chain reads each layer's inputs ahead of
+    the previous layer's ops): refused with ALIAS before any launch. Shared
+    inputs (weights, even every input) and one cache named by several layers
+    stay allowed."""
+    import ctypes
+    f = lib.kcr_decode_chain_batch
+
+    class Layer(ctypes.Structure):
+        _fields_ = [(f"p{i}", ctypes.c_void_p) for i in range(11)]
+
+    def table(n, base=1 << 30, step=1 << 22):
+        arr = (Layer * n)()
+        for i in range(n):
+            arr[i] = Layer(*[base + (i * 11 + j) * step for j in range(11)])
+        return arr
+
+    H = 1 << 34
+    # pointer roles in kcr_chain_layer order
+    D_ATTN, W_ATTN, Y_ATTN, QKV, Q_OUT, CACHE, D_MLP, W_MLP, Y_MLP, GATE_UP, ACT = range(11)
+
+    def call(layers, n=3, batch=4):
+        return f(ctypes.cast(layers, ctypes.c_void_p), n, batch, H, 1536, 8960, 12, 2, 128, H + A,
+                 H + A + 64, H + 2 * A, H + 8 * A, 4097, 16, 64, 1e-6, BF16, None)
+
+    def with_(l, role, other_l, other_role, off=0):
+        t = table(3)
+        setattr(t[l], f"p{role}", getattr(t[other_l], f"p{other_role}") + off)
+        return t
+
+    assert call(table(3)) == DEVICE
+    # layer 0's act read back as layer 1's d_attn / qkv / gate_up
+    assert call(with_(1, D_ATTN, 0, ACT)) == ALIAS
+    assert call(with_(2, QKV, 0, Y_MLP)) == ALIAS
+    assert call(with_(1, GATE_UP, 0, Q_OUT, off=1024)) == ALIAS
+    # layer 1 writing over an input of layer 0 (a later layer's output)
+    assert call(with_(0, D_MLP, 1, Y_ATTN)) == ALIAS
+    # two layers writing one output buffer, or an output over another layer's cache
+    assert call(with_(1, Y_ATTN, 0, Y_ATTN)) == ALIAS
+    assert call(with_(2, ACT, 0, CACHE, off=4096)) == ALIAS
+    # the same range on a later row only: refused at batch 4, not at batch 1
+    row = 1536 * 2
+    assert call(with_(1, D_ATTN, 0, Y_MLP, off=3 * row)) == ALIAS
+    assert call(with_(1, D_ATTN, 0, Y_MLP, off=3 * row), batch=1) == DEVICE
+    # shared inputs: one weight pair for all layers, one gate_up for two layers
+    t = table(3)
+    for i in range(3):
+        t[i].p1, t[i].p7 = t[0].p1, t[0].p1
+    t[2].p9 = t[1].p9
+    assert call(t) == DEVICE
+    # a cache shared by every layer, but not a cache that only partly overlaps
+    t = table(3)
+    t[1].p5 = t[2].p5 = t[0].p5
+    assert call(t) == DEVICE
+    assert call(with_(1, CACHE, 0, CACHE, off=4096)) == ALIAS
+    # the same checks through the batch-1 entry point
+    assert lib.kcr_decode_chain_b1(ctypes.cast(with_(1, D_ATTN, 0, ACT), ctypes.c_void_p), 3, H, 1536, 8960,
+                                   12, 2, 128, H + A, H + A + 64, H + 2 * A, H + 8 * A, 4097, 16, 64, 1e-6,
+                                   BF16, None) == ALIAS

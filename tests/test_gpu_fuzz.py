@@ -105,6 +105,41 @@ def test_fuzz_norms(kcr, case):
     assert_close(y.cpu().double().numpy(), y_ref, dt, f"norm case {case}")
 
 
+@pytest.mark.parametrize("case", range(24))
+def test_fuzz_norm_wave_rows(kcr, case):
+    """Small calls whose rows are exactly 64 * VPT 16-byte vectors (VPT 1..8)
+    take the one-wave-per-row kernel: every VPT in every dtype, plain and
+    add, with row strides, buffer offsets and in-place output."""
+    rng = np.random.default_rng(12000 + case)
+    dt = DTS[case % 3]
+    vpt = 1 + (case // 3) % 8
+    vec = 16 // dt.itemsize
+    d = 64 * vpt * vec
+    rows = int(rng.choice([1, int(rng.integers(2, 64)), int(rng.integers(200, 400))]))
+    add = bool(case % 2)
+    pad = int(rng.choice([0, 8, 32])) * (2 if dt.itemsize == 2 else 1)
+    off = int(rng.choice([0, 8])) * (2 if dt.itemsize == 2 else 1)
+    in_place = (not add) and bool(rng.integers(0, 2))
+    say(f"wave-row case {case}: dt={dt} d={d} rows={rows} add={add} pad={pad} off={off} in_place={in_place}")
+    g = workloads.gen(13000 + case)
+    x0 = (workloads.randn([rows, d], g) * float(rng.choice([1.0, 30.0]))).to(dt)
+    w0 = (0.5 + torch.rand([d], generator=g)).to(dt)
+    eps = float(np.float32(1e-6))
+    x = strided(x0, d + pad, off)
+    y = x if in_place else strided(torch.zeros_like(x0), d + pad, off)
+    w = w0.cuda()
+    if add:
+        d0 = workloads.randn([rows, d], g).to(dt)
+        dl = strided(d0, d + pad, off)
+        kcr.add_rmsnorm(x, dl, w, eps, out=y)
+        x_ref, y_ref = oracle.add_rmsnorm(np_bits(x0), np_bits(d0), np_bits(w0), eps)
+        assert np.array_equal(np_bits(x.cpu()).view(np.uint8), x_ref.view(np.uint8)), "residual"
+    else:
+        kcr.rmsnorm(x, w, eps, out=y)
+        y_ref = oracle.rmsnorm(np_bits(x0), np_bits(w0), eps)
+    assert_close(y.cpu().double().numpy(), y_ref, dt, f"wave-row case {case}")
+
+
 @pytest.mark.parametrize("case", range(36))
 def test_fuzz_gated(kcr, case):
     rng = np.random.default_rng(3000 + case)
