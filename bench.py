@@ -11,19 +11,25 @@ HBM before timing starts. The timed step is a captured HIP graph replay.
 Prints ONE JSON line:
   value        algorithmic bytes of a step / step time (GB/s), whole job
   ms_per_step  decode-step fused-op latency (graph replay)
-  roofline     dominant kernel (swiglu at the chain's shape): algorithmic
-               bytes per launch / its mean duration, measured with events
-               stamped at kernel start and end (hipExtLaunchKernel) in whole
-               steps that run back to back behind graph replays
+  roofline     the step's dominant kernel: the chain op with the largest
+               summed kernel time per step (durations from events stamped
+               at each kernel's start and end, hipExtLaunchKernel, in whole
+               steps that run back to back behind graph replays); its
+               algorithmic bytes per launch / its mean duration, with every
+               chain op's share and fraction beside it
   cpu_baseline the CPU fp64 oracle on a bounded sample of the same workload;
                per_config: the oracle at each parity-shape config, with
                every oracle thread and with one
   kernels      each kernel at its large shape on cold, rotated buffers
   ceiling      1 GiB device copies: the library's copy kernel and hipMemcpy
-  decode_token_b1  per-op latency of the batch-1 decode token
+  decode_token_b1  per-op latency of the batch-1 decode token (per launch in
+               a graph, and event-stamped durations, which include the
+               stamps' own cost)
   decode_chain_b1  the 28-layer chain at batch 1: graph of 112 launches vs one launch
   decode_chain_b256_one_launch  the timed step's chain (batch 256) as one launch,
-               one workgroup per token, beside the graph of 112 launches
+               one workgroup per token, beside the graph of 112 launches; its
+               rate over its own algorithmic bytes (h read once per token)
+               and over the counter-measured HBM traffic
   source_sha256    hash of the library's sources the line was measured with
 """
 from __future__ import annotations
@@ -240,6 +246,59 @@ def large_shapes(kcr, iters: int):
     return out
 
 
+def chain_roofline(chain, op_graph: dict, per_op: dict, n_steps: int) -> dict:
+    """The roofline object for the step's dominant kernel: the chain op with
+    the largest kernel time per step. A launch's time is its per-launch time
+    inside a captured graph of that op's 28 launches on the chain's buffers
+    (HIP events on the launch stream around graph replays), which matches
+    the rocprofv3 trace of the timed replays; HIP events stamped at a single
+    kernel's start and end have a floor near 4 us on this part, so those
+    (per_op, from whole eager steps) are reported beside it only. Every
+    chain op is listed with its launches, time share and fraction of peak."""
+    from kv_cache_rmsnorm_amd.chain import norm_bytes, rope_bytes, swiglu_bytes
+    import torch
+    B, hid, inter = chain.h.shape[0], chain.hidden, chain.inter
+    s = chain.h.element_size()
+    distinct = int(torch.unique(chain.positions).numel())
+    nbytes = dict(add_rmsnorm=norm_bytes(B, hid, s, True),
+                  rope_kvstore=rope_bytes(B, chain.hq, chain.hkv, chain.dh, s, distinct),
+                  swiglu=swiglu_bytes(B, inter, s))
+    shapes = dict(add_rmsnorm=f"x, delta [{B}, {hid}] bf16 -> x, y",
+                  rope_kvstore=f"{B} tokens, {chain.hq}q/{chain.hkv}kv heads x{chain.dh}, bf16, paged store",
+                  swiglu=f"gate_up [{B}, {2 * inter}] -> [{B}, {inter}] bf16")
+    in_graph = dict(add_rmsnorm=(op_graph["add_rmsnorm"] + op_graph["add_rmsnorm_2"]) / 2,
+                    rope_kvstore=op_graph["rope_kvstore"], swiglu=op_graph["swiglu"])
+    ops = {}
+    for op, v in per_op.items():
+        us = in_graph[op]
+        n = len(v) / n_steps
+        gbs = nbytes[op] / (us * 1e-6) / 1e9
+        ops[op] = dict(shape=shapes[op], launches_per_step=n, bytes_per_launch=nbytes[op],
+                       mean_us=round(us, 3), us_per_step=round(us * n, 2), achieved_gbs=round(gbs, 1),
+                       frac=round(gbs / PEAK_GBS, 4),
+                       event_stamped_mean_us=round(1e3 * statistics.fmean(v), 3))
+    total = sum(o["us_per_step"] for o in ops.values())
+    for o in ops.values():
+        o["share_of_kernel_time"] = round(o["us_per_step"] / total, 4)
+    dom = max(ops, key=lambda k: ops[k]["us_per_step"])
+    d = ops[dom]
+    traffic, note = counter_traffic(dom)
+    roof = dict(bound="hbm", kernel=dom,
+                selected_by="largest kernel time per step (per-launch time in a graph of the op's launches "
+                            "x launches per step)",
+                shape=d["shape"], bytes_per_launch=d["bytes_per_launch"], mean_us=d["mean_us"],
+                mean_us_method="HIP events on the launch stream around replays of a captured graph of the op's "
+                               "28 launches on the chain's buffers, per launch",
+                launches_per_step=d["launches_per_step"], share_of_kernel_time=d["share_of_kernel_time"],
+                achieved=d["achieved_gbs"], peak=PEAK_GBS, unit="GB/s", frac=d["frac"], traffic=traffic,
+                traffic_source=f"{COUNTER_PROFILE} (rocprofv3 FETCH_SIZE + WRITE_SIZE of bench.py --pmc-pass, "
+                               f"scaled by the copy kernel's counts)",
+                chain_ops=ops)
+    if note:
+        roof["traffic_note"] = note
+    return roof
+
+
 def graph_op_us(kcr, chain, reps: int):
     """Per-launch time of each op inside a captured graph of its 28 launches
     (one per layer, the chain's shapes and buffers), unprofiled."""
@@ -377,10 +436,15 @@ def decode_token_latency(kcr, reps: int):
             timed_launch(kcr, fn, ev[2 * i], ev[2 * i + 1])
         torch.cuda.synchronize()
         st = kernel_stats([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(200)])
-        out[name] = dict(in_graph_us_per_launch=round(in_graph, 3), kernel_median_us=round(st["median_us"], 3),
-                         kernel_p20_us=round(st["p20_us"], 3), kernel_p80_us=round(st["p80_us"], 3))
+        out[name] = dict(in_graph_us_per_launch=round(in_graph, 3),
+                         event_stamped_median_us=round(st["median_us"], 3),
+                         event_stamped_p20_us=round(st["p20_us"], 3), event_stamped_p80_us=round(st["p80_us"], 3))
+    out["note"] = ("event_stamped_*: HIP events recorded at the kernel's own start and end of single "
+                   "launches with the GPU otherwise idle; at this size the stamps' own cost dominates, "
+                   "so the per-launch time inside a graph (in_graph_us_per_launch) is the latency figure")
     log("decode token (batch 1): " + ", ".join(f"{k} {v['in_graph_us_per_launch']:.2f} us/launch in graph, "
-                                               f"{v['kernel_median_us']:.2f} us kernel" for k, v in out.items()))
+                                               f"{v['event_stamped_median_us']:.2f} us event-stamped"
+                                               for k, v in out.items() if k != "note"))
     return out
 
 
@@ -391,7 +455,8 @@ def decode_chain_one_launch(kcr, chain, graph_us: float, reps: int):
     from events over `reps` replays of a captured one-node graph; the
     kernel's own duration from events stamped at its start and end."""
     import torch
-    nb = chain.bytes_per_step()["step"]
+    by = chain.bytes_per_step()
+    nb, nb_one = by["step"], by["one_launch_step"]
     chain.capture_one_launch()
     for _ in range(5):
         chain.graph_one.replay()
@@ -410,13 +475,23 @@ def decode_chain_one_launch(kcr, chain, graph_us: float, reps: int):
         chain.step_one_launch()
         torch.cuda.synchronize()
         samples.append(ev[0].elapsed_time(ev[1]) * 1e3)
-    res = dict(step_bytes=nb, graph_112_launches_us=round(graph_us, 2), one_launch_us=round(one_us, 2),
-               one_launch_kernel_median_us=round(statistics.median(samples), 2),
-               one_launch_gbs=round(nb / (one_us * 1e-6) / 1e9, 1),
-               one_launch_frac_of_peak=round(nb / (one_us * 1e-6) / 1e9 / PEAK_GBS, 4),
+    traffic, note = counter_traffic("one_launch_b256")
+    res = dict(graph_step_bytes=nb, one_launch_bytes=nb_one,
+               one_launch_bytes_note="the graph step's algorithmic bytes less the residual's re-reads "
+                                     "(h stays in registers: read once per token, not once per add) and "
+                                     "less the per-layer re-reads of positions, slots and cos/sin rows",
+               graph_112_launches_us=round(graph_us, 2), one_launch_us=round(one_us, 2),
+               one_launch_event_stamped_median_us=round(statistics.median(samples), 2),
+               one_launch_gbs=round(nb_one / (one_us * 1e-6) / 1e9, 1),
+               one_launch_frac_of_peak=round(nb_one / (one_us * 1e-6) / 1e9 / PEAK_GBS, 4),
+               counter_traffic_bytes=traffic,
+               counter_traffic_gbs=round(traffic / (one_us * 1e-6) / 1e9, 1) if traffic else None,
+               counter_traffic_frac_of_peak=round(traffic / (one_us * 1e-6) / 1e9 / PEAK_GBS, 4) if traffic else None,
                speedup=round(graph_us / one_us, 2))
-    log(f"batch-256 chain in one launch: {one_us:.1f} us/step ({res['one_launch_gbs']} GB/s), "
-        f"graph of 112 launches {graph_us:.1f} us/step")
+    if note:
+        res["counter_traffic_note"] = note
+    log(f"batch-256 chain in one launch: {one_us:.1f} us/step ({res['one_launch_gbs']} GB/s of its own "
+        f"algorithmic bytes), graph of 112 launches {graph_us:.1f} us/step")
     return res
 
 
@@ -689,27 +764,286 @@ def pmc_pass():
     log("pmc pass done")
 
 
-def counter_traffic(kernel_name: str):
-    """HBM bytes per launch of the dominant kernel from the committed
-    rocprofv3 counter summary, if it was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", "swiglu_decode_chain_b256_counters.md")
-    if not os.path.exists(path):
-        return None, None
-    text = open(path).read()
-    m = re.search(r"```json\n(.*?)\n```", text, re.S)
-    if not m:
-        return None, None
-    data = json.loads(m.group(1))
-    if data.get("source_sha256") != kernel_source_sha():
-        return None, "kernel source changed since the counters were taken"
-    return data.get("traffic_bytes_per_launch"), None
+COUNTER_PROFILE = os.path.join("profiles", "hbm_bytes_counters.md")
+
+# Sources each measured kernel is built from: a counter figure is used only
+# while their hash matches the one recorded with it.
+KERNEL_SOURCES = {
+    "add_rmsnorm": ("norm_engine.h", "norm.h", "norm_inst.hip", "rmsnorm.hip", "kcr_device.h", "kcr_host.h"),
+    "rope_kvstore": ("rope_kvstore.hip", "kcr_device.h", "kcr_host.h"),
+    "swiglu": ("swiglu.hip", "kcr_device.h", "kcr_host.h"),
+    "one_launch_b256": ("decode_chain.hip", "kcr_device.h", "kcr_host.h"),
+    "one_launch_b1": ("decode_chain.hip", "kcr_device.h", "kcr_host.h"),
+}
 
 
-def kernel_source_sha() -> str:
+def kernel_source_sha(op: str) -> str:
     h = hashlib.sha256()
-    for f in ("swiglu.hip", "kcr_device.h", "kcr_host.h"):
+    for f in KERNEL_SOURCES[op]:
         h.update(open(os.path.join(ROOT, "kv_cache_rmsnorm_amd", "csrc", f), "rb").read())
     return h.hexdigest()
+
+
+def counter_traffic(op: str):
+    """HBM bytes per launch of a decode-chain kernel from the committed
+    rocprofv3 counter summary (FETCH_SIZE, WRITE_SIZE), if it was taken on
+    the current kernel source; else (None, reason)."""
+    path = os.path.join(ROOT, COUNTER_PROFILE)
+    if not os.path.exists(path):
+        return None, f"no {COUNTER_PROFILE}"
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None, f"no counter block in {COUNTER_PROFILE}"
+    entry = json.loads(m.group(1)).get("decode_chain", {}).get(op)
+    if not entry:
+        return None, f"{op} not in {COUNTER_PROFILE}"
+    if entry.get("source_sha256") != kernel_source_sha(op):
+        return None, "kernel source changed since the counters were taken"
+    return entry.get("traffic_bytes_per_launch"), None
+
+
+def _dim(r: dict, key: str) -> int:
+    """A launch dimension from a rocprofv3 CSV row: one column, or _X/_Y/_Z."""
+    if key in r:
+        return int(r[key])
+    return int(r[key + "_X"]) * int(r[key + "_Y"]) * int(r[key + "_Z"])
+
+
+def _pmc_dispatches(csv_dir: str, counter: str):
+    """[(dispatch id, kernel name, grid, block, value)] of the library's
+    kernels (the cos/sin table builds aside) in dispatch order."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {csv_dir}")
+    out = []
+    for r in csv.DictReader(open(files[0])):
+        name = r["Kernel_Name"]
+        if r["Counter_Name"] != counter or "kcr::" not in name or "rope_table_kernel" in name:
+            continue
+        out.append((int(r["Dispatch_Id"]), name, _dim(r, "Grid_Size"), _dim(r, "Workgroup_Size"),
+                    float(r["Counter_Value"])))
+    out.sort()
+    return out
+
+
+def counter_summary(fetch_dir: str, write_dir: str):
+    """Markdown summary of two `rocprofv3 --pmc` runs of `bench.py
+    --pmc-pass` (FETCH_SIZE, then WRITE_SIZE): HBM bytes per dispatch,
+    scaled by the copy kernel's exactly known 1 GiB in and out; the decode
+    chain's kernels (identified by their place in the pass's fixed launch
+    order) with the hash of their sources; and every kernel grouped by
+    name and grid."""
+    import workloads
+    from kv_cache_rmsnorm_amd.chain import chain_bytes
+    fe, wr = _pmc_dispatches(fetch_dir, "FETCH_SIZE"), _pmc_dispatches(write_dir, "WRITE_SIZE")
+    n = 1 << 30
+    copies = [i for i, d in enumerate(fe) if "copy_kernel" in d[1]][:3]
+    sf = n / (1024 * statistics.fmean(fe[i][4] for i in copies))
+    sw = n / (1024 * statistics.fmean(wr[i][4] for i in copies))
+    i0 = copies[-1] + 1
+    # The fixed part of the pass (copies, chain steps, one-launch chains) must
+    # have launched the same kernels in both runs; the large shapes' warm-up
+    # is timed, so their counts may differ and they are grouped per run.
+    fixed = i0 + 224 + 6
+    assert [d[1:4] for d in fe[:fixed]] == [d[1:4] for d in wr[:fixed]], "the passes' fixed launches differ"
+    wl = workloads.decode_chain(layers=1)
+    B, hid, inter, hq, hkv, dh = 256, wl["hidden"], wl["inter"], wl["hq"], wl["hkv"], wl["dh"]
+    per = chain_bytes(28, B, hid, inter, hq, hkv, dh, 2)
+    alg = dict(add_rmsnorm=per["per_layer"]["add_rmsnorm"] // 2, rope_kvstore=per["per_layer"]["rope_kvstore"],
+               swiglu=per["per_layer"]["swiglu"], one_launch_b256=per["one_launch_step"],
+               one_launch_b1=chain_bytes(28, 1, hid, inter, hq, hkv, dh, 2)["one_launch_step"])
+    order = ["add_rmsnorm", "rope_kvstore", "add_rmsnorm", "swiglu"]
+    groups = {}
+    for k in range(2 * 112):   # two eager steps of the 28-layer chain
+        groups.setdefault(order[k % 4], []).append(i0 + k)
+    groups["one_launch_b256"] = [i0 + 224 + k for k in range(3)]
+    groups["one_launch_b1"] = [i0 + 227 + k for k in range(3)]
+    chain = {}
+    for op, idx in groups.items():
+        names = {fe[i][1] for i in idx}
+        assert len(names) == 1, f"{op}: mixed kernels {names}"
+        f = statistics.fmean(fe[i][4] for i in idx)
+        w = statistics.fmean(wr[i][4] for i in idx)
+        traffic = int(round(1024 * (f * sf + w * sw)))
+        chain[op] = dict(kernel=fe[idx[0]][1].replace("void kcr::", "").split("(")[0], grid=fe[idx[0]][2],
+                         block=fe[idx[0]][3], dispatches=len(idx), fetch_kib=round(f, 1), write_kib=round(w, 1),
+                         traffic_bytes_per_launch=traffic, algorithmic_bytes_per_launch=alg[op],
+                         ratio=round(traffic / alg[op], 4), source_sha256=kernel_source_sha(op))
+    table = {}
+    for lst, j in ((fe, 0), (wr, 1)):
+        for d in lst:
+            key = (d[1].replace("void kcr::", "").split("(")[0], d[2], d[3])
+            table.setdefault(key, ([], []))[j].append(d[4])
+    print("# HBM byte counters per dispatch (FETCH_SIZE, WRITE_SIZE)\n")
+    print("Commands (two passes, one counter each, then this summary; from the repository root on the "
+          "MI355X machine, `REPO=$(pwd)`):\n")
+    print("```")
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        print(f"cd /tmp && timeout -s KILL 300 rocprofv3 --pmc {c} --output-format csv -d $REPO/gpurun_out/pmc_{c} "
+              f"-o pmc -- python3 -u $REPO/bench.py --pmc-pass")
+    print("cd $REPO && python3 bench.py --counter-summary gpurun_out/pmc_FETCH_SIZE gpurun_out/pmc_WRITE_SIZE")
+    print("```\n")
+    print(f"Scale: the library's copy kernel moves exactly 1 GiB in and 1 GiB out per dispatch; FETCH_SIZE is "
+          f"scaled by {sf:.4f} and WRITE_SIZE by {sw:.4f} (KiB per dispatch to bytes).\n")
+    print("## Decode chain (28 layers, batch 256, bf16) and its one-launch forms\n")
+    print("| op | kernel | grid x block | dispatches | FETCH KiB | WRITE KiB | scaled HBM bytes | algorithmic bytes | ratio |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for op, e in chain.items():
+        print(f"| {op} | `{e['kernel']}` | {e['grid']} x {e['block']} | {e['dispatches']} | {e['fetch_kib']} | "
+              f"{e['write_kib']} | {e['traffic_bytes_per_launch']} | {e['algorithmic_bytes_per_launch']} | {e['ratio']:.3f} |")
+    print("\n## Every kernel of the pass, by name and grid (means over its dispatches)\n")
+    print("| kernel | grid x block | dispatches (fetch/write pass) | FETCH KiB | WRITE KiB | scaled HBM bytes |")
+    print("|---|---|---|---|---|---|")
+    for (name, grid, blk), (vf, vw) in sorted(table.items(), key=lambda kv: -statistics.fmean(kv[1][0] or [0])):
+        if not vf or not vw:
+            continue
+        f, w = statistics.fmean(vf), statistics.fmean(vw)
+        print(f"| `{name}` | {grid} x {blk} | {len(vf)}/{len(vw)} | {f:.1f} | {w:.1f} | {int(round(1024 * (f * sf + w * sw)))} |")
+    print("\nbench.py reads the block below for `roofline.traffic` and the one-launch chain's "
+          "`counter_traffic_bytes`, and drops an entry once the hash of its kernel's sources changes.\n")
+    print("```json")
+    print(json.dumps(dict(scale_fetch=round(sf, 6), scale_write=round(sw, 6), decode_chain=chain), indent=1))
+    print("```")
+
+
+SQ_PASSES = (
+    "SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CU_CYCLES SQ_WAIT_INST_ANY SQ_WAIT_ANY SQ_ACTIVE_INST_VALU "
+    "SQ_ACTIVE_INST_VMEM SQ_ACTIVE_INST_ANY",
+    "SQ_INSTS_VALU SQ_INSTS_VMEM SQ_INSTS_SALU SQ_INSTS_LDS SQ_INSTS_VALU_TRANS_F SQ_CYCLES",
+)
+
+
+def sq_summary(cycles_dir: str, insts_dir: str):
+    """Markdown summary of two `rocprofv3 --pmc` runs of `bench.py
+    --pmc-pass` with the shader-sequencer counters of SQ_PASSES: per kernel
+    and grid, the share of wave-cycles in VALU work, waiting and issue
+    stalls, and instructions per wave."""
+    import csv
+    import glob
+
+    def load(d):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        acc = {}
+        for r in csv.DictReader(open(files[0])):
+            name = r["Kernel_Name"]
+            if "kcr::" not in name or "rope_table_kernel" in name:
+                continue
+            key = (name.replace("void kcr::", "").split("(")[0], _dim(r, "Grid_Size"), _dim(r, "Workgroup_Size"))
+            acc.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        return {k: {c: statistics.fmean(v) for c, v in cs.items()} for k, cs in acc.items()}
+
+    cyc, ins = load(cycles_dir), load(insts_dir)
+    print("# Shader-sequencer counters per dispatch (where waves spend their cycles)\n")
+    print("Commands (two passes, then this summary; from the repository root on the MI355X machine, "
+          "`REPO=$(pwd)`):\n")
+    print("```")
+    for tag, counters in zip(("SQ", "SQI"), SQ_PASSES):
+        print(f"cd /tmp && timeout -s KILL 300 rocprofv3 --pmc {counters} --output-format csv "
+              f"-d $REPO/gpurun_out/pmc_{tag} -o pmc -- python3 -u $REPO/bench.py --pmc-pass")
+    print("cd $REPO && python3 bench.py --sq-summary gpurun_out/pmc_SQ gpurun_out/pmc_SQI")
+    print("```\n")
+    print("Means over all dispatches of each kernel and grid in the pass (eager launches of the decode chain, "
+          "the one-launch chains, the large shapes). Wave-cycle counters are summed over waves. `VALU share` = "
+          "SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES, `waiting` = SQ_WAIT_ANY / SQ_WAVE_CYCLES (memory, barriers, "
+          "dependencies), `issue stall` = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES.\n")
+    print("| kernel | grid x block | waves | VALU instr per wave | VMEM instr per wave | SALU instr per wave | "
+          "LDS instr per wave | VALU share | waiting | issue stall |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
+    for key in sorted(cyc, key=lambda k: -cyc[k].get("SQ_WAVES", 0) * k[1]):
+        c, i = cyc[key], ins.get(key, {})
+        w, wc = c.get("SQ_WAVES", 0.0), c.get("SQ_WAVE_CYCLES", 0.0)
+        if w <= 0 or wc <= 0:
+            continue
+        per = lambda n: f"{i[n] / w:.1f}" if n in i else "-"
+        print(f"| `{key[0]}` | {key[1]} x {key[2]} | {w:.0f} | {per('SQ_INSTS_VALU')} | {per('SQ_INSTS_VMEM')} | "
+              f"{per('SQ_INSTS_SALU')} | {per('SQ_INSTS_LDS')} | {100 * c.get('SQ_ACTIVE_INST_VALU', 0) / wc:.1f}% | "
+              f"{100 * c.get('SQ_WAIT_ANY', 0) / wc:.1f}% | {100 * c.get('SQ_WAIT_INST_ANY', 0) / wc:.1f}% |")
+
+
+def trace_summary(trace_dir: str, steps: int):
+    """Markdown summary of `rocprofv3 --kernel-trace --stats` over a default
+    bench run: every library kernel by name and grid, then the launches
+    split into segments at gaps over 200 us, where the timed region is the
+    segment of `steps` graph replays of the 112-launch chain."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
+    ks = []
+    for r in csv.DictReader(open(files[0])):
+        name = r["Kernel_Name"]
+        if "kcr::" not in name or "rope_table_kernel" in name:
+            continue
+        short = name.replace("void kcr::", "").split("(")[0]
+        ks.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), short, _dim(r, "Grid_Size"),
+                   _dim(r, "Workgroup_Size")))
+    ks.sort()
+
+    def stats(v):
+        v = sorted(v)
+        return len(v), statistics.fmean(v), statistics.median(v), v[0], v[-1]
+
+    groups = {}
+    for a, b, n, g, w in ks:
+        groups.setdefault((n, g, w), []).append((b - a) / 1e3)
+    print("# rocprofv3 kernel trace of the default bench run\n")
+    print("Command (from the repository root on the MI355X machine, `REPO=$(pwd)`), then this summary:\n")
+    print("```")
+    print("cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $REPO/gpurun_out/prof_bench "
+          "-o bench -- python3 -u $REPO/bench.py")
+    print(f"cd $REPO && python3 bench.py --trace-summary gpurun_out/prof_bench --steps {steps}")
+    print("```\n")
+    print("Durations from the trace's own start/end stamps, in us. Under the profiler the dispatches of a "
+          "graph replay are spaced further apart than unprofiled.\n")
+    print("## Every library kernel, by name and grid\n")
+    print("| kernel | grid x block | launches | mean us | median us | min us | max us |")
+    print("|---|---|---|---|---|---|---|")
+    for (n, g, w), v in sorted(groups.items(), key=lambda kv: -statistics.fmean(kv[1])):
+        c, mean, med, lo, hi = stats(v)
+        print(f"| `{n}` | {g} x {w} | {c} | {mean:.2f} | {med:.2f} | {lo:.2f} | {hi:.2f} |")
+    segs, cur = [], [ks[0]]
+    for prev, k in zip(ks, ks[1:]):
+        if k[0] - prev[1] > 200_000:
+            segs.append(cur)
+            cur = []
+        cur.append(k)
+    segs.append(cur)
+    print("\n## Segments of at least 112 launches (split at gaps over 200 us)\n")
+    print("| segment | launches | start-to-start us | kernels (n, mean us) |")
+    print("|---|---|---|---|")
+    timed = None
+    for i, sg in enumerate(segs):
+        if len(sg) < 112:
+            continue
+        per = {}
+        for a, b, n, g, w in sg:
+            per.setdefault(f"{n} {g}x{w}", []).append((b - a) / 1e3)
+        gap = (sg[-1][0] - sg[0][0]) / 1e3 / max(1, len(sg) - 1)
+        desc = "; ".join(f"`{k}` n={len(v)} {statistics.fmean(v):.2f}" for k, v in per.items())
+        print(f"| {i} | {len(sg)} | {gap:.2f} | {desc} |")
+        if len(sg) == 112 * steps and timed is None and len(per) == 3:
+            timed = per
+    # The timed graph replays end right before the launch-floor graph (the
+    # 16-byte copy, grid 64): the 112 * steps chain launches before it.
+    floor = next((i for i, k in enumerate(ks) if k[2] == "kcr::copy_kernel" and k[3] == 64), None)
+    if floor is not None and floor >= 112 * steps:
+        per = {}
+        for a, b, n, g, w in ks[floor - 112 * steps:floor]:
+            per.setdefault(f"{n} {g}x{w}", []).append((b - a) / 1e3)
+        if len(per) == 3:
+            timed = per
+    if timed:
+        print(f"\n## The timed region: {steps} graph replays of the 112-launch chain\n")
+        print("| kernel | launches | launches per step | mean us | median us | us per step |")
+        print("|---|---|---|---|---|---|")
+        for k, v in sorted(timed.items(), key=lambda kv: -sum(kv[1])):
+            c, mean, med, lo, hi = stats(v)
+            print(f"| `{k}` | {c} | {c / steps:.0f} | {mean:.2f} | {med:.2f} | {mean * c / steps:.1f} |")
 
 
 def library_source_sha() -> str:
@@ -739,7 +1073,22 @@ def main():
     ap.add_argument("--skip-sweep", action="store_true", help="skip the [512, D] RMSNorm sweep")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="only launch each kernel eagerly (for rocprofv3 --pmc runs); no JSON line")
+    ap.add_argument("--counter-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the HBM byte-counter summary of two --pmc-pass runs (FETCH_SIZE, WRITE_SIZE)")
+    ap.add_argument("--sq-summary", nargs=2, metavar=("SQ_DIR", "SQI_DIR"),
+                    help="print the shader-sequencer counter summary of two --pmc-pass runs (SQ_PASSES)")
+    ap.add_argument("--trace-summary", metavar="TRACE_DIR",
+                    help="print the summary of a rocprofv3 --kernel-trace run of the default bench")
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.steps)
+        return
+    if args.sq_summary:
+        sq_summary(*args.sq_summary)
+        return
+    if args.counter_summary:
+        counter_summary(*args.counter_summary)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); the ops "
@@ -750,7 +1099,7 @@ def main():
     import torch
     import kv_cache_rmsnorm_amd as kcr
     import workloads
-    from kv_cache_rmsnorm_amd.chain import DecodeChain, swiglu_bytes
+    from kv_cache_rmsnorm_amd.chain import DecodeChain
 
     assert torch.cuda.is_available(), "bench.py needs a HIP device"
     if args.pmc_pass:
@@ -776,9 +1125,6 @@ def main():
     torch.cuda.synchronize()
     chain.capture()
     per_op, sums = instrumented_steps(kcr, chain, max(3, args.steps // 5))
-    sw = per_op["swiglu"]
-    sw_us = 1e3 * statistics.fmean(sw)
-    sw_bytes = swiglu_bytes(B, inter, 2)
     kernel_sum_us = 1e3 * statistics.median(sums)
 
     # eager steps (one Python launch per op)
@@ -810,7 +1156,7 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     value = nbytes["step"] / (ms * 1e-3) / 1e9
     log(f"graph step {ms * 1e3:.1f} us = {value:.0f} GB/s; eager {eager_ms * 1e3:.1f} us; "
-        f"kernel sum {kernel_sum_us:.1f} us; swiglu {sw_us:.2f} us")
+        f"event-stamped kernel sum {kernel_sum_us:.1f} us")
 
     floor_us = launch_floor(kcr, 4 * len(chain.layers), max(10, args.steps // 2))
     log(f"launch floor: {floor_us:.2f} us per graph node of a 16-byte copy")
@@ -822,14 +1168,10 @@ def main():
     ceiling = copy_ceiling(kcr, args.kernel_iters)
     kernels = {} if args.skip_large else large_shapes(kcr, args.kernel_iters)
 
-    traffic, traffic_note = counter_traffic("swiglu")
-    achieved = sw_bytes / (sw_us * 1e-6) / 1e9
-    roofline = dict(bound="hbm", kernel="swiglu", shape=f"gate_up [{B}, {2 * inter}] -> [{B}, {inter}] bf16",
-                    bytes_per_launch=sw_bytes, mean_us=round(sw_us, 3), launches=len(sw),
-                    achieved=round(achieved, 1), peak=PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / PEAK_GBS, 4), traffic=traffic)
-    if traffic_note:
-        roofline["traffic_note"] = traffic_note
+    roofline = chain_roofline(chain, op_graph, per_op, len(sums))
+    log(f"roofline: dominant kernel {roofline['kernel']} ({100 * roofline['share_of_kernel_time']:.0f}% of the "
+        f"step's kernel time), {roofline['mean_us']:.2f} us per launch, {roofline['achieved']:.0f} GB/s "
+        f"({100 * roofline['frac']:.1f}% of peak)")
 
     cpu = None
     if not args.skip_cpu:

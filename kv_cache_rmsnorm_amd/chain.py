@@ -166,4 +166,11 @@ def chain_bytes(layers, B, hidden, inter, hq, hkv, dh, s, distinct_positions=1) 
                rope_kvstore=rope_bytes(B, hq, hkv, dh, s, distinct_positions),
                swiglu=swiglu_bytes(B, inter, s))
     per_layer = sum(per.values())
-    return dict(per_layer=per, layer=per_layer, step=layers * per_layer)
+    step = layers * per_layer
+    # The one-launch chain (kcr_decode_chain_batch) keeps the residual h in
+    # registers: it reads h once per token instead of once per add (2 adds
+    # per layer), and the positions, slots and cos/sin rows once per step
+    # instead of once per layer. Its stores are those of the separate ops.
+    one = (step - (2 * layers - 1) * B * hidden * s
+           - (layers - 1) * (B * 16 + distinct_positions * dh * 4))
+    return dict(per_layer=per, layer=per_layer, step=step, one_launch_step=one)

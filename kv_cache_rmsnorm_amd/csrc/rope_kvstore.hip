@@ -247,23 +247,38 @@ static int dispatch_rope_lpu(const RopeArgs& a, int64_t T_tokens, void* stream) 
 // line code with no early exit: in the 28-layer, batch-256 decode chain on
 // MI355X this took the step 5-7 us below the unit kernel above at the same
 // work split.
-template <typename T, int LPU, bool QKN>
+//
+// DH: head_dim when fixed at compile time (0: a.dh). FUSED: q, k and v are
+// head ranges of one row per token -- k = q + n_head heads, v = k +
+// n_kv_head heads, one token stride and one head stride -- the layout of a
+// fused QKV projection's output (mer.dev "AsyncT vLLM notes (1)", section
+// 3.3), so every lane reads from one base pointer. Both only shorten the
+// address arithmetic ahead of the first load: together 4-5 us per step of
+// the 28-layer, batch-256 decode chain on MI355X.
+template <typename T, int LPU, bool QKN, int DH = 0, bool FUSED = false>
 __global__ __launch_bounds__(1024) void rope_token_kernel(const RopeArgs a) {
     using S = typename T::storage;
     constexpr int kVec = T::kVec;
     const int tid = threadIdx.x, c = tid % LPU, u0 = tid / LPU;
     const bool on = u0 < a.nvh;
     const int u = on ? u0 : a.nvh - 1;
-    const int half = a.dh >> 1;
+    const int dh = DH ? DH : a.dh;
+    const int half = dh >> 1;
     const int64_t t = blockIdx.x;
     const int g = (int)fastdiv((uint32_t)u, a.gsize);
     const int r = u - g * (int)a.gsize.d;
     const int kind = r < a.group ? 0 : (r == a.group ? 1 : 2);  // query, K, V
     const int hh = g * a.group + r;
-    const S* base = static_cast<const S*>(kind == 0 ? a.q : (kind == 1 ? a.k : a.v));
-    const int64_t ts = kind == 0 ? a.q_ts : (kind == 1 ? a.k_ts : a.v_ts);
-    const int64_t hs = kind == 0 ? a.q_hs : (kind == 1 ? a.k_hs : a.v_hs);
-    const S* src = base + t * ts + (int64_t)(kind == 0 ? hh : g) * hs;
+    const S* src;
+    if constexpr (FUSED) {
+        const int head = kind == 0 ? hh : (kind == 1 ? a.hq + g : a.hq + a.hkv + g);
+        src = static_cast<const S*>(a.q) + t * a.q_ts + (int64_t)head * a.q_hs;
+    } else {
+        const S* base = static_cast<const S*>(kind == 0 ? a.q : (kind == 1 ? a.k : a.v));
+        const int64_t ts = kind == 0 ? a.q_ts : (kind == 1 ? a.k_ts : a.v_ts);
+        const int64_t hs = kind == 0 ? a.q_hs : (kind == 1 ? a.k_hs : a.v_hs);
+        src = base + t * ts + (int64_t)(kind == 0 ? hh : g) * hs;
+    }
     const int64_t p = a.pos[t], slot = a.slots[t];
     const int c0 = c * kVec;
     const u32x4 x1 = ld16_nt<T>(src, c0), x2 = ld16_nt<T>(src, half + c0);
@@ -299,7 +314,7 @@ __global__ __launch_bounds__(1024) void rope_token_kernel(const RopeArgs a) {
 #pragma unroll
         for (int e = 0; e < kVec; ++e) ss += f1[e] * f1[e] + f2[e] * f2[e];
         ss = group_sum<LPU>(ss);
-        const float rs = __builtin_amdgcn_rsqf(ss / (float)a.dh + a.eps);
+        const float rs = __builtin_amdgcn_rsqf(ss / (float)dh + a.eps);
 #pragma unroll
         for (int e = 0; e < kVec; ++e) {
             f1[e] = f1[e] * rs * w1[e];
@@ -315,9 +330,9 @@ __global__ __launch_bounds__(1024) void rope_token_kernel(const RopeArgs a) {
     const bool rot = kind < 2 && p_ok;
     const u32x4 o1 = rot ? pack<T>(r1) : x1, o2 = rot ? pack<T>(r2) : x2;
     const bool store_kv = p_ok && slot >= 0 && slot < a.n_slots;
-    S* dst = kind == 0 ? static_cast<S*>(a.q_out) + (t * a.hq + hh) * a.dh
+    S* dst = kind == 0 ? static_cast<S*>(a.q_out) + (t * a.hq + hh) * dh
                        : static_cast<S*>(a.cache) +
-                             (((int64_t)(kind - 1) * a.n_slots + (store_kv ? slot : 0)) * a.hkv + g) * (int64_t)a.dh;
+                             (((int64_t)(kind - 1) * a.n_slots + (store_kv ? slot : 0)) * a.hkv + g) * (int64_t)dh;
     if (on && (kind == 0 || store_kv)) {
         st16_nt<T>(dst, c0, o1);
         st16_nt<T>(dst, half + c0, o2);
@@ -332,7 +347,18 @@ static int launch_rope_token(const RopeArgs& a, int64_t T_tokens, void* stream) 
     const int chunks = (a.dh / 2) / T::kVec;
     const int lanes = a.nvh * chunks;
     if ((chunks & (chunks - 1)) != 0 || lanes > 1024) return 1;
-    const dim3 grid((uint32_t)T_tokens), block((uint32_t)((lanes + 63) / 64 * 64));
+    const int64_t block_lanes = (lanes + 63) / 64 * 64;
+    if (T_tokens * block_lanes > (int64_t)0xFFFFFFFFu) return 1;  // one grid: under 2^32 work-items
+    const dim3 grid((uint32_t)T_tokens), block((uint32_t)block_lanes);
+    using S = typename T::storage;
+    const bool fused = a.k == static_cast<const S*>(a.q) + (int64_t)a.hq * a.q_hs &&
+                       a.v == static_cast<const S*>(a.k) + (int64_t)a.hkv * a.q_hs && a.k_ts == a.q_ts &&
+                       a.v_ts == a.q_ts && a.k_hs == a.q_hs && a.v_hs == a.q_hs;
+    if (a.dh == 128) {
+        constexpr int L = 64 / T::kVec;
+        return fused ? launch(rope_token_kernel<T, L, QKN, 128, true>, grid, block, stream, a)
+                     : launch(rope_token_kernel<T, L, QKN, 128, false>, grid, block, stream, a);
+    }
     switch (chunks) {
         case 1: return launch(rope_token_kernel<T, 1, QKN>, grid, block, stream, a);
         case 2: return launch(rope_token_kernel<T, 2, QKN>, grid, block, stream, a);
@@ -355,12 +381,19 @@ static int launch_rope_token(const RopeArgs& a, int64_t T_tokens, void* stream) 
 // (each kernel then writes its dirty L2 lines back before the next starts).
 constexpr int64_t kRopeSmallBatch = 4096;
 
+// Every call whose token fits one workgroup takes the token kernel: in the
+// decode chain it measured 5-7 us per step below the unit kernel, and at the
+// 64-sequence prefill shape (70k tokens) 0.5-1.3% above the two-head unit
+// kernel (96.0-96.5 against 97.0-97.3 us, two runs; with the Q/K norm the
+// same). The unit kernels remain for head layouts the token kernel does not
+// take (half a head not a power-of-two number of chunks, or more than 1024
+// lanes of heads per token).
 template <typename T, bool QKN>
 static int dispatch_rope(const RopeArgs& a, int64_t T_tokens, void* stream) {
-    if (T_tokens > kRopeSmallBatch) return dispatch_rope_lpu<T, 2, QKN, 256>(a, T_tokens, stream);
     const int rc = launch_rope_token<T, QKN>(a, T_tokens, stream);
     if (rc <= 0) return rc;
-    return dispatch_rope_lpu<T, 1, QKN, 128>(a, T_tokens, stream);
+    return T_tokens <= kRopeSmallBatch ? dispatch_rope_lpu<T, 1, QKN, 128>(a, T_tokens, stream)
+                                       : dispatch_rope_lpu<T, 2, QKN, 256>(a, T_tokens, stream);
 }
 
 // ---------------------------------------------------------- cos/sin tables

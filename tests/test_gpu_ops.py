@@ -69,7 +69,8 @@ def test_rmsnorm_widest_bf16(kcr, d):
 
 
 # Rows wider than the register-resident engine (4096 vectors): the two-pass
-# kernel, LDS-staged while a row fits in 160 KB, else reading the row twice.
+# kernel, LDS-staged while a row fits in 160 KB, else reading the part beyond
+# LDS twice.
 WIDE = [(torch.bfloat16, 32769), (torch.bfloat16, 40000), (torch.bfloat16, 65536),
         (torch.bfloat16, 81000), (torch.bfloat16, 100003), (torch.float16, 50001),
         (torch.float16, 131072), (torch.float32, 16385), (torch.float32, 40000),
