@@ -246,7 +246,19 @@ def large_shapes(kcr, iters: int):
     return out
 
 
-def chain_roofline(chain, op_graph: dict, per_op: dict, n_steps: int) -> dict:
+def chain_op_bytes(chain) -> dict:
+    """Algorithmic bytes per launch of each chain op at the chain's shape."""
+    from kv_cache_rmsnorm_amd.chain import norm_bytes, rope_bytes, swiglu_bytes
+    import torch
+    B, hid, inter = chain.h.shape[0], chain.hidden, chain.inter
+    s = chain.h.element_size()
+    distinct = int(torch.unique(chain.positions).numel())
+    return dict(add_rmsnorm=norm_bytes(B, hid, s, True),
+                rope_kvstore=rope_bytes(B, chain.hq, chain.hkv, chain.dh, s, distinct),
+                swiglu=swiglu_bytes(B, inter, s))
+
+
+def chain_roofline(chain, op_graph: dict, per_op: dict, n_steps: int, copy_us: dict) -> dict:
     """The roofline object for the step's dominant kernel: the chain op with
     the largest kernel time per step. A launch's time is its per-launch time
     inside a captured graph of that op's 28 launches on the chain's buffers
@@ -255,14 +267,8 @@ def chain_roofline(chain, op_graph: dict, per_op: dict, n_steps: int) -> dict:
     kernel's start and end have a floor near 4 us on this part, so those
     (per_op, from whole eager steps) are reported beside it only. Every
     chain op is listed with its launches, time share and fraction of peak."""
-    from kv_cache_rmsnorm_amd.chain import norm_bytes, rope_bytes, swiglu_bytes
-    import torch
     B, hid, inter = chain.h.shape[0], chain.hidden, chain.inter
-    s = chain.h.element_size()
-    distinct = int(torch.unique(chain.positions).numel())
-    nbytes = dict(add_rmsnorm=norm_bytes(B, hid, s, True),
-                  rope_kvstore=rope_bytes(B, chain.hq, chain.hkv, chain.dh, s, distinct),
-                  swiglu=swiglu_bytes(B, inter, s))
+    nbytes = chain_op_bytes(chain)
     shapes = dict(add_rmsnorm=f"x, delta [{B}, {hid}] bf16 -> x, y",
                   rope_kvstore=f"{B} tokens, {chain.hq}q/{chain.hkv}kv heads x{chain.dh}, bf16, paged store",
                   swiglu=f"gate_up [{B}, {2 * inter}] -> [{B}, {inter}] bf16")
@@ -276,6 +282,8 @@ def chain_roofline(chain, op_graph: dict, per_op: dict, n_steps: int) -> dict:
         ops[op] = dict(shape=shapes[op], launches_per_step=n, bytes_per_launch=nbytes[op],
                        mean_us=round(us, 3), us_per_step=round(us * n, 2), achieved_gbs=round(gbs, 1),
                        frac=round(gbs / PEAK_GBS, 4),
+                       size_matched_copy_us=round(copy_us[op], 3),
+                       frac_of_size_matched_copy=round(copy_us[op] / us, 4),
                        event_stamped_mean_us=round(1e3 * statistics.fmean(v), 3))
     total = sum(o["us_per_step"] for o in ops.values())
     for o in ops.values():
@@ -291,12 +299,49 @@ def chain_roofline(chain, op_graph: dict, per_op: dict, n_steps: int) -> dict:
                                "28 launches on the chain's buffers, per launch",
                 launches_per_step=d["launches_per_step"], share_of_kernel_time=d["share_of_kernel_time"],
                 achieved=d["achieved_gbs"], peak=PEAK_GBS, unit="GB/s", frac=d["frac"], traffic=traffic,
+                size_matched_copy_us=d["size_matched_copy_us"],
+                size_matched_copy_note="per-launch time of a graph of 28 plain copies moving the same bytes "
+                                       "(half read, half written): what any kernel of this size attains in a graph",
+                frac_of_size_matched_copy=d["frac_of_size_matched_copy"],
                 traffic_source=f"{COUNTER_PROFILE} (rocprofv3 FETCH_SIZE + WRITE_SIZE of bench.py --pmc-pass, "
                                f"scaled by the copy kernel's counts)",
                 chain_ops=ops)
     if note:
         roof["traffic_note"] = note
     return roof
+
+
+def graph_copy_us(kcr, nbytes: int, n_launch: int, reps: int) -> float:
+    """Per-launch time of a captured graph of n_launch copies that each move
+    `nbytes` (nbytes / 2 read, nbytes / 2 written) on their own buffers: the
+    attainable rate of a kernel of that size inside a graph."""
+    import torch
+    half = (nbytes // 2 + 15) // 16 * 16
+    srcs = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(n_launch)]
+    dsts = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(n_launch)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for a, b in zip(dsts, srcs):
+            kcr.copy_(a, b)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for a, b in zip(dsts, srcs):
+            kcr.copy_(a, b)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = events(2)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * n_launch)
+    del g, srcs, dsts
+    return us
 
 
 def graph_op_us(kcr, chain, reps: int):
@@ -1168,7 +1213,10 @@ def main():
     ceiling = copy_ceiling(kcr, args.kernel_iters)
     kernels = {} if args.skip_large else large_shapes(kcr, args.kernel_iters)
 
-    roofline = chain_roofline(chain, op_graph, per_op, len(sums))
+    copy_us = {op: graph_copy_us(kcr, b, len(chain.layers), max(10, args.steps // 2))
+               for op, b in chain_op_bytes(chain).items()}
+    log("size-matched copies in a graph: " + ", ".join(f"{k} {v:.2f} us" for k, v in copy_us.items()))
+    roofline = chain_roofline(chain, op_graph, per_op, len(sums), copy_us)
     log(f"roofline: dominant kernel {roofline['kernel']} ({100 * roofline['share_of_kernel_time']:.0f}% of the "
         f"step's kernel time), {roofline['mean_us']:.2f} us per launch, {roofline['achieved']:.0f} GB/s "
         f"({100 * roofline['frac']:.1f}% of peak)")
