@@ -344,6 +344,47 @@ def graph_copy_us(kcr, nbytes: int, n_launch: int, reps: int) -> float:
     return us
 
 
+def copy_equivalent_step_us(kcr, chain, reps: int) -> float:
+    """Step time of a captured graph of 112 plain copies in the chain's
+    order, each moving the bytes of the chain op at its place (half read,
+    half written) on buffers of its own: what a graph of launches of these
+    sizes attains on this device."""
+    import torch
+    nb = chain_op_bytes(chain)
+    order = ["add_rmsnorm", "rope_kvstore", "add_rmsnorm", "swiglu"] * len(chain.layers)
+    pairs = []
+    for op in order:
+        half = (nb[op] // 2 + 15) // 16 * 16
+        pairs.append((torch.empty(half, dtype=torch.uint8, device="cuda"),
+                      torch.empty(half, dtype=torch.uint8, device="cuda")))
+
+    def step():
+        for a, b in pairs:
+            kcr.copy_(a, b)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(5):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = events(2)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del g, pairs
+    torch.cuda.empty_cache()
+    return us
+
+
 def graph_op_us(kcr, chain, reps: int):
     """Per-launch time of each op inside a captured graph of its 28 launches
     (one per layer, the chain's shapes and buffers), unprofiled."""
@@ -1075,7 +1116,7 @@ def trace_summary(trace_dir: str, steps: int):
             timed = per
     # The timed graph replays end right before the launch-floor graph (the
     # 16-byte copy, grid 64): the 112 * steps chain launches before it.
-    floor = next((i for i, k in enumerate(ks) if k[2] == "kcr::copy_kernel" and k[3] == 64), None)
+    floor = next((i for i, k in enumerate(ks) if k[2].split("::")[-1] == "copy_kernel" and k[3] == 64), None)
     if floor is not None and floor >= 112 * steps:
         per = {}
         for a, b, n, g, w in ks[floor - 112 * steps:floor]:
@@ -1215,6 +1256,8 @@ def main():
 
     copy_us = {op: graph_copy_us(kcr, b, len(chain.layers), max(10, args.steps // 2))
                for op, b in chain_op_bytes(chain).items()}
+    copy_step_us = copy_equivalent_step_us(kcr, chain, max(20, args.steps))
+    log(f"copy-equivalent step (112 plain copies of the ops' sizes): {copy_step_us:.1f} us")
     log("size-matched copies in a graph: " + ", ".join(f"{k} {v:.2f} us" for k, v in copy_us.items()))
     roofline = chain_roofline(chain, op_graph, per_op, len(sums), copy_us)
     log(f"roofline: dominant kernel {roofline['kernel']} ({100 * roofline['share_of_kernel_time']:.0f}% of the "
@@ -1238,6 +1281,11 @@ def main():
                                "block 16, bf16",
                    "launch": "hipgraph replay of 112 kernels", "global_batch": B},
         "frac_of_peak": round(value / PEAK_GBS, 4),
+        "copy_equivalent_step_us": round(copy_step_us, 2),
+        "copy_equivalent_note": "a graph of 112 plain copies in the chain's order, each moving the bytes of the "
+                                "op at its place (half read, half written): what a step of launches of these "
+                                "sizes attains",
+        "step_frac_of_copy_equivalent": round(copy_step_us / (ms * 1e3), 4),
         "step_bytes": nbytes["step"],
         "eager_ms_per_step": round(eager_ms, 5),
         "event_stamped_kernel_sum_us_per_step": round(kernel_sum_us, 2),

@@ -428,31 +428,29 @@ __global__ __launch_bounds__(kWideThreads) void wide_norm_kernel(const NormArgs 
 
 
 // Two-pass row norm for rows wider than LDS: lane t owns vectors
-// t + k * 1024 of the row; the first REG of them (k < REG) stay in
-// registers, the next `lds_vecs` vectors of the row in LDS, and only those
-// beyond are read again in loop 2 (from L2 or the Infinity Cache when they
-// are still there), so the extra traffic is the part that fits nowhere.
-// U vectors per lane are in flight per step of loop 1. Measured on MI355X
-// at [512, 262144] bf16: REG = 0 with the LDS full, 128.4 us, against
-// 139.7 us re-reading the whole row; keeping 2 or 4 vectors per lane in
-// registers as well measured 140-164 us (the register tier lengthens loop 1
-// without adding bytes in flight), so the dispatch uses REG = 0.
+// t + k * 1024 of the row; the first `lds_vecs` vectors of the row stay in
+// LDS after loop 1, and only those beyond are read again in loop 2 (from L2
+// or the Infinity Cache when they are still there), so the extra traffic is
+// the part that fits nowhere. U vectors per lane are in flight per step of
+// loop 1. Measured on MI355X at [512, 262144] bf16: 128.4 us with the LDS
+// full, against 139.7 us re-reading the whole row; also keeping 2 or 4
+// vectors per lane in registers measured 140-164 us (the register tier
+// lengthens loop 1 without adding bytes in flight), so there is none.
 struct TierArgs {
     NormArgs n;
-    int32_t lds_vecs;  // vectors of each row kept in LDS after the register tier
+    int32_t lds_vecs;  // vectors of each row kept in LDS
 };
 
-template <typename T, bool ADD, int REG, int U>
+template <typename T, bool ADD, int U>
 __global__ __launch_bounds__(kWideThreads) void wide_tier_kernel(const TierArgs ta) {
     extern __shared__ u32x4 stage[];
+    __shared__ float part[2][kWideWaves];
     const NormArgs& a = ta.n;
     const int lds_vecs = ta.lds_vecs;
-    __shared__ float part[2][kWideWaves];
     constexpr int kVec = T::kVec, W = kWideThreads;
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int64_t d = a.d;
     const int nvec = (int)((d + kVec - 1) / kVec);
-    const int lds_end = REG * W + lds_vecs;  // vectors [REG * W, lds_end) live in LDS
     int it = 0;
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x, ++it) {
         const void* xrow = row_ptr<T>(a.x, row, a.x_stride);
@@ -461,43 +459,10 @@ __global__ __launch_bounds__(kWideThreads) void wide_tier_kernel(const TierArgs 
         const bool vd = ADD && vec_ok(drow);
         void* orow = ADD ? row_ptr<T>(a.x_out, row, a.x_stride) : nullptr;
         float ss = 0.0f;
-        // Adds delta (ADD), stores the rounded sum, and accumulates the
-        // sum of squares of what the norm sees.
-        auto fold = [&](u32x4& xv, const u32x4& dv, int v) {
-            float xf[kVec];
-            unpack<T>(xv, xf);
-            if constexpr (ADD) {
-                float df[kVec];
-                unpack<T>(dv, df);
-#pragma unroll
-                for (int e = 0; e < kVec; ++e) xf[e] += df[e];
-                xv = pack<T>(xf);
-                store_raw<T, true>(orow, (int64_t)v * kVec, d, xv, vx);
-                unpack<T>(xv, xf);
-            }
-#pragma unroll
-            for (int e = 0; e < kVec; ++e) ss += xf[e] * xf[e];
-        };
-        // registers
-        u32x4 xr[REG > 0 ? REG : 1];
-        {
-            u32x4 dr[REG > 0 ? REG : 1];
-#pragma unroll
-            for (int k = 0; k < REG; ++k) {
-                const int v = tid + k * W;
-                xr[k] = u32x4{0u, 0u, 0u, 0u};
-                if (v < nvec) xr[k] = load_raw<T, true>(xrow, (int64_t)v * kVec, d, vx);
-                if constexpr (ADD) {
-                    dr[k] = u32x4{0u, 0u, 0u, 0u};
-                    if (v < nvec) dr[k] = load_raw<T, true>(drow, (int64_t)v * kVec, d, vd);
-                }
-            }
-#pragma unroll
-            for (int k = 0; k < REG; ++k)
-                if (tid + k * W < nvec) fold(xr[k], dr[k], tid + k * W);
-        }
-        // LDS, then the part that is read again in loop 2 (cached loads)
-        for (int v0 = REG * W + tid; v0 < nvec; v0 += W * U) {
+        // Loop 1: the part kept in LDS with nontemporal loads, the part read
+        // again with cached ones; the add variant stores the rounded sum,
+        // which is what the norm sees (and what loop 2 reads again).
+        for (int v0 = tid; v0 < nvec; v0 += W * U) {
             u32x4 xv[U], dv[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -505,8 +470,8 @@ __global__ __launch_bounds__(kWideThreads) void wide_tier_kernel(const TierArgs 
                 xv[u] = u32x4{0u, 0u, 0u, 0u};
                 dv[u] = xv[u];
                 if (v < nvec) {
-                    xv[u] = v < lds_end ? load_raw<T, true>(xrow, (int64_t)v * kVec, d, vx)
-                                        : load_raw<T, false>(xrow, (int64_t)v * kVec, d, vx);
+                    xv[u] = v < lds_vecs ? load_raw<T, true>(xrow, (int64_t)v * kVec, d, vx)
+                                         : load_raw<T, false>(xrow, (int64_t)v * kVec, d, vx);
                     if constexpr (ADD) dv[u] = load_raw<T, true>(drow, (int64_t)v * kVec, d, vd);
                 }
             }
@@ -514,8 +479,20 @@ __global__ __launch_bounds__(kWideThreads) void wide_tier_kernel(const TierArgs 
             for (int u = 0; u < U; ++u) {
                 const int v = v0 + u * W;
                 if (v >= nvec) continue;
-                fold(xv[u], dv[u], v);
-                if (v < lds_end) stage[v - REG * W] = xv[u];
+                float xf[kVec];
+                unpack<T>(xv[u], xf);
+                if constexpr (ADD) {
+                    float df[kVec];
+                    unpack<T>(dv[u], df);
+#pragma unroll
+                    for (int e = 0; e < kVec; ++e) xf[e] += df[e];
+                    xv[u] = pack<T>(xf);
+                    store_raw<T, true>(orow, (int64_t)v * kVec, d, xv[u], vx);
+                    unpack<T>(xv[u], xf);
+                }
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) ss += xf[e] * xf[e];
+                if (v < lds_vecs) stage[v] = xv[u];
             }
         }
         ss = wave_sum(ss);
@@ -526,11 +503,13 @@ __global__ __launch_bounds__(kWideThreads) void wide_tier_kernel(const TierArgs 
         for (int i = 0; i < kWideWaves; ++i) tot += part[it & 1][i];
         const float r = __builtin_amdgcn_rsqf(tot / (float)a.d + a.eps);
 
+        // Loop 2: the same lane owns the same vectors as in loop 1.
         void* yrow = row_ptr<T>(a.y, row, a.y_stride);
         const bool vy = vec_ok(yrow);
         const bool vw = vec_ok(a.w);
         const void* src = ADD ? static_cast<const void*>(orow) : xrow;
-        auto emit = [&](const u32x4& xv, int v) {
+        for (int v = tid; v < nvec; v += W) {
+            const u32x4 xv = v < lds_vecs ? stage[v] : load_raw<T, false>(src, (int64_t)v * kVec, d, vx);
             const u32x4 wv = load_raw<T, false>(a.w, (int64_t)v * kVec, d, vw);
             float xf[kVec], wf[kVec], yf[kVec];
             unpack<T>(xv, xf);
@@ -538,12 +517,7 @@ __global__ __launch_bounds__(kWideThreads) void wide_tier_kernel(const TierArgs 
 #pragma unroll
             for (int e = 0; e < kVec; ++e) yf[e] = xf[e] * r * wf[e];
             store_raw<T, true>(yrow, (int64_t)v * kVec, d, pack<T>(yf), vy);
-        };
-#pragma unroll
-        for (int k = 0; k < REG; ++k)
-            if (tid + k * W < nvec) emit(xr[k], tid + k * W);
-        for (int v = REG * W + tid; v < nvec; v += W)
-            emit(v < lds_end ? stage[v - REG * W] : load_raw<T, false>(src, (int64_t)v * kVec, d, vx), v);
+        }
     }
 }
 
@@ -559,7 +533,7 @@ static bool wide_lds_ready(size_t limit) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
     if (done[dev].load(std::memory_order_acquire)) return true;
-    const void* kern = TIER ? reinterpret_cast<const void*>(wide_tier_kernel<T, ADD, 0, kWideUnroll>)
+    const void* kern = TIER ? reinterpret_cast<const void*>(wide_tier_kernel<T, ADD, kWideUnroll>)
                             : reinterpret_cast<const void*>(wide_norm_kernel<T, ADD, true>);
     if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)limit) != hipSuccess)
         return false;
@@ -583,7 +557,7 @@ static int launch_wide(const NormArgs& a, void* stream) {
     }
     const int lds_vecs = (int)(cap / 16);
     if (lds_vecs > 0 && !wide_lds_ready<T, ADD, true>(cap)) return KCR_ERR_LAUNCH;
-    return launch(wide_tier_kernel<T, ADD, 0, kWideUnroll>, grid, dim3(kWideThreads), stream,
+    return launch(wide_tier_kernel<T, ADD, kWideUnroll>, grid, dim3(kWideThreads), stream,
                   TierArgs{a, lds_vecs}, (size_t)lds_vecs * 16);
 }
 
