@@ -71,8 +71,12 @@ __global__ __launch_bounds__(64) void clip_norm_kernel(const ClipArgs a) {
 
 template <typename T, bool APC, bool GPC>
 static int launch_clip(const ClipArgs& a, dim3 grid, void* stream, bool vec) {
-    return vec ? launch(clip_norm_kernel<T, APC, GPC, true>, grid, dim3(64), stream, a)
-               : launch(clip_norm_kernel<T, APC, GPC, false>, grid, dim3(64), stream, a);
+    // fp32 rows are always dword aligned: only 2-byte types need element access.
+    if constexpr (sizeof(typename T::storage) == 4)
+        return launch(clip_norm_kernel<T, APC, GPC, true>, grid, dim3(64), stream, a);
+    else
+        return vec ? launch(clip_norm_kernel<T, APC, GPC, true>, grid, dim3(64), stream, a)
+                   : launch(clip_norm_kernel<T, APC, GPC, false>, grid, dim3(64), stream, a);
 }
 
 }  // namespace kcr

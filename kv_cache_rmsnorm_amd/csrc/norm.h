@@ -55,7 +55,7 @@ struct NormShape {
     int vpt, wpr, groups;
 };
 
-inline NormShape norm_shape(int64_t nvec, bool add) {
+constexpr NormShape norm_shape(int64_t nvec, bool add) {
     if (nvec <= 0) return {0, 0, 0};
     if (!add && nvec <= 5 * 64) {
         const int vpt = (int)((nvec + 63) / 64);
@@ -82,6 +82,25 @@ inline NormShape norm_shape(int64_t nvec, bool add) {
     }
     return {best_v, best_w, best_w <= 3 ? 2 : 1};
 }
+
+// The (vpt, wpr) pairs norm_shape returns for some width of up to kRegMaxVec
+// vectors, with the groups it pairs them with (0: never returned). Evaluated
+// at compile time, so the dispatch instantiates exactly these shapes.
+struct RuleShapes {
+    int8_t groups[9][9];
+};
+
+constexpr RuleShapes rule_shapes(bool add) {
+    RuleShapes r{};
+    for (int64_t n = 1; n <= kRegMaxVec; ++n) {
+        const NormShape s = norm_shape(n, add);
+        if (s.vpt >= 1 && s.vpt <= 8 && s.wpr >= 1 && s.wpr <= 8) r.groups[s.vpt][s.wpr] = (int8_t)s.groups;
+    }
+    return r;
+}
+
+template <bool ADD>
+constexpr RuleShapes kRuleShapes = rule_shapes(ADD);
 
 
 }  // namespace kcr

@@ -562,24 +562,59 @@ static int launch_wide(const NormArgs& a, void* stream) {
 }
 
 // ------------------------------------------------------------ dispatch
+// Large calls: the rule's shape with the rule's row groups per workgroup.
+// Only the shapes the rule can return are instantiated (kRuleShapes).
 template <typename T, bool ADD, int VPT, int WPR>
-static int launch_g(const NormArgs& a, void* stream, int groups) {
-    if (groups == 4) return launch_norm<T, NormCfg<VPT, WPR, 4, true, true>, ADD>(a, stream);
-    if (groups == 2) return launch_norm<T, NormCfg<VPT, WPR, 2, true, true>, ADD>(a, stream);
-    return launch_norm<T, NormCfg<VPT, WPR, 1, true, true>, ADD>(a, stream);
+static int launch_rule(const NormArgs& a, void* stream) {
+    constexpr int G = kRuleShapes<ADD>.groups[VPT][WPR];
+    if constexpr (G == 0) return KCR_ERR_SHAPE;
+    else return launch_norm<T, NormCfg<VPT, WPR, G, true, true>, ADD>(a, stream);
 }
 
-template <typename T, bool ADD, int WPR>
-static int launch_w(const NormArgs& a, void* stream, int vpt, int groups) {
-    switch (vpt) {
-        case 1: return launch_g<T, ADD, 1, WPR>(a, stream, groups);
-        case 2: return launch_g<T, ADD, 2, WPR>(a, stream, groups);
-        case 3: return launch_g<T, ADD, 3, WPR>(a, stream, groups);
-        case 4: return launch_g<T, ADD, 4, WPR>(a, stream, groups);
-        case 5: return launch_g<T, ADD, 5, WPR>(a, stream, groups);
-        case 6: return WPR == 8 ? launch_g<T, ADD, 6, WPR>(a, stream, groups) : KCR_ERR_SHAPE;
-        case 7: return WPR == 8 ? launch_g<T, ADD, 7, WPR>(a, stream, groups) : KCR_ERR_SHAPE;
-        case 8: return WPR == 8 ? launch_g<T, ADD, 8, WPR>(a, stream, groups) : KCR_ERR_SHAPE;
+// Small calls (decode batches): the rule's shape with one row group per
+// workgroup. In the 28-layer, batch-256 decode chain on MI355X (a captured
+// graph of 112 launches) this takes the step from 341 to 335 us against the
+// two-group shapes that win at large shapes. Loads and stores stay nontemporal: cached
+// ones measured 20-34 us slower per step there, since every kernel must
+// write its dirty L2 lines back before the next one starts. Small calls are
+// latency-bound: where the shape leaves lanes past the row's end, they issue
+// every load before waiting (EAGER, load_whole); where every lane holds a whole
+// vector, the plain form saves the zeroing moves.
+template <typename T, bool ADD, int VPT, int WPR, bool EAGER>
+static int launch_rule_small(const NormArgs& a, void* stream) {
+    if constexpr (kRuleShapes<ADD>.groups[VPT][WPR] == 0) return KCR_ERR_SHAPE;
+    else return launch_norm<T, NormCfg<VPT, WPR, 1, true, true, 1, EAGER>, ADD>(a, stream);
+}
+
+template <typename T, bool ADD, int VPT>
+static int launch_rule_v(const NormArgs& a, void* stream, int wpr, bool small, bool eager) {
+    switch (wpr) {
+#define KCR_RULE_CASE(W)                                                                    \
+    case W:                                                                                 \
+        if (!small) return launch_rule<T, ADD, VPT, W>(a, stream);                          \
+        return eager ? launch_rule_small<T, ADD, VPT, W, true>(a, stream)                   \
+                     : launch_rule_small<T, ADD, VPT, W, false>(a, stream);
+        KCR_RULE_CASE(1) KCR_RULE_CASE(2) KCR_RULE_CASE(3) KCR_RULE_CASE(4)
+        KCR_RULE_CASE(5) KCR_RULE_CASE(6) KCR_RULE_CASE(7) KCR_RULE_CASE(8)
+#undef KCR_RULE_CASE
+    }
+    return KCR_ERR_SHAPE;
+}
+
+template <typename T, bool ADD>
+static int launch_by_rule(const NormArgs& a, void* stream, const NormShape& s, bool small) {
+    const int64_t nvec = (a.d + T::kVec - 1) / T::kVec;
+    if (!small && kRuleShapes<ADD>.groups[s.vpt][s.wpr] != s.groups) return KCR_ERR_SHAPE;
+    const bool eager = (int64_t)s.vpt * 64 * s.wpr > nvec;
+    switch (s.vpt) {
+        case 1: return launch_rule_v<T, ADD, 1>(a, stream, s.wpr, small, eager);
+        case 2: return launch_rule_v<T, ADD, 2>(a, stream, s.wpr, small, eager);
+        case 3: return launch_rule_v<T, ADD, 3>(a, stream, s.wpr, small, eager);
+        case 4: return launch_rule_v<T, ADD, 4>(a, stream, s.wpr, small, eager);
+        case 5: return launch_rule_v<T, ADD, 5>(a, stream, s.wpr, small, eager);
+        case 6: return launch_rule_v<T, ADD, 6>(a, stream, s.wpr, small, eager);
+        case 7: return launch_rule_v<T, ADD, 7>(a, stream, s.wpr, small, eager);
+        case 8: return launch_rule_v<T, ADD, 8>(a, stream, s.wpr, small, eager);
     }
     return KCR_ERR_SHAPE;
 }
@@ -633,8 +668,7 @@ static int launch_unaligned(const NormArgs& a, void* stream) {
             case 8: return launch_norm<T, NormCfg<8, 1, 2, true, true>, ADD, false>(a, stream);
         }
     }
-    switch ((nvec + 511) / 512) {
-        case 1: return launch_norm<T, NormCfg<1, 8, 1, true, true>, ADD, false>(a, stream);
+    switch ((nvec + 511) / 512) {  // 2..8 here: up to 512 vectors took the one-wave shapes
         case 2: return launch_norm<T, NormCfg<2, 8, 1, true, true>, ADD, false>(a, stream);
         case 3: return launch_norm<T, NormCfg<3, 8, 1, true, true>, ADD, false>(a, stream);
         case 4: return launch_norm<T, NormCfg<4, 8, 1, true, true>, ADD, false>(a, stream);
@@ -642,59 +676,6 @@ static int launch_unaligned(const NormArgs& a, void* stream) {
         case 6: return launch_norm<T, NormCfg<6, 8, 1, true, true>, ADD, false>(a, stream);
         case 7: return launch_norm<T, NormCfg<7, 8, 1, true, true>, ADD, false>(a, stream);
         case 8: return launch_norm<T, NormCfg<8, 8, 1, true, true>, ADD, false>(a, stream);
-    }
-    return KCR_ERR_SHAPE;
-}
-
-// Small calls (decode batches): one row group per workgroup. In the
-// 28-layer, batch-256 decode chain on MI355X (a captured graph of 112
-// launches) this takes the step from 341 to 335 us against the two-group
-// shapes that win at large shapes. Loads and stores stay nontemporal: cached
-// ones measured 20-34 us slower per step there, since every kernel must
-// write its dirty L2 lines back before the next one starts. Small calls are
-// latency-bound: where the shape leaves lanes past the row's end, they issue
-// every load before waiting (EAGER, load_whole); where every lane holds a whole
-// vector, the plain form saves the zeroing moves.
-template <typename T, bool ADD, int WPR, bool EAGER>
-static int launch_small_w(const NormArgs& a, void* stream, int vpt) {
-    switch (vpt) {
-        case 1: return launch_norm<T, NormCfg<1, WPR, 1, true, true, 1, EAGER>, ADD>(a, stream);
-        case 2: return launch_norm<T, NormCfg<2, WPR, 1, true, true, 1, EAGER>, ADD>(a, stream);
-        case 3: return launch_norm<T, NormCfg<3, WPR, 1, true, true, 1, EAGER>, ADD>(a, stream);
-        case 4: return launch_norm<T, NormCfg<4, WPR, 1, true, true, 1, EAGER>, ADD>(a, stream);
-        case 5: return launch_norm<T, NormCfg<5, WPR, 1, true, true, 1, EAGER>, ADD>(a, stream);
-        case 6: return WPR == 8 ? launch_norm<T, NormCfg<6, WPR, 1, true, true, 1, EAGER>, ADD>(a, stream) : KCR_ERR_SHAPE;
-        case 7: return WPR == 8 ? launch_norm<T, NormCfg<7, WPR, 1, true, true, 1, EAGER>, ADD>(a, stream) : KCR_ERR_SHAPE;
-        case 8: return WPR == 8 ? launch_norm<T, NormCfg<8, WPR, 1, true, true, 1, EAGER>, ADD>(a, stream) : KCR_ERR_SHAPE;
-    }
-    return KCR_ERR_SHAPE;
-}
-
-template <typename T, bool ADD>
-static int launch_small(const NormArgs& a, void* stream, const NormShape& s) {
-    const int64_t nvec = (a.d + T::kVec - 1) / T::kVec;
-    if ((int64_t)s.vpt * 64 * s.wpr > nvec) {
-        switch (s.wpr) {
-            case 1: return launch_small_w<T, ADD, 1, true>(a, stream, s.vpt);
-            case 2: return launch_small_w<T, ADD, 2, true>(a, stream, s.vpt);
-            case 3: return launch_small_w<T, ADD, 3, true>(a, stream, s.vpt);
-            case 4: return launch_small_w<T, ADD, 4, true>(a, stream, s.vpt);
-            case 5: return launch_small_w<T, ADD, 5, true>(a, stream, s.vpt);
-            case 6: return launch_small_w<T, ADD, 6, true>(a, stream, s.vpt);
-            case 7: return launch_small_w<T, ADD, 7, true>(a, stream, s.vpt);
-            case 8: return launch_small_w<T, ADD, 8, true>(a, stream, s.vpt);
-        }
-        return KCR_ERR_SHAPE;
-    }
-    switch (s.wpr) {
-        case 1: return launch_small_w<T, ADD, 1, false>(a, stream, s.vpt);
-        case 2: return launch_small_w<T, ADD, 2, false>(a, stream, s.vpt);
-        case 3: return launch_small_w<T, ADD, 3, false>(a, stream, s.vpt);
-        case 4: return launch_small_w<T, ADD, 4, false>(a, stream, s.vpt);
-        case 5: return launch_small_w<T, ADD, 5, false>(a, stream, s.vpt);
-        case 6: return launch_small_w<T, ADD, 6, false>(a, stream, s.vpt);
-        case 7: return launch_small_w<T, ADD, 7, false>(a, stream, s.vpt);
-        case 8: return launch_small_w<T, ADD, 8, false>(a, stream, s.vpt);
     }
     return KCR_ERR_SHAPE;
 }
@@ -720,19 +701,9 @@ int run_norm(const NormArgs& a, void* stream) {
     if (norm_call_bytes<T, ADD>(a) <= kNormSmallCallBytes) {
         const int rc = launch_wave_rows<T, ADD>(a, stream);
         if (rc <= 0) return rc;
-        return launch_small<T, ADD>(a, stream, s);
+        return launch_by_rule<T, ADD>(a, stream, s, true);
     }
-    switch (s.wpr) {
-        case 1: return launch_w<T, ADD, 1>(a, stream, s.vpt, s.groups);
-        case 2: return launch_w<T, ADD, 2>(a, stream, s.vpt, s.groups);
-        case 3: return launch_w<T, ADD, 3>(a, stream, s.vpt, s.groups);
-        case 4: return launch_w<T, ADD, 4>(a, stream, s.vpt, s.groups);
-        case 5: return launch_w<T, ADD, 5>(a, stream, s.vpt, s.groups);
-        case 6: return launch_w<T, ADD, 6>(a, stream, s.vpt, s.groups);
-        case 7: return launch_w<T, ADD, 7>(a, stream, s.vpt, s.groups);
-        case 8: return launch_w<T, ADD, 8>(a, stream, s.vpt, s.groups);
-    }
-    return KCR_ERR_SHAPE;
+    return launch_by_rule<T, ADD>(a, stream, s, false);
 }
 
 }  // namespace kcr

@@ -234,7 +234,10 @@ static int dispatch_rope_lpu(const RopeArgs& a, int64_t T_tokens, void* stream) 
     if (chunks <= 8) return launch_rope<T, RopeCfg<8, HPU, true, true, BLOCK>, QKN>(a, T_tokens, stream);
     if (chunks <= 16) return launch_rope<T, RopeCfg<16, HPU, true, true, BLOCK>, QKN>(a, T_tokens, stream);
     if (chunks <= 32) return launch_rope<T, RopeCfg<32, HPU, true, true, BLOCK>, QKN>(a, T_tokens, stream);
-    if (chunks <= 64) return launch_rope<T, RopeCfg<64, HPU, true, true, BLOCK>, QKN>(a, T_tokens, stream);
+    // 64 chunks of half a head: only fp32 reaches it under KCR_ROPE_MAX_HEAD_DIM.
+    if constexpr (T::kVec * 64 * 2 <= KCR_ROPE_MAX_HEAD_DIM) {
+        if (chunks <= 64) return launch_rope<T, RopeCfg<64, HPU, true, true, BLOCK>, QKN>(a, T_tokens, stream);
+    }
     return KCR_ERR_SHAPE;
 }
 
@@ -359,14 +362,21 @@ static int launch_rope_token(const RopeArgs& a, int64_t T_tokens, void* stream) 
         return fused ? launch(rope_token_kernel<T, L, QKN, 128, true>, grid, block, stream, a)
                      : launch(rope_token_kernel<T, L, QKN, 128, false>, grid, block, stream, a);
     }
+    // Every other power-of-two chunk count up to KCR_ROPE_MAX_HEAD_DIM (the
+    // count of head_dim 128 took the fixed-size form above).
+    auto generic = [&](auto lpu) -> int {
+        constexpr int L = decltype(lpu)::value;
+        if constexpr (L == 64 / T::kVec || T::kVec * L * 2 > KCR_ROPE_MAX_HEAD_DIM) return 1;
+        else return launch(rope_token_kernel<T, L, QKN>, grid, block, stream, a);
+    };
     switch (chunks) {
-        case 1: return launch(rope_token_kernel<T, 1, QKN>, grid, block, stream, a);
-        case 2: return launch(rope_token_kernel<T, 2, QKN>, grid, block, stream, a);
-        case 4: return launch(rope_token_kernel<T, 4, QKN>, grid, block, stream, a);
-        case 8: return launch(rope_token_kernel<T, 8, QKN>, grid, block, stream, a);
-        case 16: return launch(rope_token_kernel<T, 16, QKN>, grid, block, stream, a);
-        case 32: return launch(rope_token_kernel<T, 32, QKN>, grid, block, stream, a);
-        case 64: return launch(rope_token_kernel<T, 64, QKN>, grid, block, stream, a);
+        case 1: return generic(std::integral_constant<int, 1>{});
+        case 2: return generic(std::integral_constant<int, 2>{});
+        case 4: return generic(std::integral_constant<int, 4>{});
+        case 8: return generic(std::integral_constant<int, 8>{});
+        case 16: return generic(std::integral_constant<int, 16>{});
+        case 32: return generic(std::integral_constant<int, 32>{});
+        case 64: return generic(std::integral_constant<int, 64>{});
     }
     return 1;
 }

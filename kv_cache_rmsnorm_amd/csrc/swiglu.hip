@@ -131,8 +131,12 @@ __global__ __launch_bounds__(kSwigluRowBlock) void swiglu_rows_kernel(const Swig
 template <typename T, typename C, typename Act>
 static int launch_swiglu(const SwigluArgs& a, void* stream, bool vec) {
     const dim3 grid((uint32_t)(((int64_t)a.total + C::BLOCK * C::UNROLL - 1) / (C::BLOCK * C::UNROLL)));
-    return vec ? launch(swiglu_kernel<T, C, Act, true>, grid, dim3(C::BLOCK), stream, a)
-               : launch(swiglu_kernel<T, C, Act, false>, grid, dim3(C::BLOCK), stream, a);
+    // fp32 rows are always dword aligned: only 2-byte types need element access.
+    if constexpr (sizeof(typename T::storage) == 4)
+        return launch(swiglu_kernel<T, C, Act, true>, grid, dim3(C::BLOCK), stream, a);
+    else
+        return vec ? launch(swiglu_kernel<T, C, Act, true>, grid, dim3(C::BLOCK), stream, a)
+                   : launch(swiglu_kernel<T, C, Act, false>, grid, dim3(C::BLOCK), stream, a);
 }
 
 // Shared argument checks of the gated activations.

@@ -113,3 +113,33 @@ def test_trace_summary_timed_region(tmp_path, capsys):
     timed = text.split("## The timed region")[1]
     assert f"| {56 * steps} | 56 | 2.00 |" in timed.replace("`", "")
     assert f"| {28 * steps} | 28 | 4.00 |" in timed.replace("`", "")
+
+
+def test_kernel_coverage_summary(tmp_path):
+    """tests/kernel_coverage.py: compiled variants from nm's launch-stub
+    symbols, run variants from a kernel trace (return type, parameter list and
+    spacing ignored), and the variants that never ran listed by name."""
+    import kernel_coverage as kc
+    nm = ("0000000000001000 T kcr::__device_stub__copy_kernel(kcr::CopyArgs)\n"
+          "0000000000002000 T void kcr::__device_stub__row_norm_kernel<kcr::Bf16, kcr::NormCfg<1, 3, 2, true, "
+          "true, 1, false>, true, true>(kcr::NormArgs)\n"
+          "0000000000003000 T void kcr::__device_stub__row_norm_kernel<kcr::F32, kcr::NormCfg<5, 2, 4, true, "
+          "true, 1, false>, false, true>(kcr::NormArgs)\n"
+          "0000000000004000 T kcr::run_norm(kcr::NormArgs const&, void*)\n")
+    compiled = kc.compiled_kernels(nm)
+    assert len(compiled) == 3
+    d = tmp_path / "trace"
+    d.mkdir()
+    with open(d / "t_kernel_trace.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kind", "Kernel_Name"])
+        w.writerow(["KERNEL_DISPATCH", "kcr::copy_kernel(kcr::CopyArgs)"])
+        w.writerow(["KERNEL_DISPATCH", "void kcr::row_norm_kernel<kcr::Bf16, kcr::NormCfg<1, 3, 2, true, true, 1, "
+                                       "false>, true, true>(kcr::NormArgs)"])
+        w.writerow(["KERNEL_DISPATCH", "void at::native::vectorized_elementwise_kernel<4>(int)"])
+    ran = kc.traced_kernels(str(d))
+    text = kc.summary(compiled, ran)
+    assert "| `kcr::row_norm_kernel` | 2 | 1 |" in text
+    assert "| all | 3 | 2 |" in text
+    assert "kcr::row_norm_kernel<kcr::F32,kcr::NormCfg<5,2,4,true,true,1,false>,false,true>" in text
+    assert "Every compiled" not in text

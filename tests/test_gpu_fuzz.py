@@ -105,18 +105,19 @@ def test_fuzz_norms(kcr, case):
     assert_close(y.cpu().double().numpy(), y_ref, dt, f"norm case {case}")
 
 
-@pytest.mark.parametrize("case", range(24))
+@pytest.mark.parametrize("case", range(48))
 def test_fuzz_norm_wave_rows(kcr, case):
     """Small calls whose rows are exactly 64 * VPT 16-byte vectors (VPT 1..8)
     take the one-wave-per-row kernel: every VPT in every dtype, plain and
-    add, with row strides, buffer offsets and in-place output."""
+    add (48 cases, one per combination), with row strides, buffer offsets
+    and in-place output."""
     rng = np.random.default_rng(12000 + case)
     dt = DTS[case % 3]
-    vpt = 1 + (case // 3) % 8
+    add = bool((case // 3) % 2)
+    vpt = 1 + case // 6
     vec = 16 // dt.itemsize
     d = 64 * vpt * vec
     rows = int(rng.choice([1, int(rng.integers(2, 64)), int(rng.integers(200, 400))]))
-    add = bool(case % 2)
     pad = int(rng.choice([0, 8, 32])) * (2 if dt.itemsize == 2 else 1)
     off = int(rng.choice([0, 8])) * (2 if dt.itemsize == 2 else 1)
     in_place = (not add) and bool(rng.integers(0, 2))

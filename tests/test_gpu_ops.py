@@ -131,8 +131,9 @@ def test_rmsnorm_wide_row_loop(kcr):
 # 4096 rows (some read two rows per row group before writing either); 4099
 # rows leave the last group half empty.
 TUNED = [(torch.bfloat16, 1536), (torch.bfloat16, 2048), (torch.bfloat16, 2176),
-         (torch.bfloat16, 4096), (torch.bfloat16, 5120), (torch.float16, 2176),
-         (torch.float16, 4096), (torch.float32, 1024), (torch.float32, 2176)]
+         (torch.bfloat16, 4096), (torch.bfloat16, 5120), (torch.float16, 1536),
+         (torch.float16, 2048), (torch.float16, 2176), (torch.float16, 4096), (torch.float16, 5120),
+         (torch.float32, 1024), (torch.float32, 2176)]
 
 
 @pytest.mark.parametrize("dt,d", TUNED, ids=lambda v: DT_ID.get(v, str(v)))
