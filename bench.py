@@ -863,10 +863,23 @@ KERNEL_SOURCES = {
 }
 
 
+_C_TOKENS = re.compile(r'"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'|//[^\n]*|/\*.*?\*/', re.S)
+
+
+def code_only(text: str) -> str:
+    """C/C++ source with its comments removed and its whitespace collapsed
+    (string and character literals kept), so that an edit to comments or
+    layout alone leaves the hash below unchanged."""
+    text = _C_TOKENS.sub(lambda m: " " if m.group(0)[0] == "/" else m.group(0), text)
+    return re.sub(r"\s+", " ", text).strip()
+
+
 def kernel_source_sha(op: str) -> str:
+    """Hash of the code (comments and layout ignored) of the files that make
+    up an op's kernels and their launch."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[op]:
-        h.update(open(os.path.join(ROOT, "kv_cache_rmsnorm_amd", "csrc", f), "rb").read())
+        h.update(code_only(open(os.path.join(ROOT, "kv_cache_rmsnorm_amd", "csrc", f)).read()).encode())
     return h.hexdigest()
 
 

@@ -13,18 +13,21 @@
 //  * Virtual heads: following the GQA mapping of the same section,
 //    kv_head = head / (n_head / n_kv_head), KV group g is the query heads
 //    g*G .. g*G+G-1 (G = n_head / n_kv_head, contiguous in memory), then K
-//    head g, then V head g -- G + 2 heads of equal cost. A work unit is a run
-//    of HPU consecutive virtual heads of one token (1 for decode batches, 2
-//    for prefill), so every unit does the same work and no lane idles on
-//    K/V.
-//  * LPU lanes per unit (the next power of two at or above the number of
-//    16-byte chunks in half a head: 8 for bf16 head_dim 128). Lane c owns
-//    chunk c of the first half AND chunk c of the second half, so each
+//    head g, then V head g -- G + 2 heads of equal cost.
+//  * LPU lanes per virtual head (the number of 16-byte chunks in half a
+//    head, rounded up to a power of two: 8 for bf16 head_dim 128). Lane c
+//    owns chunk c of the first half AND chunk c of the second half, so each
 //    rotation pair (i, i + d/2) sits in one lane and needs no shuffle.
-//  * cos/sin for the lane's frequencies are loaded once per unit (fp32
-//    table rows, L2-resident across tokens) and reused for its HPU heads;
-//    all heads of a unit are loaded before any is stored. One-pass grid,
-//    nontemporal loads and stores of the streamed heads.
+//  * One workgroup per token (rope_token_kernel) wherever half a head is a
+//    power-of-two number of chunks and the token's heads fit 1024 lanes:
+//    the token's position and slot are then scalar loads. Other head
+//    layouts take the unit kernel (rope_kvstore_kernel): a unit is a run of
+//    HPU consecutive virtual heads of one token (1 for decode batches, 2 for
+//    prefill), so every unit does the same work and no lane idles on K/V.
+//  * cos/sin for the lane's frequencies are loaded once per token or unit
+//    (fp32 table rows, L2-resident across tokens); all heads are loaded
+//    before any is stored. One-pass grid, nontemporal loads and stores of
+//    the streamed heads.
 //  * K_rot and V are written with 16-byte stores at
 //    ((which * n_slots + slot) * n_kv_head + g) * head_dim: the cache's
 //    (block, offset) pair flattens to the slot, so no division is needed.

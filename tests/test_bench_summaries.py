@@ -143,3 +143,13 @@ def test_kernel_coverage_summary(tmp_path):
     assert "| all | 3 | 2 |" in text
     assert "kcr::row_norm_kernel<kcr::F32,kcr::NormCfg<5,2,4,true,true,1,false>,false,true>" in text
     assert "Every compiled" not in text
+
+
+def test_source_hash_ignores_comments_only():
+    """The counter summary's source hash changes with the code, not with its
+    comments or layout; string literals that look like comments are code."""
+    base = 'int f(int x) {  // doubles x\n    return 2 * x; /* the\n product */ }\nconst char* s = "a // b";\n'
+    same = '/* header */\nint f(int x) {\n  return 2 * x;\n}\nconst char* s = "a // b";  // tail\n'
+    assert bench.code_only(base) == bench.code_only(same)
+    assert bench.code_only(base) != bench.code_only(base.replace("2 * x", "3 * x"))
+    assert bench.code_only(base) != bench.code_only(base.replace('"a // b"', '"a // c"'))
