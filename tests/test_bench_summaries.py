@@ -153,3 +153,15 @@ def test_source_hash_ignores_comments_only():
     assert bench.code_only(base) == bench.code_only(same)
     assert bench.code_only(base) != bench.code_only(base.replace("2 * x", "3 * x"))
     assert bench.code_only(base) != bench.code_only(base.replace('"a // b"', '"a // c"'))
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py measures one GPU: --gpus above 1 (or a WORLD_SIZE above 1)
+    exits with status 2 and says why, before touching a device."""
+    import subprocess
+    for args, env in ((["--gpus", "2"], {}), ([], {"WORLD_SIZE": "4"})):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], capture_output=True, text=True,
+                           env={**os.environ, **env}, timeout=120)
+        assert r.returncode == 2, r.stderr
+        assert "one GPU only" in r.stderr
+        assert r.stdout == ""
