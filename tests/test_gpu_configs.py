@@ -452,3 +452,19 @@ def test_large_wide_rmsnorm_sampled(kcr, rows, d):
                                      np.random.default_rng(6).choice(rows, 24, replace=False)]))
     ref = oracle.rmsnorm(np_bits(wl["x"][pick]), np_bits(wl["w"]), f32eps(wl["eps"]))
     assert_close(y[pick].double().numpy(), ref, torch.bfloat16, "sampled wide rows")
+
+
+def test_large_wide_add_rmsnorm_sampled(kcr):
+    """The residual-add form of the LDS-staged wide-row kernel at the
+    benchmark's shape, [2048, 65536] bf16: the updated residual bit-exact and
+    the normalised rows within tolerance, on sampled rows."""
+    rows, d = 2048, 65536
+    say(f"large wide add_rmsnorm [{rows}, {d}] bf16, sampled rows")
+    wl = workloads.add_rmsnorm_rows(rows=rows, d=d, dtype="bf16", seed=3)
+    x = wl["x"].cuda()
+    y = kcr.add_rmsnorm(x, wl["delta"].cuda(), wl["w"].cuda(), wl["eps"]).cpu()
+    pick = np.unique(np.concatenate([[0, rows - 1], np.random.default_rng(7).choice(rows, 30, replace=False)]))
+    x_ref, y_ref = oracle.add_rmsnorm(np_bits(wl["x"][pick]), np_bits(wl["delta"][pick]), np_bits(wl["w"]),
+                                      f32eps(wl["eps"]))
+    assert np.array_equal(np_bits(x[torch.from_numpy(pick).cuda()].cpu()).view(np.uint8), x_ref.view(np.uint8))
+    assert_close(y[pick].double().numpy(), y_ref, torch.bfloat16, "sampled wide add rows")
