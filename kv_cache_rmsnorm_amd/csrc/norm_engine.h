@@ -255,17 +255,22 @@ template <typename T, bool ADD>
 static bool rows_dword_aligned(const NormArgs& a);
 
 // ------------------------------------------------------- decode-size rows
-// Small calls whose rows are exactly VPT * 64 whole 16-byte vectors (every
-// row base dword aligned): one wave per row, lane l holding vectors l,
-// l + 64, ..., so the row needs no LDS exchange, and no access is
-// predicated. The code is kept to the straight line the decode chain
-// rewards: every load of the row is issued before the first wait, offsets
-// within the row are 32-bit, and there is no element path. In the 28-layer,
-// batch-256 decode chain on MI355X (a graph of 112 launches) this took the
-// step from 331 to 314 us against the row engine at the same sizes; the
-// next launches' loads waited less (RoPE's median load latency 373 -> 224
-// ns) when the add kernel's stores followed this pattern.
-template <typename T, int VPT, bool ADD>
+// Small calls whose rows are whole 16-byte vectors (every row base dword
+// aligned), at most VPT * 64 of them: one wave per row, lane l holding
+// vectors l, l + 64, ..., so the row needs no LDS exchange. The code is kept
+// to the straight line the decode chain rewards: every load of the row is
+// issued before the first wait, offsets within the row are 32-bit, and there
+// is no element path. In the 28-layer, batch-256 decode chain on MI355X (a
+// graph of 112 launches) this took the step from 331 to 314 us against the
+// row engine at the same sizes; the next launches' loads waited less (RoPE's
+// median load latency 373 -> 224 ns) when the add kernel's stores followed
+// this pattern.
+// RAGGED: the row has fewer than VPT * 64 vectors. Lanes past its end load
+// the row's last vector (in bounds, on lines the wave reads anyway), select
+// zero in place of it and store nothing, so the loads stay unconditional:
+// at [512, 2176] bf16, 2.92 against 3.20 us per launch in a graph for the
+// row engine's one-wave shape with predicated loads.
+template <typename T, int VPT, bool ADD, bool RAGGED = false>
 __global__ __launch_bounds__(64) void row_norm_wave_kernel(const NormArgs a) {
     using S = typename T::storage;
     constexpr int kVec = T::kVec;
@@ -274,12 +279,32 @@ __global__ __launch_bounds__(64) void row_norm_wave_kernel(const NormArgs a) {
     const S* xr = static_cast<const S*>(a.x) + row * a.x_stride;
     const S* dr = ADD ? static_cast<const S*>(a.delta) + row * a.delta_stride : nullptr;
     u32x4 x[VPT], dv[VPT], w[VPT];
+    bool in[VPT];  // RAGGED: the lane's vector j lies in the row
+    if constexpr (RAGGED) {
+        const int nvec = a.d / kVec;  // whole vectors (checked on the host)
 #pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-        const int e = (j * 64 + lane) * kVec;
-        x[j] = ld16_nt<T>(xr, e);
-        if constexpr (ADD) dv[j] = ld16_nt<T>(dr, e);
-        w[j] = ld16<T>(a.w, e);
+        for (int j = 0; j < VPT; ++j) {
+            const int v = j * 64 + lane;
+            in[j] = v < nvec;
+            const int e = (in[j] ? v : nvec - 1) * kVec;
+            x[j] = ld16_nt<T>(xr, e);
+            if constexpr (ADD) dv[j] = ld16_nt<T>(dr, e);
+            w[j] = ld16<T>(a.w, e);
+        }
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            x[j] = in[j] ? x[j] : z;
+            if constexpr (ADD) dv[j] = in[j] ? dv[j] : z;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            const int e = (j * 64 + lane) * kVec;
+            x[j] = ld16_nt<T>(xr, e);
+            if constexpr (ADD) dv[j] = ld16_nt<T>(dr, e);
+            w[j] = ld16<T>(a.w, e);
+        }
     }
     float ss = 0.0f;
     S* const xo = ADD ? static_cast<S*>(a.x_out) + row * a.x_stride : nullptr;
@@ -293,7 +318,7 @@ __global__ __launch_bounds__(64) void row_norm_wave_kernel(const NormArgs a) {
 #pragma unroll
             for (int e = 0; e < kVec; ++e) xf[e] += df[e];
             x[j] = pack<T>(xf);  // the rounded sum: stored, and normalised below
-            st16_nt<T>(xo, (j * 64 + lane) * kVec, x[j]);
+            if (!RAGGED || in[j]) st16_nt<T>(xo, (j * 64 + lane) * kVec, x[j]);
             unpack<T>(x[j], xf);
         }
 #pragma unroll
@@ -309,20 +334,45 @@ __global__ __launch_bounds__(64) void row_norm_wave_kernel(const NormArgs a) {
         unpack<T>(w[j], wf);
 #pragma unroll
         for (int e = 0; e < kVec; ++e) yf[e] = xf[e] * rs * wf[e];
-        st16_nt<T>(yr, (j * 64 + lane) * kVec, pack<T>(yf));
+        if (!RAGGED || in[j]) st16_nt<T>(yr, (j * 64 + lane) * kVec, pack<T>(yf));
     }
 }
 
+// Rows of whole vectors short of a multiple of 64 take one wave while they
+// need at most this many vectors per lane: 5 plain (where the rule gives one
+// wave too), 4 for the add variant. Measured in graphs of [512, D] launches
+// on MI355X against the rule's shapes: plain D = 1000 and 2176 bf16, 1000
+// fp32 5-9% faster; add D = 1000 bf16 and fp32 7-8% faster, D = 2176 bf16
+// 1% slower; one wave of 6-8 vectors 3-10% slower.
+template <bool ADD>
+constexpr int kRaggedWaveMaxVpt = ADD ? 4 : 5;
+
 // Launches row_norm_wave_kernel when the call qualifies (dword-aligned rows
-// of exactly 64, 128, ..., 512 vectors); returns 1 when it does not.
+// of whole vectors: exactly 64, 128, ..., 512 of them, or a ragged count up
+// to kRaggedWaveMaxVpt * 64); returns 1 when it does not.
 template <typename T, bool ADD>
 static int launch_wave_rows(const NormArgs& a, void* stream) {
     constexpr int64_t kRow = 64 * T::kVec;
-    if (a.d % kRow != 0 || a.d / kRow > 8 || !rows_dword_aligned<T, ADD>(a)) return 1;
+    if (a.d % T::kVec != 0 || !rows_dword_aligned<T, ADD>(a)) return 1;
     // one 64-lane workgroup per row; small calls stay far below 2^26 rows
     if (a.rows >= (int64_t(1) << 26)) return 1;
+    const int64_t vpt = (a.d + kRow - 1) / kRow;
+    const bool exact = a.d % kRow == 0;
+    if (vpt > (exact ? 8 : kRaggedWaveMaxVpt<ADD>)) return 1;
     const dim3 grid((uint32_t)a.rows), block(64);
-    switch (a.d / kRow) {
+    if (!exact) {
+        switch (vpt) {
+            case 1: return launch(row_norm_wave_kernel<T, 1, ADD, true>, grid, block, stream, a);
+            case 2: return launch(row_norm_wave_kernel<T, 2, ADD, true>, grid, block, stream, a);
+            case 3: return launch(row_norm_wave_kernel<T, 3, ADD, true>, grid, block, stream, a);
+            case 4: return launch(row_norm_wave_kernel<T, 4, ADD, true>, grid, block, stream, a);
+            default:
+                if constexpr (kRaggedWaveMaxVpt<ADD> >= 5)
+                    return launch(row_norm_wave_kernel<T, 5, ADD, true>, grid, block, stream, a);
+                return 1;
+        }
+    }
+    switch (vpt) {
         case 1: return launch(row_norm_wave_kernel<T, 1, ADD>, grid, block, stream, a);
         case 2: return launch(row_norm_wave_kernel<T, 2, ADD>, grid, block, stream, a);
         case 3: return launch(row_norm_wave_kernel<T, 3, ADD>, grid, block, stream, a);

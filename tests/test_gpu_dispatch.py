@@ -81,16 +81,17 @@ def run_norm(kcr, x0, d0, w0, add, what):
 @pytest.mark.parametrize("add", [False, True], ids=["plain", "add"])
 @pytest.mark.parametrize("dt", DTS, ids=DT_ID.get)
 def test_norm_small_call_shapes(kcr, dt, add):
-    """Small calls (the decode-size tier) at every width class, including
-    the one-wave kernel at exact multiples of 64 vectors."""
+    """Small calls (the decode-size tier) at every width class: rows of
+    whole vectors (the one-wave kernel, exact or ragged, where it applies)
+    and rows whose last vector is cut short (the rule's shapes)."""
     rng = np.random.default_rng(21000 + 2 * DTS.index(dt) + add)
     vec = vec_of(dt)
     g = workloads.gen(21100 + 2 * DTS.index(dt) + add)
     for nvec in NVEC:
-        widths = [norm_width(nvec, vec, rng, even=dt.itemsize == 2)]
-        if nvec % 64 == 0:   # also a ragged last vector: the rule's shape, not the one-wave kernel
-            widths.append(nvec * vec - (2 if dt.itemsize == 2 else 1))
-        for d in widths:
+        # whole vectors (one-wave kernels up to their limits) and a last
+        # vector cut short (the rule's shapes with their element tail)
+        short = int(rng.integers(1, vec // 2)) * 2 if dt.itemsize == 2 else int(rng.integers(1, vec))
+        for d in (nvec * vec, nvec * vec - short):
             rows = int(rng.integers(1, 6))
             say(f"small-call norm dt={DT_ID[dt]} add={add} d={d} ({nvec} vectors) rows={rows}")
             x0 = (workloads.randn([rows, d], g) * 3).to(dt)
