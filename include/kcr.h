@@ -334,10 +334,11 @@ int kcr_paged_kv_gather(const void* kv_cache, int64_t num_blocks, int block_size
  *
  * Each op is the one defined above (the koas-w.github.io 2026-03-31 post,
  * sections 1, 2 and 4) and its results are those of the separate calls made
- * in this order. One workgroup runs every op of every layer in turn with
- * workgroup barriers only, keeping the residual h in registers; the
- * launch-overhead elimination (one launch instead of four per layer) that
- * m.lsln.cn/news/61269 section 4 seeks with CUDA Graph. Batch 1 only: the
+ * in this order: the launch-overhead elimination (one launch instead of four
+ * per layer) that m.lsln.cn/news/61269 section 4 seeks with CUDA Graph. Only
+ * the residual passes from op to op, so inside the launch one workgroup runs
+ * the token's residual chain (h in registers) while other workgroups run
+ * every layer's RoPE + store and SwiGLU at the same time. Batch 1 only: the
  * ops' GEMMs and attention (not part of this library) are not in between.
  *
  *   layers [n_layers]  HOST array of per-layer device pointers (read during
@@ -385,12 +386,12 @@ int kcr_decode_chain_b1(const kcr_chain_layer* layers, int n_layers, void* h, in
  * kcr_decode_chain_batch -- the same chain for `batch` tokens in one launch:
  * kcr_decode_chain_b1 is this call with batch = 1. Every op of the chain is
  * row-wise, so token b's outputs depend on token b's inputs alone (and on
- * the shared weights and tables); one workgroup per token runs the whole
- * chain, and the tokens' workgroups never wait for one another. The results
- * are those of the separate calls, each over the whole batch, in the order
- * above.
+ * the shared weights and tables); one workgroup per token runs its residual
+ * chain, other workgroups its RoPE + stores and every (layer, token) SwiGLU,
+ * and no workgroup waits for another. The results are those of the
+ * separate calls, each over the whole batch, in the order above.
  *
- *   batch        0 <= batch < 2^22 tokens (0: nothing is launched)
+ *   batch        0 <= batch < 2^20 tokens (0: nothing is launched)
  *   layers       as for kcr_decode_chain_b1, each per-token tensor with
  *        `batch` contiguous rows (token b's row at b times the row width):
  *        d_attn, y_attn, d_mlp, y_mlp [batch, hidden];
@@ -403,8 +404,8 @@ int kcr_decode_chain_b1(const kcr_chain_layer* layers, int n_layers, void* h, in
  *        unspecified (as for kcr_rope_kvstore).
  *
  * For both entry points, a buffer that one layer writes may not overlap any
- * buffer of another layer, since each layer's inputs are read ahead of the
- * previous layer's ops (KCR_ERR_ALIAS, checked before anything is launched).
+ * buffer of another layer, since the layers' ops run concurrently
+ * (KCR_ERR_ALIAS, checked before anything is launched).
  * Inputs may be shared between layers (e.g. one weight), and so may a
  * cache when the layers name exactly the same cache range: the chain never
  * reads the cache, and the last layer's K/V rows land there, as with the

@@ -5,33 +5,31 @@
 // add + RMSNorm, SwiGLU (section 2).
 //
 // gfx950 design
-//  * One workgroup per token (512 lanes where the token's row, RoPE units
-//    and SwiGLU vectors fit, else 1024) runs every op of every layer in
-//    turn; ops are separated by workgroup barriers only, so the 4 launches
-//    per layer of the separate entry points (and their graph-node or host
-//    launch cost) become one launch per step. Every op of the chain is
-//    row-wise (a token's outputs depend on that token's inputs alone), so
-//    the tokens' workgroups never wait for one another: no device-wide
-//    barrier is needed at any batch size. A batch of 256 fills the 256 CUs
-//    with one workgroup each.
-//  * The residual h lives in registers for the whole step: lane l owns
-//    16-byte vector l of the row, adds delta to it, stores the rounded sum
-//    (the in-place update of each add) and normalises it. The row's sum of
-//    squares is reduced in-wave with DPP, then across the waves through
-//    two alternating LDS slot arrays (one barrier per norm).
-//  * Loads are software-pipelined by half layers. The MLP half's inputs
-//    (delta, weight, the gate/up vectors) are issued together before the
-//    layer's first op; the attention half's (delta, weight, the token's
-//    q/k/v chunks) one layer ahead, as soon as the previous layer's RoPE has
-//    consumed its own. Each half's loads are therefore in flight while the
-//    other half computes, in the registers the layer already holds. The
-//    cos/sin rows of the token's position are the same for every layer and
-//    are read once.
-//  * The per-layer pointer table travels in the argument block; it is read
-//    into the scalar cache at kernel start, so no layer's start waits on a
-//    scalar-cache miss for its pointers.
-//  * RoPE lane mapping as in rope_kvstore.hip: a unit of LPU lanes per
-//    virtual head in KV-group order, lane c owning chunk c of both halves.
+//  * Only the residual carries a dependency from op to op: each add reads
+//    the h the previous one wrote. RoPE and SwiGLU read only the layer's own
+//    inputs, which nothing in the chain writes. So one launch holds three
+//    kinds of 256-lane workgroup, chosen by workgroup index: one per token
+//    runs the token's residual chain (2 add+norms per layer, h in registers,
+//    the next layers' deltas and weights in flight); per token, workgroups
+//    of query heads and of key/value heads run every layer's RoPE and store
+//    in layer order; and one per (layer, token, 256 vectors) runs a SwiGLU
+//    chunk. The step's time is then that of the residual chain at small
+//    batches and that of the stream of bytes at large ones, instead of the
+//    sum of every op of every layer on one workgroup per token.
+//  * Workgroups never wait for one another, and only the residual
+//    workgroups use barriers (one per norm, for the row's sum of squares
+//    across their 4 waves).
+//  * Each role's layer loop is software-pipelined: the inputs of the next
+//    PD (residual) or PDR (RoPE) layers are loaded before the current layer
+//    computes, in a ring of register sets; a scheduling barrier between
+//    layers keeps each layer's arithmetic waiting on its own inputs only.
+//    Batches up to 64 tokens take deeper rings (the residual chain's
+//    latency bounds the step); larger batches shallower ones, since the
+//    kernel's register count sets how many SwiGLU waves a CU holds.
+//  * The per-layer pointer table travels in the argument block; the
+//    looping roles read it into the scalar cache at their start.
+//  * RoPE lane mapping as in rope_kvstore.hip: LPU lanes per head, lane c
+//    owning chunk c of both halves.
 #include <algorithm>
 
 #include "kcr_device.h"
@@ -39,14 +37,25 @@
 
 namespace kcr {
 
-// Lanes per token: 1024 at most (the shape limits below), 512 where the
-// row, the RoPE units and the SwiGLU fit (fewer waves per barrier; measured
-// faster at every batch).
-constexpr int kChainThreads = 1024;
-constexpr int kChainSmallThreads = 512;
-constexpr int kChainMaxSwigluIters = 4;  // inter <= 4096 vectors at 1024 lanes
-// Tokens per launch: batch * 1024 lanes must stay below 2^32.
-constexpr int64_t kChainMaxBatch = (int64_t(1) << 22) - 1;
+// Shape limits of the entry points (vectors of 16 bytes): hidden <= 1024,
+// inter <= 4096, and the token's virtual heads (query, key and value heads,
+// each head_dim/2 elements wide in units of LPU lanes) <= 1024 lanes.
+constexpr int kChainMaxHiddenVec = 1024;
+constexpr int kChainMaxInterVec = 4096;
+constexpr int kChainMaxRopeLanes = 1024;
+// Lanes per workgroup, for every role.
+constexpr int kFlowThreads = 256;
+// The residual role holds ceil(hidden vectors / 256) vectors per lane.
+constexpr int kFlowMaxHpl = kChainMaxHiddenVec / kFlowThreads;
+// Batches up to this size take the deeply prefetched form (the residual
+// chain's latency bounds the step); larger ones the lean form (the SwiGLU
+// stream's occupancy does).
+constexpr int64_t kFlowDeepMaxBatch = 64;
+// SwiGLU workgroups in one grid; beyond this many chunks each loops.
+constexpr int64_t kFlowMaxSwigluGroups = int64_t(1) << 22;
+// Tokens per launch: the grid (batch * (1 + query and key/value groups)
+// plus the SwiGLU groups) times 256 lanes stays below 2^32.
+constexpr int64_t kChainMaxBatch = (int64_t(1) << 20) - 1;
 
 struct ChainArgs {
     kcr_chain_layer layers[KCR_B1_MAX_LAYERS];
@@ -59,6 +68,10 @@ struct ChainArgs {
     int32_t n_layers, hidden, inter, hq, hkv, dh, group, lpu;
     int64_t qkv_w;  // (hq + 2 hkv) * dh
     float eps;
+    // grid layout: [0, batch) residual groups, then batch * (n_rq + n_rkv)
+    // RoPE groups, then s_groups SwiGLU groups covering s_total chunks
+    int64_t batch, s_total, s_groups;
+    int32_t n_rq, n_rkv, n_s;
 };
 
 // The argument-block warm-up in the kernel relies on this entry layout.
@@ -81,218 +94,302 @@ __device__ __forceinline__ float block_sum(float v, float (*part)[WAVES], int sl
     return t;
 }
 
-template <typename T, int SWI, int THREADS>
-__global__ __launch_bounds__(THREADS) void decode_chain_kernel(const ChainArgs a) {
+// The layer table sits in the kernel's argument block and each layer's
+// pointers are first read at that layer's start, where a scalar-cache miss
+// stalls the wave. Bring the whole table into the scalar cache: the fields
+// read here (bytes 0, 40 and 80 of each 88-byte, 8-byte-aligned entry) leave
+// no gap of 64 bytes, so every 64-byte line of the table holds one of them.
+// The block always holds KCR_B1_MAX_LAYERS entries (unused ones zero), so
+// every read is in bounds.
+__device__ __forceinline__ void warm_layer_table(const ChainArgs& a) {
+    uintptr_t acc = 0;
+#pragma unroll
+    for (int l = 0; l < KCR_B1_MAX_LAYERS; ++l) {
+        const kcr_chain_layer& E = a.layers[l];
+        acc |= reinterpret_cast<uintptr_t>(E.d_attn) | reinterpret_cast<uintptr_t>(E.kv_cache) |
+               reinterpret_cast<uintptr_t>(E.act);
+    }
+    asm volatile("" ::"s"(acc));
+}
+
+// Ends one layer of a role's software pipeline: no memory access moves
+// across (the compiler barrier) and no instruction at all (the scheduling
+// barrier), so each layer's arithmetic waits only for its own inputs, which
+// were loaded PD layers earlier.
+__device__ __forceinline__ void layer_fence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// The chain in one launch as three kinds of workgroup, picked by the
+// workgroup index. Only the residual depends on the previous op; RoPE and
+// SwiGLU read nothing the chain writes. So the residual chain (the step's
+// one dependency chain) runs in one workgroup per token, and every layer's
+// RoPE and SwiGLU run beside it, all at once.
+//  * Residual (one per token): h in registers for the whole step, lane l
+//    owning vectors l, l + 256, ...; per layer the two add+norms, storing
+//    y_attn and y_mlp; h itself is stored once, at the end (a caller sees
+//    only the final residual: every buffer that could observe an earlier
+//    one is refused as an overlap). The inputs of the next PD layers are in
+//    flight at all times.
+//  * RoPE (per token, n_rq groups of query heads, then n_rkv of key and
+//    value heads): every layer in order, the next PDR layers' q/k/v chunks
+//    in flight. A token's cache rows are written by the same lanes layer
+//    after layer, so with layers that share a cache the last layer's rows
+//    remain.
+//  * SwiGLU (per layer, token and chunk of 256 vectors).
+template <typename T, int HPL, bool DEEP>
+__global__ __launch_bounds__(kFlowThreads) void decode_chain_kernel(const ChainArgs a) {
     using S = typename T::storage;
     constexpr int kVec = T::kVec;
-    constexpr int kWaves = THREADS / 64;
+    constexpr int kWaves = kFlowThreads / 64;
+    // layers in flight: the residual's inputs take 16 VGPRs per layer and
+    // vector per lane, so PD * HPL stays at 4 (deep) or 2
+    constexpr int PD = (DEEP ? 4 : 2) / HPL > 1 ? (DEEP ? 4 : 2) / HPL : 1;
+    constexpr int PDR = DEEP ? 4 : 2;
     __shared__ float part[2][kWaves];
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-    // This workgroup's token and its row offsets (uniform).
-    const int64_t tok = blockIdx.x;
-    const int64_t hrow = tok * a.hidden;
+    const int n = a.n_layers;
+    const int64_t bid = blockIdx.x;
+    const int64_t nR = a.batch * (a.n_rq + a.n_rkv);
 
-    // residual: lane tid owns vector tid of the token's row of h
-    const int hv = a.hidden / kVec;
-    const bool own_h = tid < hv;
-    const int64_t he = (int64_t)tid * kVec;
-    const int64_t he_c = own_h ? he : 0;  // in-bounds load address for every lane
-    S* const h = static_cast<S*>(a.h) + hrow;
-    u32x4 hreg = ld16<T>(h, he_c);
-
-    // RoPE: unit = virtual head (KV-group order), lane c = chunk c of both halves
-    const int half = a.dh >> 1;
-    const int unit = tid / a.lpu, c = tid % a.lpu;
-    const int nvh = a.hkv * (a.group + 2);
-    const bool rope_on = unit < nvh && c * kVec < half;
-    const int g = rope_on ? unit / (a.group + 2) : 0;
-    const int r = rope_on ? unit - g * (a.group + 2) : 0;
-    const int kind = r < a.group ? 0 : (r == a.group ? 1 : 2);  // query, K, V
-    const int src_head = kind == 0 ? g * a.group + r : (kind == 1 ? a.hq + g : a.hq + a.hkv + g);
-    const int64_t c0 = rope_on ? (int64_t)c * kVec : 0;
-    const int64_t p = a.pos[tok];
-    const int64_t slot = a.slots[tok];
-    const bool p_ok = p >= 0 && p < a.max_pos;
-    const bool store_kv = p_ok && slot >= 0 && slot < a.n_slots;
-    float cs[kVec], sn[kVec];
-    if (rope_on) {
-        const float* cr = a.cos_t + (p_ok ? p : 0) * half + c0;
-        const float* sr = a.sin_t + (p_ok ? p : 0) * half + c0;
+    if (bid < a.batch) {
+        // ------------------------------------------------------ residual
+        const int64_t hrow = bid * a.hidden;
+        const int hv = a.hidden / kVec;
+        S* const h = static_cast<S*>(a.h) + hrow;
+        bool own[HPL], won[HPL];
+        int64_t ec[HPL];  // in-bounds element offset for every lane
+        float hf[HPL][kVec];  // the residual, each value exactly its stored rounding
 #pragma unroll
-        for (int i = 0; i < kVec; i += 4) {
-            const u32x4 cv = *reinterpret_cast<const u32x4*>(cr + i);
-            const u32x4 sv = *reinterpret_cast<const u32x4*>(sr + i);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                cs[i + e] = __uint_as_float(cv[e]);
-                sn[i + e] = __uint_as_float(sv[e]);
-            }
+        for (int k = 0; k < HPL; ++k) {
+            const int v = tid + k * kFlowThreads;
+            own[k] = v < hv;
+            ec[k] = own[k] ? (int64_t)v * kVec : 0;
+            unpack<T>(ld16<T>(h, ec[k]), hf[k]);
+            // whether this wave owns any of slot k (uniform: a scalar branch)
+            won[k] = __builtin_amdgcn_readfirstlane((int)(wave * 64 + k * kFlowThreads < hv)) != 0;
         }
-    }
-    const int iv = a.inter / kVec;
-
-    // The attention half's inputs of layer l (delta, weight, the token's
-    // q/k/v chunks). They are loaded one layer ahead: layer l + 1's are
-    // issued once layer l's RoPE has consumed its own, so they are in flight
-    // during layer l's MLP half. Every load is unconditional: lanes with
-    // nothing to load read an in-bounds clamped address and ignore the
-    // result. In straight-line code the compiler waits for exactly the loads
-    // each op needs; loads under lane-dependent branches made it wait for all
-    // of them, and for earlier stores, before every op.
-    u32x4 dA, wA, x1, x2;
-    auto load_attn = [&](int l) {
-        const kcr_chain_layer& L = a.layers[l];
-        dA = ld16_nt<T>(static_cast<const S*>(L.d_attn) + hrow, he_c);
-        wA = ld16<T>(L.w_attn, he_c);
-        const S* src = static_cast<const S*>(L.qkv) + tok * a.qkv_w + (int64_t)src_head * a.dh;
-        x1 = ld16_nt<T>(src, c0);
-        x2 = ld16_nt<T>(src, half + c0);
-    };
-    load_attn(0);
-    // The layer table sits in the kernel's argument block and each layer's
-    // pointers are first read at that layer's start, where a scalar-cache
-    // miss stalls every wave. Bring the whole table into the scalar cache
-    // now, behind the first layer's loads: the fields read here (bytes 0,
-    // 40 and 80 of each 88-byte, 8-byte-aligned entry) leave no gap of 64
-    // bytes, so every 64-byte line of the table holds one of them. The
-    // block always holds KCR_B1_MAX_LAYERS entries (unused ones zero), so
-    // every read is in bounds.
-    {
-        uintptr_t acc = 0;
+        struct Set {
+            u32x4 dA[HPL], wA[HPL], dM[HPL], wM[HPL];
+        };
+        Set s[PD];
+        auto load = [&](Set& st, int l) {
+            const kcr_chain_layer& L = a.layers[l];
 #pragma unroll
-        for (int l = 0; l < KCR_B1_MAX_LAYERS; ++l) {
-            const kcr_chain_layer& E = a.layers[l];
-            acc |= reinterpret_cast<uintptr_t>(E.d_attn) | reinterpret_cast<uintptr_t>(E.kv_cache) |
-                   reinterpret_cast<uintptr_t>(E.act);
-        }
-        asm volatile("" ::"s"(acc));
-    }
-
-    for (int l = 0; l < a.n_layers; ++l) {
-        const kcr_chain_layer& L = a.layers[l];
-        // The token's rows of the layer's per-token tensors (uniform).
-        const S* const d_mlp = static_cast<const S*>(L.d_mlp) + hrow;
-        const S* const gate_up = static_cast<const S*>(L.gate_up) + tok * 2 * (int64_t)a.inter;
-        // The MLP half's inputs, issued together before the layer's first op.
-        const u32x4 dM = ld16_nt<T>(d_mlp, he_c);
-        const u32x4 wM = ld16<T>(L.w_mlp, he_c);
-        u32x4 gr[SWI], ur[SWI];
-#pragma unroll
-        for (int k = 0; k < SWI; ++k) {
-            const int v = tid + k * THREADS;
-            const int64_t e = v < iv ? (int64_t)v * kVec : 0;
-            gr[k] = ld16_nt<T>(gate_up, e);
-            ur[k] = ld16_nt<T>(gate_up, (int64_t)a.inter + e);
-        }
-        // The layer's output pointers, read while the loads are in flight
-        // (uniform; a per-lane choice between two fields of the argument
-        // block would be a vector load that every later wait must cover).
-        S* const q_out = static_cast<S*>(L.q_out) + tok * (int64_t)a.hq * a.dh;
-        S* const kv_cache = static_cast<S*>(L.kv_cache);
-        S* const y_attn = static_cast<S*>(L.y_attn) + hrow;
-        S* const y_mlp = static_cast<S*>(L.y_mlp) + hrow;
-        S* const act = static_cast<S*>(L.act) + tok * (int64_t)a.inter;
-        // Compiler-only barrier: keeps every load above issued here, ahead of
-        // the lane-dependent branches that use them (the compiler otherwise
-        // sinks a load into its only user and then waits for all loads).
-        asm volatile("" ::: "memory");
-
-        // 1. h <- round(h + d_attn); y_attn = rmsnorm(h) * w_attn
-        for (int n = 0; n < 2; ++n) {
-            const u32x4 dv = n == 0 ? dA : dM;
-            const u32x4 wv = n == 0 ? wA : wM;
-            float ss = 0.0f;
-            float xf[kVec];
-            if (own_h) {
-                float df[kVec];
-                unpack<T>(hreg, xf);
-                unpack<T>(dv, df);
-#pragma unroll
-                for (int e = 0; e < kVec; ++e) xf[e] += df[e];
-                hreg = pack<T>(xf);
-                st16_nt<T>(h, he, hreg);
-                unpack<T>(hreg, xf);  // the rounded sum is what the norm sees
-#pragma unroll
-                for (int e = 0; e < kVec; ++e) ss += xf[e] * xf[e];
+            for (int k = 0; k < HPL; ++k) {
+                st.dA[k] = ld16_nt<T>(static_cast<const S*>(L.d_attn) + hrow, ec[k]);
+                st.wA[k] = ld16<T>(L.w_attn, ec[k]);
+                st.dM[k] = ld16_nt<T>(static_cast<const S*>(L.d_mlp) + hrow, ec[k]);
+                st.wM[k] = ld16<T>(L.w_mlp, ec[k]);
             }
-            const float tot = block_sum<kWaves>(ss, part, n, wave, lane);
-            if (own_h) {
-                const float rs = __builtin_amdgcn_rsqf(tot / (float)a.hidden + a.eps);
-                float wf[kVec], yf[kVec];
-                unpack<T>(wv, wf);
+        };
 #pragma unroll
-                for (int e = 0; e < kVec; ++e) yf[e] = xf[e] * rs * wf[e];
-                st16_nt<T>(n == 0 ? y_attn : y_mlp, he, pack<T>(yf));
-            }
-            if (n == 1) break;
-
-            // 2. RoPE of the token's query and key heads, K_rot and V to the cache
-            if (rope_on && (kind == 0 || store_kv)) {
-                u32x4 o1 = x1, o2 = x2;
-                if (kind < 2 && p_ok) {
-                    float f1[kVec], f2[kVec], r1[kVec], r2[kVec];
-                    unpack<T>(x1, f1);
-                    unpack<T>(x2, f2);
+        for (int j = 0; j < PD; ++j) load(s[j], j < n ? j : n - 1);
+        warm_layer_table(a);
+        layer_fence();
+        auto layer = [&](Set& st, int l) {
+            const kcr_chain_layer& L = a.layers[l];
 #pragma unroll
-                    for (int e = 0; e < kVec; ++e) {
-                        r1[e] = f1[e] * cs[e] - f2[e] * sn[e];
-                        r2[e] = f2[e] * cs[e] + f1[e] * sn[e];
+            for (int nn = 0; nn < 2; ++nn) {
+                // h <- round(h + delta); y = rmsnorm(h) * w
+                S* const y = static_cast<S*>(nn == 0 ? L.y_attn : L.y_mlp) + hrow;
+                float ss = 0.0f;
+#pragma unroll
+                for (int k = 0; k < HPL; ++k) {
+                    if (won[k]) {
+                        float df[kVec];
+                        unpack<T>(nn == 0 ? st.dA[k] : st.dM[k], df);
+#pragma unroll
+                        for (int e = 0; e < kVec; ++e) hf[k][e] += df[e];
+                        unpack<T>(pack<T>(hf[k]), hf[k]);  // the rounded sum is what the norm sees
+                        float sk = 0.0f;
+#pragma unroll
+                        for (int e = 0; e < kVec; ++e) sk = __builtin_fmaf(hf[k][e], hf[k][e], sk);
+                        ss += own[k] ? sk : 0.0f;
                     }
-                    o1 = pack<T>(r1);
-                    o2 = pack<T>(r2);
                 }
-                S* dst = kind == 0
-                             ? q_out + (int64_t)src_head * a.dh
-                             : kv_cache + (((int64_t)(kind - 1) * a.n_slots + slot) * a.hkv + g) * (int64_t)a.dh;
-                st16_nt<T>(dst, c0, o1);
-                st16_nt<T>(dst, half + c0, o2);
+                const float tot = block_sum<kWaves>(ss, part, nn, wave, lane);
+                const float rs = __builtin_amdgcn_rsqf(tot / (float)a.hidden + a.eps);
+#pragma unroll
+                for (int k = 0; k < HPL; ++k) {
+                    if (won[k]) {
+                        float wf[kVec], yf[kVec];
+                        unpack<T>(nn == 0 ? st.wA[k] : st.wM[k], wf);
+#pragma unroll
+                        for (int e = 0; e < kVec; ++e) yf[e] = hf[k][e] * rs * wf[e];
+                        const u32x4 yv = pack<T>(yf);
+                        if (own[k]) st16_nt<T>(y, ec[k], yv);
+                    }
+                }
             }
-            // The next layer's attention-half inputs (the last layer reads its
-            // own again and ignores them).
-            load_attn(l + 1 < a.n_layers ? l + 1 : l);
-            asm volatile("" ::: "memory");
+        };
+        // whole groups of PD layers, then the rest (each set already holds
+        // its layer)
+        int l = 0;
+        for (; l + PD <= n; l += PD) {
+#pragma unroll
+            for (int j = 0; j < PD; ++j) {
+                layer(s[j], l + j);
+                load(s[j], l + j + PD < n ? l + j + PD : n - 1);
+                layer_fence();
+            }
         }
+#pragma unroll
+        for (int j = 0; j < PD - 1; ++j)
+            if (l + j < n) layer(s[j], l + j);
+#pragma unroll
+        for (int k = 0; k < HPL; ++k)
+            if (own[k]) st16_nt<T>(h, ec[k], pack<T>(hf[k]));
+        return;
+    }
 
-        // 4. act = silu(gate) * up
+    if (bid < a.batch + nR) {
+        // ------------------------------------------------------ RoPE
+        // No barriers in this role: lanes without work leave at once.
+        const int64_t r = bid - a.batch;
+        const int per_tok = a.n_rq + a.n_rkv;
+        const int64_t tok = r / per_tok;
+        const int chunk = (int)(r - tok * per_tok);
+        const bool is_q = chunk < a.n_rq;  // uniform
+        const int half = a.dh >> 1;
+        // unit = head: query heads, or key heads [0, hkv) then value heads
+        const int unit = (is_q ? chunk : chunk - a.n_rq) * (kFlowThreads / a.lpu) + tid / a.lpu;
+        const int c = tid % a.lpu;  // lane c owns chunk c of both halves
+        if (unit >= (is_q ? a.hq : 2 * a.hkv) || c * kVec >= half) return;
+        const int64_t p = a.pos[tok];
+        const int64_t slot = a.slots[tok];
+        const bool p_ok = p >= 0 && p < a.max_pos;
+        const bool store_kv = p_ok && slot >= 0 && slot < a.n_slots;
+        if (!is_q && !store_kv) return;
+        const bool is_v = !is_q && unit >= a.hkv;
+        const int g = is_v ? unit - a.hkv : unit;  // KV head of a key or value unit
+        const int src_head = is_q ? unit : a.hq + unit;
+        const int64_t c0 = (int64_t)c * kVec;
+        // query and key heads rotate at a valid position; value heads and
+        // query heads at an invalid one are copied
+        const bool rot = p_ok && !is_v;
+        const int64_t dst_off = is_q ? tok * (int64_t)a.hq * a.dh + (int64_t)unit * a.dh
+                                     : (((int64_t)(is_v ? 1 : 0) * a.n_slots + slot) * a.hkv + g) * (int64_t)a.dh;
+        float cs[kVec], sn[kVec];
+        {
+            const float* cr = a.cos_t + (p_ok ? p : 0) * half + c0;
+            const float* sr = a.sin_t + (p_ok ? p : 0) * half + c0;
 #pragma unroll
-        for (int k = 0; k < SWI; ++k) {
-            const int v = tid + k * THREADS;
-            if (v < iv) {
-                float gf[kVec], uf[kVec], of[kVec];
-                unpack<T>(gr[k], gf);
-                unpack<T>(ur[k], uf);
+            for (int i = 0; i < kVec; i += 4) {
+                const u32x4 cv = *reinterpret_cast<const u32x4*>(cr + i);
+                const u32x4 sv = *reinterpret_cast<const u32x4*>(sr + i);
 #pragma unroll
-                for (int e = 0; e < kVec; ++e) {
-                    const float ex = __builtin_amdgcn_exp2f(gf[e] * -1.4426950408889634f);
-                    of[e] = gf[e] * __builtin_amdgcn_rcpf(1.0f + ex) * uf[e];
+                for (int e = 0; e < 4; ++e) {
+                    cs[i + e] = __uint_as_float(cv[e]);
+                    sn[i + e] = __uint_as_float(sv[e]);
                 }
-                st16_nt<T>(act, (int64_t)v * kVec, pack<T>(of));
             }
+        }
+        struct Set {
+            u32x4 x1, x2;
+        };
+        Set s[PDR];
+        auto load = [&](Set& st, int l) {
+            const S* src = static_cast<const S*>(a.layers[l].qkv) + tok * a.qkv_w + (int64_t)src_head * a.dh;
+            st.x1 = ld16_nt<T>(src, c0);
+            st.x2 = ld16_nt<T>(src, half + c0);
+        };
+        // (the table rows first: the loop's first wait covers them alone)
+#pragma unroll
+        for (int j = 0; j < PDR; ++j) load(s[j], j < n ? j : n - 1);
+        warm_layer_table(a);
+        layer_fence();
+        auto layer = [&](Set& st, int l) {
+            const kcr_chain_layer& L = a.layers[l];
+            float f1[kVec], f2[kVec], r1[kVec], r2[kVec];
+            unpack<T>(st.x1, f1);
+            unpack<T>(st.x2, f2);
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) {
+                r1[e] = __builtin_fmaf(f1[e], cs[e], -(f2[e] * sn[e]));
+                r2[e] = __builtin_fmaf(f2[e], cs[e], f1[e] * sn[e]);
+            }
+            const u32x4 p1 = pack<T>(r1), p2 = pack<T>(r2);
+            u32x4 o1, o2;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                o1[i] = rot ? p1[i] : st.x1[i];
+                o2[i] = rot ? p2[i] : st.x2[i];
+            }
+            // the destination's base pointer is uniform (is_q is): a scalar load
+            S* const dst = static_cast<S*>(is_q ? L.q_out : L.kv_cache) + dst_off;
+            st16_nt<T>(dst, c0, o1);
+            st16_nt<T>(dst, half + c0, o2);
+        };
+        int l = 0;
+        for (; l + PDR <= n; l += PDR) {
+#pragma unroll
+            for (int j = 0; j < PDR; ++j) {
+                layer(s[j], l + j);
+                load(s[j], l + j + PDR < n ? l + j + PDR : n - 1);
+                layer_fence();
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < PDR - 1; ++j)
+            if (l + j < n) layer(s[j], l + j);
+        return;
+    }
+
+    // ---------------------------------------------------------- SwiGLU
+    // chunk index = (layer * batch + token) * n_s + chunk of 256 vectors
+    const int iv = a.inter / kVec;
+    for (int64_t sx = bid - a.batch - nR; sx < a.s_total; sx += a.s_groups) {
+        const int64_t row = sx / a.n_s;  // layer * batch + token
+        const int chunk = (int)(sx - row * a.n_s);
+        const int l = (int)(row / a.batch);
+        const int64_t tok = row - (int64_t)l * a.batch;
+        const kcr_chain_layer& L = a.layers[l];
+        const int v = chunk * kFlowThreads + tid;
+        const int64_t e = v < iv ? (int64_t)v * kVec : 0;
+        const S* const gate_up = static_cast<const S*>(L.gate_up) + tok * 2 * (int64_t)a.inter;
+        const u32x4 gv = ld16_nt<T>(gate_up, e);
+        const u32x4 uv = ld16_nt<T>(gate_up, (int64_t)a.inter + e);
+        if (v < iv) {
+            float gf[kVec], uf[kVec], of[kVec];
+            unpack<T>(gv, gf);
+            unpack<T>(uv, uf);
+#pragma unroll
+            for (int i = 0; i < kVec; ++i) {
+                const float ex = __builtin_amdgcn_exp2f(gf[i] * -1.4426950408889634f);
+                of[i] = gf[i] * __builtin_amdgcn_rcpf(1.0f + ex) * uf[i];
+            }
+            st16_nt<T>(static_cast<S*>(L.act) + tok * (int64_t)a.inter, (int64_t)v * kVec, pack<T>(of));
         }
     }
 }
 
-template <typename T, int THREADS>
-static int launch_chain_t(const ChainArgs& a, int64_t batch, void* stream) {
-    const int iters = (a.inter / T::kVec + THREADS - 1) / THREADS;
-    const dim3 grid((uint32_t)batch), block(THREADS);
-    switch (iters) {
-        case 1: return launch(decode_chain_kernel<T, 1, THREADS>, grid, block, stream, a);
-        case 2: return launch(decode_chain_kernel<T, 2, THREADS>, grid, block, stream, a);
-        case 3: return launch(decode_chain_kernel<T, 3, THREADS>, grid, block, stream, a);
-        default: return launch(decode_chain_kernel<T, kChainMaxSwigluIters, THREADS>, grid, block, stream, a);
+template <typename T, bool DEEP>
+static int launch_chain_t(const ChainArgs& a, int hpl, void* stream) {
+    const int64_t groups = a.batch * (1 + a.n_rq + a.n_rkv) + a.s_groups;
+    const dim3 grid((uint32_t)groups), block(kFlowThreads);
+    switch (hpl) {
+        case 1: return launch(decode_chain_kernel<T, 1, DEEP>, grid, block, stream, a);
+        case 2: return launch(decode_chain_kernel<T, 2, DEEP>, grid, block, stream, a);
+        case 3: return launch(decode_chain_kernel<T, 3, DEEP>, grid, block, stream, a);
+        default: return launch(decode_chain_kernel<T, kFlowMaxHpl, DEEP>, grid, block, stream, a);
     }
 }
 
-// 512 lanes when the token's row, its RoPE units and its SwiGLU vectors (at
-// most 4 per lane) fit, else 1024.
+// Completes the grid layout in `a` and launches.
 template <typename T>
-static int launch_chain(const ChainArgs& a, int64_t batch, void* stream) {
-    const bool small = a.hidden / T::kVec <= kChainSmallThreads &&
-                       a.hkv * (a.group + 2) * a.lpu <= kChainSmallThreads &&
-                       a.inter / T::kVec <= kChainMaxSwigluIters * kChainSmallThreads;
-    return small ? launch_chain_t<T, kChainSmallThreads>(a, batch, stream)
-                 : launch_chain_t<T, kChainThreads>(a, batch, stream);
+static int launch_chain(ChainArgs& a, void* stream) {
+    constexpr int kVec = T::kVec;
+    const int hpl = (a.hidden / kVec + kFlowThreads - 1) / kFlowThreads;
+    const int per_group = kFlowThreads / a.lpu;  // heads per RoPE workgroup
+    a.n_rq = (a.hq + per_group - 1) / per_group;
+    a.n_rkv = (2 * a.hkv + per_group - 1) / per_group;
+    a.n_s = (a.inter / kVec + kFlowThreads - 1) / kFlowThreads;
+    a.s_total = (int64_t)a.n_layers * a.batch * a.n_s;
+    a.s_groups = std::min(a.s_total, kFlowMaxSwigluGroups);
+    return a.batch <= kFlowDeepMaxBatch ? launch_chain_t<T, true>(a, hpl, stream)
+                                        : launch_chain_t<T, false>(a, hpl, stream);
 }
 
 // One per-layer buffer of a chain call: its byte range, its layer, its
@@ -347,15 +444,15 @@ extern "C" int kcr_decode_chain_batch(const kcr_chain_layer* layers, int n_layer
     if (n_head % n_kv_head != 0) return KCR_ERR_HEADS;
     const size_t es = dtype_size(dtype);
     const int vec = (int)(16 / es);
-    if (hidden < 1 || hidden % vec != 0 || hidden / vec > kChainThreads) return KCR_ERR_SHAPE;
-    if (inter < 1 || inter % vec != 0 || inter / vec > kChainMaxSwigluIters * kChainThreads) return KCR_ERR_SHAPE;
+    if (hidden < 1 || hidden % vec != 0 || hidden / vec > kChainMaxHiddenVec) return KCR_ERR_SHAPE;
+    if (inter < 1 || inter % vec != 0 || inter / vec > kChainMaxInterVec) return KCR_ERR_SHAPE;
     if (head_dim < 2 || head_dim % 2 != 0 || (head_dim / 2) % vec != 0 || head_dim > KCR_ROPE_MAX_HEAD_DIM)
         return KCR_ERR_SHAPE;
     if (block_size < 1 || num_blocks < 0 || max_pos < 1) return KCR_ERR_SHAPE;
     const int group = n_head / n_kv_head;
     int lpu = 1;
     while (lpu * vec < head_dim / 2) lpu *= 2;
-    if ((int64_t)n_kv_head * (group + 2) * lpu > kChainThreads) return KCR_ERR_SHAPE;
+    if ((int64_t)n_kv_head * (group + 2) * lpu > kChainMaxRopeLanes) return KCR_ERR_SHAPE;
     if (n_layers == 0 || batch == 0) return KCR_OK;
     if (!layers || !h || !positions || !slot_mapping || !cos_tab || !sin_tab) return KCR_ERR_NULL;
     if (!aligned16(h) || !aligned16(cos_tab) || !aligned16(sin_tab) ||
@@ -425,7 +522,8 @@ extern "C" int kcr_decode_chain_batch(const kcr_chain_layer* layers, int n_layer
     a.lpu = lpu;
     a.eps = eps;
     a.qkv_w = qkv_elems;
-    return by_dtype(dtype, [&](auto t) { return launch_chain<decltype(t)>(a, batch, stream); });
+    a.batch = batch;
+    return by_dtype(dtype, [&](auto t) { return launch_chain<decltype(t)>(a, stream); });
 }
 
 extern "C" int kcr_decode_chain_b1(const kcr_chain_layer* layers, int n_layers, void* h, int hidden,

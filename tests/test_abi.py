@@ -360,7 +360,8 @@ def test_decode_chain_batch_validation(lib):
     assert call(4) == DEVICE
     assert call(1) == DEVICE
     assert call(-1) == SHAPE
-    assert call(1 << 22) == SHAPE                     # batch * 1024 lanes past 2^32
+    assert call(1 << 20) == SHAPE                     # the grid's lanes would pass 2^32
+    assert call(1 << 22) == SHAPE
     assert call(0, h=None) == OK                      # no tokens, no work
     assert call(4, hidden=1537) == SHAPE
     bad = table(2)

@@ -326,18 +326,29 @@ def test_gated_launch_forms(kcr, dt, relu):
 # ------------------------------------------------------ one-launch chain
 @pytest.mark.parametrize("dt", DTS, ids=DT_ID.get)
 def test_chain_launch_forms(kcr, dt):
-    """The one-launch chain with 512-lane workgroups (row of at most 512
-    vectors) and 1024-lane ones (wider rows), each at 1 to 4 SwiGLU vectors
-    per lane."""
+    """The one-launch chain's kernel forms: the residual rows at 1 to 4
+    vectors per lane (200, 300, 700 and 1000-1024 vectors), each in the
+    deeply pipelined form (batches up to 64) and the lean one (larger
+    batches), with layer counts below, at and past a whole number of
+    pipeline groups; RoPE over two workgroups of query heads, and over two of
+    key/value heads."""
     from kv_cache_rmsnorm_amd.chain import DecodeChain
     from test_gpu_configs import check_chain
     vec = vec_of(dt)
-    forms = [(256, n) for n in (300, 800, 1300, 1900)] + [(600, n) for n in (600, 1500, 2500, 3500)]
-    for i, (hv, iv) in enumerate(forms):
+    # (row vectors, SwiGLU vectors, layers, batch, query heads, KV heads, head_dim)
+    forms = [(200, 300, 5, 3, 4, 2, 64), (300, 700, 2, 3, 4, 2, 64), (700, 1000, 5, 3, 4, 2, 64),
+             (1024, 1500, 3, 3, 4, 2, 64),
+             (200, 300, 3, 65, 80, 4, 64), (300, 700, 3, 65, 4, 2, 64), (700, 1000, 3, 65, 4, 2, 64),
+             (1000, 257, 2, 65, 4, 2, 64)]
+    # key/value heads over two workgroups (LPU lanes per head, 256 lanes each)
+    kv = 16 if vec == 8 else 8
+    forms.append((64, 256, 3, 2, kv, kv, 256))
+    for i, (hv, iv, layers, batch, hq, hkv, dh) in enumerate(forms):
         hidden, inter = hv * vec, iv * vec
-        say(f"chain dt={DT_ID[dt]} hidden={hidden} inter={inter}")
-        wl = workloads.decode_chain(layers=2, batch=5, ctx=20, dtype=dt, seed=28000 + 10 * i + DTS.index(dt),
-                                    hidden=hidden, inter=inter, hq=4, hkv=2, dh=64, block_size=16)
+        say(f"chain dt={DT_ID[dt]} hidden={hidden} inter={inter} layers={layers} batch={batch} heads={hq}/{hkv}x{dh}")
+        wl = workloads.decode_chain(layers=layers, batch=batch, ctx=20, dtype=dt,
+                                    seed=28000 + 10 * i + DTS.index(dt), hidden=hidden, inter=inter,
+                                    hq=hq, hkv=hkv, dh=dh, block_size=16)
         chain = DecodeChain(wl, "cuda", sentinel_cache=True)
         chain.step_one_launch()
         torch.cuda.synchronize()
