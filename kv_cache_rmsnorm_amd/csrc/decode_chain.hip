@@ -17,8 +17,9 @@
 //    batches and that of the stream of bytes at large ones, instead of the
 //    sum of every op of every layer on one workgroup per token.
 //  * Workgroups never wait for one another, and only the residual
-//    workgroups use barriers (one per norm, for the row's sum of squares
-//    across their 4 waves).
+//    workgroups use barriers: one per layer, for the sums of squares of the
+//    layer's two rows across their 4 waves (the second add needs only the
+//    first add's h, not its norm, so both adds come first).
 //  * Each role's layer loop is software-pipelined: the inputs of the next
 //    PD (residual) or PDR (RoPE) layers are loaded before the current layer
 //    computes, in a ring of register sets; a scheduling barrier between
@@ -79,21 +80,6 @@ static_assert(sizeof(kcr_chain_layer) == 88 && offsetof(kcr_chain_layer, kv_cach
                   offsetof(kcr_chain_layer, act) == 80,
               "kcr_chain_layer: 11 pointers");
 
-// Sum over the workgroup's lanes, every lane gets the result. `slot`
-// alternates between the two norms of a layer: a lane rewrites slot s only
-// after passing the barrier of the other slot, which every lane reaches
-// after its last read of slot s.
-template <int WAVES>
-__device__ __forceinline__ float block_sum(float v, float (*part)[WAVES], int slot, int wave, int lane) {
-    v = wave_sum(v);
-    if (lane == 0) part[slot][wave] = v;
-    __syncthreads();
-    float t = 0.0f;
-#pragma unroll
-    for (int i = 0; i < WAVES; ++i) t += part[slot][i];
-    return t;
-}
-
 // The layer table sits in the kernel's argument block and each layer's
 // pointers are first read at that layer's start, where a scalar-cache miss
 // stalls the wave. Bring the whole table into the scalar cache: the fields
@@ -147,7 +133,7 @@ __global__ __launch_bounds__(kFlowThreads) void decode_chain_kernel(const ChainA
     // vector per lane, so PD * HPL stays at 4 (deep) or 2
     constexpr int PD = (DEEP ? 4 : 2) / HPL > 1 ? (DEEP ? 4 : 2) / HPL : 1;
     constexpr int PDR = DEEP ? 4 : 2;
-    __shared__ float part[2][kWaves];
+    __shared__ float2 part[2][kWaves];  // per wave: the sums of squares of a layer's two rows
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int n = a.n_layers;
     const int64_t bid = blockIdx.x;
@@ -188,13 +174,19 @@ __global__ __launch_bounds__(kFlowThreads) void decode_chain_kernel(const ChainA
         for (int j = 0; j < PD; ++j) load(s[j], j < n ? j : n - 1);
         warm_layer_table(a);
         layer_fence();
+        // One layer: h <- round(h + d_attn), y_attn = rmsnorm(h) * w_attn,
+        // h <- round(h + d_mlp), y_mlp = rmsnorm(h) * w_mlp. The second add
+        // needs only the first add's h, not its norm, so both adds come
+        // first and the two rows' sums of squares cross the waves in one
+        // exchange (one barrier per layer, two alternating slots).
         auto layer = [&](Set& st, int l) {
             const kcr_chain_layer& L = a.layers[l];
+            S* const y_attn = static_cast<S*>(L.y_attn) + hrow;
+            S* const y_mlp = static_cast<S*>(L.y_mlp) + hrow;
+            u32x4 xr[2][HPL];  // the rounded sums, packed
+            float ss[2] = {0.0f, 0.0f};
 #pragma unroll
             for (int nn = 0; nn < 2; ++nn) {
-                // h <- round(h + delta); y = rmsnorm(h) * w
-                S* const y = static_cast<S*>(nn == 0 ? L.y_attn : L.y_mlp) + hrow;
-                float ss = 0.0f;
 #pragma unroll
                 for (int k = 0; k < HPL; ++k) {
                     if (won[k]) {
@@ -202,24 +194,41 @@ __global__ __launch_bounds__(kFlowThreads) void decode_chain_kernel(const ChainA
                         unpack<T>(nn == 0 ? st.dA[k] : st.dM[k], df);
 #pragma unroll
                         for (int e = 0; e < kVec; ++e) hf[k][e] += df[e];
-                        unpack<T>(pack<T>(hf[k]), hf[k]);  // the rounded sum is what the norm sees
+                        xr[nn][k] = pack<T>(hf[k]);
+                        unpack<T>(xr[nn][k], hf[k]);  // the rounded sum is what the norm sees
                         float sk = 0.0f;
 #pragma unroll
                         for (int e = 0; e < kVec; ++e) sk = __builtin_fmaf(hf[k][e], hf[k][e], sk);
-                        ss += own[k] ? sk : 0.0f;
+                        ss[nn] += own[k] ? sk : 0.0f;
                     }
                 }
-                const float tot = block_sum<kWaves>(ss, part, nn, wave, lane);
-                const float rs = __builtin_amdgcn_rsqf(tot / (float)a.hidden + a.eps);
+            }
+            const float w0 = wave_sum(ss[0]), w1 = wave_sum(ss[1]);
+            const int slot = l & 1;
+            if (lane == 0) part[slot][wave] = make_float2(w0, w1);
+            __syncthreads();
+            float t0 = 0.0f, t1 = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kWaves; ++i) {
+                const float2 v = part[slot][i];
+                t0 += v.x;
+                t1 += v.y;
+            }
+            const float rs0 = __builtin_amdgcn_rsqf(t0 / (float)a.hidden + a.eps);
+            const float rs1 = __builtin_amdgcn_rsqf(t1 / (float)a.hidden + a.eps);
+#pragma unroll
+            for (int nn = 0; nn < 2; ++nn) {
 #pragma unroll
                 for (int k = 0; k < HPL; ++k) {
                     if (won[k]) {
-                        float wf[kVec], yf[kVec];
+                        float xf[kVec], wf[kVec], yf[kVec];
+                        unpack<T>(xr[nn][k], xf);
                         unpack<T>(nn == 0 ? st.wA[k] : st.wM[k], wf);
+                        const float rs = nn == 0 ? rs0 : rs1;
 #pragma unroll
-                        for (int e = 0; e < kVec; ++e) yf[e] = hf[k][e] * rs * wf[e];
+                        for (int e = 0; e < kVec; ++e) yf[e] = xf[e] * rs * wf[e];
                         const u32x4 yv = pack<T>(yf);
-                        if (own[k]) st16_nt<T>(y, ec[k], yv);
+                        if (own[k]) st16_nt<T>(nn == 0 ? y_attn : y_mlp, ec[k], yv);
                     }
                 }
             }
