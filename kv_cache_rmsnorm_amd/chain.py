@@ -88,8 +88,7 @@ class DecodeChain:
 
     def step_one_launch(self):
         """Any batch: the whole step's chain in one launch
-        (kcr_decode_chain_batch, one workgroup per token), same ops in the
-        same order."""
+        (kcr_decode_chain_batch), same ops with the same results."""
         if self._one is None:
             self._one = kcr.DecodeChainBatch(self.layers, self.h, self.positions, self.slot_mapping, self.cos,
                                              self.sin, self.eps, self.hq, self.hkv)

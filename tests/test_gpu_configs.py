@@ -230,6 +230,39 @@ def test_decode_chain_batch_matches_b1(kcr):
             assert torch.equal(cf[:, s].view(torch.int16), cs[:, s].view(torch.int16)), f"token {b} layer {i} cache"
 
 
+@pytest.mark.parametrize("batch", [3, 70], ids=["deep", "lean"])
+def test_decode_chain_shared_cache(kcr, batch):
+    """Layers that all name one cache range: the last layer's K/V rows
+    remain, as with the separate calls in order. The shared cache must equal,
+    bit for bit, the last layer's own cache of a run with one cache per
+    layer, every other output must match that run, and the V rows must equal
+    those the separate calls leave."""
+    from kv_cache_rmsnorm_amd.chain import DecodeChain
+    say(f"one-launch chain, 5 layers sharing one cache, batch {batch}")
+    wl = workloads.decode_chain(layers=5, batch=batch, ctx=40, seed=21 + batch, hidden=512, inter=1408,
+                                hq=8, hkv=2, dh=64, block_size=8)
+    wl["slot_mapping"][1] = -1  # a padding token stores nothing in any layer
+    per_layer = DecodeChain(wl, "cuda", sentinel_cache=True)
+    per_layer.step_one_launch()
+    shared = DecodeChain(wl, "cuda", sentinel_cache=True)
+    one = shared.layers[0]["cache"]
+    for L in shared.layers:
+        L["cache"] = one
+    shared.step_one_launch()
+    eager = DecodeChain(wl, "cuda", sentinel_cache=True)
+    for L in eager.layers:
+        L["cache"] = eager.layers[0]["cache"]
+    eager.step_eager()
+    torch.cuda.synchronize()
+    bits = lambda t: t.view(torch.int16)
+    assert torch.equal(bits(one), bits(per_layer.layers[-1]["cache"])), "shared cache"
+    assert torch.equal(bits(shared.h), bits(per_layer.h)), "residual"
+    for i, (Ls, Lp) in enumerate(zip(shared.layers, per_layer.layers)):
+        for name in ("y_attn", "q_out", "y_mlp", "act"):
+            assert torch.equal(bits(Ls[name]), bits(Lp[name])), f"layer {i} {name}"
+    assert torch.equal(bits(one[1]), bits(eager.layers[0]["cache"][1])), "V rows against the separate calls"
+
+
 def _reset_cache(chain):
     for L in chain.layers:
         L["cache"].view(torch.int16 if L["cache"].element_size() == 2 else torch.int32).fill_(-1)
