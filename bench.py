@@ -26,8 +26,9 @@ Prints ONE JSON line:
                a graph, and event-stamped durations, which include the
                stamps' own cost)
   decode_chain_b1  the 28-layer chain at batch 1: graph of 112 launches vs one launch
-  decode_chain_b256_one_launch  the timed step's chain (batch 256) as one launch,
-               one workgroup per token, beside the graph of 112 launches; its
+  decode_chain_b256_one_launch  the timed step's chain (batch 256) as one launch
+               (residual, RoPE and SwiGLU workgroups side by side), beside the
+               graph of 112 launches; its
                rate over its own algorithmic bytes (h read once per token)
                and over the counter-measured HBM traffic
   source_sha256    hash of the library's sources the line was measured with
@@ -536,8 +537,8 @@ def decode_token_latency(kcr, reps: int):
 
 def decode_chain_one_launch(kcr, chain, graph_us: float, reps: int):
     """The benchmark's step (batch 256) as one launch of
-    kcr_decode_chain_batch: one workgroup per token runs all 28 layers' ops
-    in order, on the same buffers as the graph of 112 launches. Step time
+    kcr_decode_chain_batch: all 28 layers' ops, with the same results as the
+    separate calls in order, on the same buffers as the graph of 112 launches. Step time
     from events over `reps` replays of a captured one-node graph; the
     kernel's own duration from events stamped at its start and end."""
     import torch

@@ -21,7 +21,7 @@ Ops (names as in the C ABI):
   paged_kv_gather(kv_cache, block_tables, seq_lens, max_len)
                                            K, V of each sequence, read back from the cache
   DecodeChainB1(layers, h, ...)            batch-1 decode chain of every layer in one launch
-  DecodeChainBatch(layers, h, ...)         the same chain for a batch, one workgroup per token
+  DecodeChainBatch(layers, h, ...)         the same chain for a batch of tokens in one launch
 """
 from __future__ import annotations
 

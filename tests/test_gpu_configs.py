@@ -165,8 +165,8 @@ def test_graph_replays_match_eager(kcr, batch, form):
 
 def test_decode_chain_batch_one_launch(kcr):
     """The benchmark's decode step (28 layers, batch 256) in one launch of
-    kcr_decode_chain_batch, one workgroup per token, against the oracle run
-    layer by layer."""
+    kcr_decode_chain_batch (its lean form, past 64 tokens), against the
+    oracle run layer by layer."""
     from kv_cache_rmsnorm_amd.chain import DecodeChain
     say("batch-256 decode chain, one launch")
     wl = workloads.decode_chain(seed=0)
