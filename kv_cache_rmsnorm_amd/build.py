@@ -3,13 +3,15 @@
 Every source in csrc/ is compiled by hipcc for gfx950 only, in parallel, and
 linked into kv_cache_rmsnorm_amd/libkcr.so. norm_inst.hip is compiled once
 per storage type and norm variant (six objects). Packed-fp32 instruction
-selection is switched off for the device code.
+selection is switched off for the device code. The build fails if any
+kernel uses scratch memory.
 """
 from __future__ import annotations
 
 import concurrent.futures as cf
 import glob
 import os
+import re
 import subprocess
 import sys
 
@@ -46,16 +48,37 @@ def _compile(job) -> str:
     if incremental and os.path.exists(obj) and \
             os.path.getmtime(obj) > max(os.path.getmtime(src), _headers_mtime()):
         return obj
-    cmd = [HIPCC, *CXXFLAGS, *[f"-D{k}={v}" for k, v in defines], "-c", src, "-o", obj]
+    cmd = [HIPCC, *CXXFLAGS, *[f"-D{k}={v}" for k, v in defines], "-Rpass-analysis=kernel-resource-usage",
+           "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError(f"hipcc failed on {src}")
+    remarks = [l for l in r.stderr.splitlines() if "remark:" in l]
+    bad = scratch_users(remarks)
+    if bad:
+        raise RuntimeError(f"{src}: kernels that use scratch memory (spills, or a private copy of the "
+                           f"argument block): {', '.join(bad)}")
     # hipcc's host pass does not know the packed-fp32 feature; that warning is expected.
-    noise = [l for l in r.stderr.splitlines() if l.strip() and "packed-fp32-ops" not in l]
+    noise = [l for l in r.stderr.splitlines() if "warning:" in l and "packed-fp32-ops" not in l]
     if noise:
         sys.stderr.write("\n".join(noise) + "\n")
     return obj
+
+
+def scratch_users(remarks: list[str]) -> list[str]:
+    """Kernels whose resource-usage remarks report scratch memory: every
+    kernel here keeps its state in registers and LDS, so scratch means a
+    register spill or an argument block the compiler copied to memory."""
+    bad, name = [], None
+    for line in remarks:
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) > 0 and name:
+            bad.append(name)
+    return bad
 
 
 def build(verbose: bool = True, incremental: bool = False) -> str:

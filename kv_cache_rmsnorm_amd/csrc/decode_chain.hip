@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kFlowThreads) void decode_chain_kernel(const ChainA
     // vector per lane, so PD * HPL stays at 4 (deep) or 2
     constexpr int PD = (DEEP ? 4 : 2) / HPL > 1 ? (DEEP ? 4 : 2) / HPL : 1;
     constexpr int PDR = DEEP ? 4 : 2;
-    __shared__ float2 part[2][kWaves];  // per wave: the sums of squares of a layer's two rows
+    __shared__ float4 part[2][kWaves];  // per wave: sums of squares of up to four rows
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int n = a.n_layers;
     const int64_t bid = blockIdx.x;
@@ -205,12 +205,12 @@ __global__ __launch_bounds__(kFlowThreads) void decode_chain_kernel(const ChainA
             }
             const float w0 = wave_sum(ss[0]), w1 = wave_sum(ss[1]);
             const int slot = l & 1;
-            if (lane == 0) part[slot][wave] = make_float2(w0, w1);
+            if (lane == 0) part[slot][wave] = make_float4(w0, w1, 0.0f, 0.0f);
             __syncthreads();
             float t0 = 0.0f, t1 = 0.0f;
 #pragma unroll
             for (int i = 0; i < kWaves; ++i) {
-                const float2 v = part[slot][i];
+                const float4 v = part[slot][i];
                 t0 += v.x;
                 t1 += v.y;
             }
@@ -233,20 +233,98 @@ __global__ __launch_bounds__(kFlowThreads) void decode_chain_kernel(const ChainA
                 }
             }
         };
-        // whole groups of PD layers, then the rest (each set already holds
-        // its layer)
-        int l = 0;
-        for (; l + PD <= n; l += PD) {
+        if constexpr (DEEP && HPL == 1) {
+            // Pairs of layers share one exchange (four sums per wave), and the
+            // ring holds two pairs, so a pair's inputs were loaded a whole
+            // pair earlier. One pair: layers l0 and l0 + 1 from sets base and
+            // base + 1. The last n % 4 layers go one at a time, as below (a
+            // pair with a run-time layer count made the compiler copy the
+            // whole argument block to scratch memory).
+            static_assert(PD == 4, "two pairs of layers in flight");
+            auto pair = [&](auto base_c, int l0, int slot) {
+                constexpr int base = decltype(base_c)::value;
+                u32x4 xr[2][2];  // [layer][norm]: the rounded sums, packed
+                float ss[4];
 #pragma unroll
-            for (int j = 0; j < PD; ++j) {
-                layer(s[j], l + j);
-                load(s[j], l + j + PD < n ? l + j + PD : n - 1);
+                for (int j = 0; j < 2; ++j) {
+                    ss[2 * j] = 0.0f;
+                    ss[2 * j + 1] = 0.0f;
+                    if (won[0]) {
+#pragma unroll
+                        for (int nn = 0; nn < 2; ++nn) {
+                            float df[kVec];
+                            unpack<T>(nn == 0 ? s[base + j].dA[0] : s[base + j].dM[0], df);
+#pragma unroll
+                            for (int e = 0; e < kVec; ++e) hf[0][e] += df[e];
+                            xr[j][nn] = pack<T>(hf[0]);
+                            unpack<T>(xr[j][nn], hf[0]);
+                            float sk = 0.0f;
+#pragma unroll
+                            for (int e = 0; e < kVec; ++e) sk = __builtin_fmaf(hf[0][e], hf[0][e], sk);
+                            ss[2 * j + nn] = own[0] ? sk : 0.0f;
+                        }
+                    }
+                }
+                const float4 w4 = make_float4(wave_sum(ss[0]), wave_sum(ss[1]), wave_sum(ss[2]), wave_sum(ss[3]));
+                if (lane == 0) part[slot][wave] = w4;
+                __syncthreads();
+                float t[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int i = 0; i < kWaves; ++i) {
+                    const float4 v = part[slot][i];
+                    t[0] += v.x;
+                    t[1] += v.y;
+                    t[2] += v.z;
+                    t[3] += v.w;
+                }
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    if (won[0]) {
+                        const kcr_chain_layer& L = a.layers[l0 + j];
+                        S* const y_attn = static_cast<S*>(L.y_attn) + hrow;
+                        S* const y_mlp = static_cast<S*>(L.y_mlp) + hrow;
+#pragma unroll
+                        for (int nn = 0; nn < 2; ++nn) {
+                            const float rs = __builtin_amdgcn_rsqf(t[2 * j + nn] / (float)a.hidden + a.eps);
+                            float xf[kVec], wf[kVec], yf[kVec];
+                            unpack<T>(xr[j][nn], xf);
+                            unpack<T>(nn == 0 ? s[base + j].wA[0] : s[base + j].wM[0], wf);
+#pragma unroll
+                            for (int e = 0; e < kVec; ++e) yf[e] = xf[e] * rs * wf[e];
+                            const u32x4 yv = pack<T>(yf);
+                            if (own[0]) st16_nt<T>(nn == 0 ? y_attn : y_mlp, ec[0], yv);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 2; ++j) load(s[base + j], l0 + j + PD < n ? l0 + j + PD : n - 1);
                 layer_fence();
+            };
+            int l = 0;
+            for (; l + PD <= n; l += PD) {
+                pair(std::integral_constant<int, 0>{}, l, 0);
+                pair(std::integral_constant<int, 2>{}, l + 2, 1);
             }
-        }
+            // (each exchange still alternates slots: l is even here)
 #pragma unroll
-        for (int j = 0; j < PD - 1; ++j)
-            if (l + j < n) layer(s[j], l + j);
+            for (int j = 0; j < PD - 1; ++j)
+                if (l + j < n) layer(s[j], l + j);
+        } else {
+            // whole groups of PD layers, then the rest (each set already
+            // holds its layer)
+            int l = 0;
+            for (; l + PD <= n; l += PD) {
+#pragma unroll
+                for (int j = 0; j < PD; ++j) {
+                    layer(s[j], l + j);
+                    load(s[j], l + j + PD < n ? l + j + PD : n - 1);
+                    layer_fence();
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < PD - 1; ++j)
+                if (l + j < n) layer(s[j], l + j);
+        }
 #pragma unroll
         for (int k = 0; k < HPL; ++k)
             if (own[k]) st16_nt<T>(h, ec[k], pack<T>(hf[k]));
@@ -258,8 +336,11 @@ __global__ __launch_bounds__(kFlowThreads) void decode_chain_kernel(const ChainA
         // No barriers in this role: lanes without work leave at once.
         const int64_t r = bid - a.batch;
         const int per_tok = a.n_rq + a.n_rkv;
-        const int64_t tok = r / per_tok;
-        const int chunk = (int)(r - tok * per_tok);
+        // uniform by construction; said so, so that no index into the
+        // argument block becomes a per-lane one (the block would then be
+        // copied to scratch to be indexed)
+        const int64_t tok = __builtin_amdgcn_readfirstlane((int)(r / per_tok));
+        const int chunk = __builtin_amdgcn_readfirstlane((int)(r - tok * per_tok));
         const bool is_q = chunk < a.n_rq;  // uniform
         const int half = a.dh >> 1;
         // unit = head: query heads, or key heads [0, hkv) then value heads
@@ -350,10 +431,11 @@ __global__ __launch_bounds__(kFlowThreads) void decode_chain_kernel(const ChainA
     // chunk index = (layer * batch + token) * n_s + chunk of 256 vectors
     const int iv = a.inter / kVec;
     for (int64_t sx = bid - a.batch - nR; sx < a.s_total; sx += a.s_groups) {
+        // (all uniform, and said so: see the RoPE role)
         const int64_t row = sx / a.n_s;  // layer * batch + token
-        const int chunk = (int)(sx - row * a.n_s);
-        const int l = (int)(row / a.batch);
-        const int64_t tok = row - (int64_t)l * a.batch;
+        const int chunk = __builtin_amdgcn_readfirstlane((int)(sx - row * a.n_s));
+        const int l = __builtin_amdgcn_readfirstlane((int)(row / a.batch));
+        const int64_t tok = __builtin_amdgcn_readfirstlane((int)(row - (int64_t)l * a.batch));
         const kcr_chain_layer& L = a.layers[l];
         const int v = chunk * kFlowThreads + tid;
         const int64_t e = v < iv ? (int64_t)v * kVec : 0;

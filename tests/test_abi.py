@@ -431,3 +431,23 @@ def test_decode_chain_cross_layer_alias(lib):
     assert lib.kcr_decode_chain_b1(ctypes.cast(with_(1, D_ATTN, 0, ACT), ctypes.c_void_p), 3, H, 1536, 8960,
                                    12, 2, 128, H + A, H + A + 64, H + 2 * A, H + 8 * A, 4097, 16, 64, 1e-6,
                                    BF16, None) == ALIAS
+
+
+def test_build_refuses_scratch():
+    """The build fails on any kernel that uses scratch memory (a register
+    spill, or the argument block copied to private memory). Its check reads
+    hipcc's resource-usage remarks; here, two remark excerpts in that form."""
+    import importlib.util
+    import os
+    spec = importlib.util.spec_from_file_location(
+        "kcr_build", os.path.join(os.path.dirname(__file__), "..", "kv_cache_rmsnorm_amd", "build.py"))
+    build = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(build)
+    remarks = [
+        "a.hip:9:1: remark: Function Name: _Z3fooIiEvv [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:9:1: remark:     ScratchSize [bytes/lane]: 2968 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:20:1: remark: Function Name: _Z3barv [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:20:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+    ]
+    assert build.scratch_users(remarks) == ["_Z3fooIiEvv"]
+    assert build.scratch_users(remarks[2:]) == []

@@ -330,8 +330,8 @@ def test_chain_launch_forms(kcr, dt):
     vectors per lane (200, 300, 700 and 1000-1024 vectors), each in the
     deeply pipelined form (batches up to 64) and the lean one (larger
     batches), with layer counts below, at and past a whole number of
-    pipeline groups; RoPE over two workgroups of query heads, and over two of
-    key/value heads."""
+    pipeline groups (1 to 9 layers where the deep form pairs them); RoPE
+    over two workgroups of query heads, and over two of key/value heads."""
     from kv_cache_rmsnorm_amd.chain import DecodeChain
     from test_gpu_configs import check_chain
     vec = vec_of(dt)
@@ -343,6 +343,9 @@ def test_chain_launch_forms(kcr, dt):
     # key/value heads over two workgroups (LPU lanes per head, 256 lanes each)
     kv = 16 if vec == 8 else 8
     forms.append((64, 256, 3, 2, kv, kv, 256))
+    # the deep form at one vector per lane runs pairs of layers, the last
+    # n % 4 layers one at a time: every remainder, with and without pairs
+    forms += [(100, 200, n, 2, 4, 2, 64) for n in (1, 2, 3, 4, 6, 7, 9)]
     for i, (hv, iv, layers, batch, hq, hkv, dh) in enumerate(forms):
         hidden, inter = hv * vec, iv * vec
         say(f"chain dt={DT_ID[dt]} hidden={hidden} inter={inter} layers={layers} batch={batch} heads={hq}/{hkv}x{dh}")
