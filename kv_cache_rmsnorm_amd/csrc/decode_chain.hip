@@ -18,8 +18,9 @@
 //    sum of every op of every layer on one workgroup per token.
 //  * Workgroups never wait for one another, and only the residual
 //    workgroups use barriers: one per layer, for the sums of squares of the
-//    layer's two rows across their 4 waves (the second add needs only the
-//    first add's h, not its norm, so both adds come first).
+//    layer's two rows across their 4 waves (no norm needs another's result,
+//    only the adds chain, so the adds come first), or one per pair of layers
+//    in the deep form at one vector per lane.
 //  * Each role's layer loop is software-pipelined: the inputs of the next
 //    PD (residual) or PDR (RoPE) layers are loaded before the current layer
 //    computes, in a ring of register sets; a scheduling barrier between
@@ -130,7 +131,8 @@ __global__ __launch_bounds__(kFlowThreads) void decode_chain_kernel(const ChainA
     constexpr int kVec = T::kVec;
     constexpr int kWaves = kFlowThreads / 64;
     // layers in flight: the residual's inputs take 16 VGPRs per layer and
-    // vector per lane, so PD * HPL stays at 4 (deep) or 2
+    // vector per lane, so PD is 4 (deep) or 2 (lean) divided by the vectors
+    // per lane, and at least 1
     constexpr int PD = (DEEP ? 4 : 2) / HPL > 1 ? (DEEP ? 4 : 2) / HPL : 1;
     constexpr int PDR = DEEP ? 4 : 2;
     __shared__ float4 part[2][kWaves];  // per wave: sums of squares of up to four rows
