@@ -145,6 +145,7 @@ __global__ __launch_bounds__(kFlowThreads) void decode_chain_kernel(const ChainA
         // ------------------------------------------------------ residual
         const int64_t hrow = bid * a.hidden;
         const int hv = a.hidden / kVec;
+        const float inv_h = inv_width(a.hidden);
         S* const h = static_cast<S*>(a.h) + hrow;
         bool own[HPL], won[HPL];
         int64_t ec[HPL];  // in-bounds element offset for every lane
@@ -205,9 +206,10 @@ __global__ __launch_bounds__(kFlowThreads) void decode_chain_kernel(const ChainA
                     }
                 }
             }
-            const float w0 = wave_sum(ss[0]), w1 = wave_sum(ss[1]);
+            // each wave's two sums, whole in lane 63
+            const float w0 = wave_total_lane63(ss[0]), w1 = wave_total_lane63(ss[1]);
             const int slot = l & 1;
-            if (lane == 0) part[slot][wave] = make_float4(w0, w1, 0.0f, 0.0f);
+            if (lane == 63) part[slot][wave] = make_float4(w0, w1, 0.0f, 0.0f);
             __syncthreads();
             float t0 = 0.0f, t1 = 0.0f;
 #pragma unroll
@@ -216,8 +218,8 @@ __global__ __launch_bounds__(kFlowThreads) void decode_chain_kernel(const ChainA
                 t0 += v.x;
                 t1 += v.y;
             }
-            const float rs0 = __builtin_amdgcn_rsqf(t0 / (float)a.hidden + a.eps);
-            const float rs1 = __builtin_amdgcn_rsqf(t1 / (float)a.hidden + a.eps);
+            const float rs0 = __builtin_amdgcn_rsqf(t0 * inv_h + a.eps);
+            const float rs1 = __builtin_amdgcn_rsqf(t1 * inv_h + a.eps);
 #pragma unroll
             for (int nn = 0; nn < 2; ++nn) {
 #pragma unroll
@@ -245,7 +247,10 @@ __global__ __launch_bounds__(kFlowThreads) void decode_chain_kernel(const ChainA
             static_assert(PD == 4, "two pairs of layers in flight");
             auto pair = [&](auto base_c, int l0, int slot) {
                 constexpr int base = decltype(base_c)::value;
-                u32x4 xr[2][2];  // [layer][norm]: the rounded sums, packed
+                // [layer][norm]: the rounded sums, unpacked (kept rather than
+                // unpacked again for the norms: the residual chain is bound by
+                // instruction issue)
+                float xs[2][2][kVec];
                 float ss[4];
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
@@ -258,8 +263,9 @@ __global__ __launch_bounds__(kFlowThreads) void decode_chain_kernel(const ChainA
                             unpack<T>(nn == 0 ? s[base + j].dA[0] : s[base + j].dM[0], df);
 #pragma unroll
                             for (int e = 0; e < kVec; ++e) hf[0][e] += df[e];
-                            xr[j][nn] = pack<T>(hf[0]);
-                            unpack<T>(xr[j][nn], hf[0]);
+                            unpack<T>(pack<T>(hf[0]), hf[0]);
+#pragma unroll
+                            for (int e = 0; e < kVec; ++e) xs[j][nn][e] = hf[0][e];
                             float sk = 0.0f;
 #pragma unroll
                             for (int e = 0; e < kVec; ++e) sk = __builtin_fmaf(hf[0][e], hf[0][e], sk);
@@ -267,8 +273,9 @@ __global__ __launch_bounds__(kFlowThreads) void decode_chain_kernel(const ChainA
                         }
                     }
                 }
-                const float4 w4 = make_float4(wave_sum(ss[0]), wave_sum(ss[1]), wave_sum(ss[2]), wave_sum(ss[3]));
-                if (lane == 0) part[slot][wave] = w4;
+                const float4 w4 = make_float4(wave_total_lane63(ss[0]), wave_total_lane63(ss[1]),
+                                              wave_total_lane63(ss[2]), wave_total_lane63(ss[3]));
+                if (lane == 63) part[slot][wave] = w4;
                 __syncthreads();
                 float t[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -287,12 +294,11 @@ __global__ __launch_bounds__(kFlowThreads) void decode_chain_kernel(const ChainA
                         S* const y_mlp = static_cast<S*>(L.y_mlp) + hrow;
 #pragma unroll
                         for (int nn = 0; nn < 2; ++nn) {
-                            const float rs = __builtin_amdgcn_rsqf(t[2 * j + nn] / (float)a.hidden + a.eps);
-                            float xf[kVec], wf[kVec], yf[kVec];
-                            unpack<T>(xr[j][nn], xf);
+                            const float rs = __builtin_amdgcn_rsqf(t[2 * j + nn] * inv_h + a.eps);
+                            float wf[kVec], yf[kVec];
                             unpack<T>(nn == 0 ? s[base + j].wA[0] : s[base + j].wM[0], wf);
 #pragma unroll
-                            for (int e = 0; e < kVec; ++e) yf[e] = xf[e] * rs * wf[e];
+                            for (int e = 0; e < kVec; ++e) yf[e] = xs[j][nn][e] * rs * wf[e];
                             const u32x4 yv = pack<T>(yf);
                             if (own[0]) st16_nt<T>(nn == 0 ? y_attn : y_mlp, ec[0], yv);
                         }

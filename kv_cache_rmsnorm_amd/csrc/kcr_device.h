@@ -279,20 +279,32 @@ __device__ __forceinline__ float dpp(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over all 64 lanes of a wave; every lane must be active. The result is
-// wave-uniform (the same value, bit for bit, in every lane): four DPP steps
-// leave each 16-lane row's sum in all its lanes, and the four row sums are
-// read out with v_readlane and added in a fixed order.
-__device__ __forceinline__ float wave_sum(float v) {
+// Sum over all 64 lanes of a wave, whole in lane 63 only (the other lanes
+// hold partial sums); every lane must be active. Four DPP steps leave each
+// 16-lane row's sum r0..r3 in all its lanes; then gfx9's row broadcasts add
+// row 0's sum into row 1 and row 2's into row 3 (from lanes 15 and 47), and
+// rows 0 + 1 into row 3 (from lane 31), so lane 63 holds (r3 + r2) + (r1 + r0).
+// For a reduction whose result one lane stores: no lane reads.
+constexpr int kDppRowBcast15 = 0x142;   // lane 15 of each row -> the next row
+constexpr int kDppRowBcast31 = 0x143;   // lane 31 -> rows 2 and 3
+
+__device__ __forceinline__ float wave_total_lane63(float v) {
     v += dpp<kDppQuadXor1>(v);
     v += dpp<kDppQuadXor2>(v);
     v += dpp<kDppRowHalfMirror>(v);
     v += dpp<kDppRowMirror>(v);
-    float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-    float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-    float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-    return (r0 + r1) + (r2 + r3);
+    // rows outside the row mask take the 0 passed as the old value
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRowBcast15, 0xA, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRowBcast31, 0xC, 0xF, false));
+    return v;
+}
+
+// The same sum made wave-uniform (the same value, bit for bit, in every
+// lane): lane 63's total, read out once. Each addition in lane 63 is one of
+// (r0 + r1) + (r2 + r3) with its operands swapped, so the result has the
+// bits of that order.
+__device__ __forceinline__ float wave_sum(float v) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_total_lane63(v)), 63));
 }
 
 // Sum over each aligned group of N consecutive lanes (N a power of two up to
@@ -307,6 +319,13 @@ __device__ __forceinline__ float group_sum(float v) {
     if constexpr (N >= 64) v += __shfl_xor(v, 32);
     return v;
 }
+
+// Every row norm takes its mean square as the sum of squares times the
+// width's reciprocal, 1/d rounded once to fp32 (one rounding more than a
+// division). Computed at a kernel's start, the reciprocal stays off the path
+// from a row's last load to its stores, where a division's dozen dependent
+// instructions would sit.
+__device__ __forceinline__ float inv_width(int32_t d) { return 1.0f / (float)d; }
 
 // Wave index made explicitly uniform, so that row and unit indices derived
 // from it live in scalar registers.

@@ -75,6 +75,7 @@ __global__ __launch_bounds__(C::BLOCK) void row_norm_kernel(const NormArgs a) {
     const int grp = wave / WPR;                    // row group within the workgroup
     const int rl = (wave % WPR) * 64 + lane;       // lane within the row group
     const int64_t d = a.d;
+    const float inv_d = inv_width(a.d);
     // One pass: workgroup b owns rows [b * GROUPS * RPG, (b + 1) * GROUPS * RPG).
     // (A loop over several row blocks per workgroup measured 2-5% slower: the
     // compiler then waits for the weight before the first row load.)
@@ -192,11 +193,12 @@ __global__ __launch_bounds__(C::BLOCK) void row_norm_kernel(const NormArgs a) {
                 for (int e = 0; e < kVec; ++e) ss[r] += xf[e] * xf[e];
             }
         }
-        ss[r] = wave_sum(ss[r]);
+        // (with several waves per row only lane 63 publishes the wave's sum)
+        ss[r] = WPR > 1 ? wave_total_lane63(ss[r]) : wave_sum(ss[r]);
     }
     if constexpr (WPR > 1) {
         __shared__ float part[RPG][GROUPS][WPR];
-        if (lane == 0) {
+        if (lane == 63) {
 #pragma unroll
             for (int r = 0; r < RPG; ++r) part[r][grp][wave % WPR] = ss[r];
         }
@@ -211,7 +213,7 @@ __global__ __launch_bounds__(C::BLOCK) void row_norm_kernel(const NormArgs a) {
 #pragma unroll
     for (int r = 0; r < RPG; ++r) {
         if (!live[r]) continue;
-        const float rs = __builtin_amdgcn_rsqf(ss[r] / (float)a.d + a.eps);
+        const float rs = __builtin_amdgcn_rsqf(ss[r] * inv_d + a.eps);
         void* yrow = row_ptr<T>(a.y, row0 + r, a.y_stride);
         const bool vy = VEC || vec_ok(yrow);
 #pragma unroll
@@ -276,6 +278,7 @@ __global__ __launch_bounds__(64) void row_norm_wave_kernel(const NormArgs a) {
     constexpr int kVec = T::kVec;
     const int lane = threadIdx.x;
     const int64_t row = blockIdx.x;
+    const float inv_d = inv_width(a.d);
     const S* xr = static_cast<const S*>(a.x) + row * a.x_stride;
     const S* dr = ADD ? static_cast<const S*>(a.delta) + row * a.delta_stride : nullptr;
     u32x4 x[VPT], dv[VPT], w[VPT];
@@ -325,7 +328,7 @@ __global__ __launch_bounds__(64) void row_norm_wave_kernel(const NormArgs a) {
         for (int e = 0; e < kVec; ++e) ss += xf[e] * xf[e];
     }
     ss = wave_sum(ss);
-    const float rs = __builtin_amdgcn_rsqf(ss / (float)a.d + a.eps);
+    const float rs = __builtin_amdgcn_rsqf(ss * inv_d + a.eps);
     S* const yr = static_cast<S*>(a.y) + row * a.y_stride;
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
@@ -402,6 +405,7 @@ __global__ __launch_bounds__(kWideThreads) void wide_norm_kernel(const NormArgs 
     constexpr bool kNtLoad = STAGED;  // a row read twice keeps its lines in L2
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int64_t d = a.d;
+    const float inv_d = inv_width(a.d);
     const int nvec = (a.d + kVec - 1) / kVec;
     const bool vw = vec_ok(a.w);
     int it = 0;
@@ -452,13 +456,13 @@ __global__ __launch_bounds__(kWideThreads) void wide_norm_kernel(const NormArgs 
                 for (int e = 0; e < kVec; ++e) ss += xf[e] * xf[e];
             }
         }
-        ss = wave_sum(ss);
-        if (lane == 0) part[it & 1][wave] = ss;
+        ss = wave_total_lane63(ss);
+        if (lane == 63) part[it & 1][wave] = ss;
         __syncthreads();
         float tot = 0.0f;
 #pragma unroll
         for (int i = 0; i < kWideWaves; ++i) tot += part[it & 1][i];
-        const float r = __builtin_amdgcn_rsqf(tot / (float)a.d + a.eps);
+        const float r = __builtin_amdgcn_rsqf(tot * inv_d + a.eps);
 
         const void* src = ADD ? static_cast<const void*>(orow) : xrow;
         void* yrow = row_ptr<T>(a.y, row, a.y_stride);
@@ -500,6 +504,7 @@ __global__ __launch_bounds__(kWideThreads) void wide_tier_kernel(const TierArgs 
     constexpr int kVec = T::kVec, W = kWideThreads;
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int64_t d = a.d;
+    const float inv_d = inv_width(a.d);
     const int nvec = (int)((d + kVec - 1) / kVec);
     int it = 0;
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x, ++it) {
@@ -545,13 +550,13 @@ __global__ __launch_bounds__(kWideThreads) void wide_tier_kernel(const TierArgs 
                 if (v < lds_vecs) stage[v] = xv[u];
             }
         }
-        ss = wave_sum(ss);
-        if (lane == 0) part[it & 1][wave] = ss;
+        ss = wave_total_lane63(ss);
+        if (lane == 63) part[it & 1][wave] = ss;
         __syncthreads();
         float tot = 0.0f;
 #pragma unroll
         for (int i = 0; i < kWideWaves; ++i) tot += part[it & 1][i];
-        const float r = __builtin_amdgcn_rsqf(tot / (float)a.d + a.eps);
+        const float r = __builtin_amdgcn_rsqf(tot * inv_d + a.eps);
 
         // Loop 2: the same lane owns the same vectors as in loop 1.
         void* yrow = row_ptr<T>(a.y, row, a.y_stride);

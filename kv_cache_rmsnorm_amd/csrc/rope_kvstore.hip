@@ -169,7 +169,7 @@ __global__ __launch_bounds__(C::BLOCK) void rope_kvstore_kernel(const RopeArgs a
 #pragma unroll
                 for (int e = 0; e < kVec; ++e) ss += f1[e] * f1[e] + f2[e] * f2[e];
                 ss = group_sum<LPU>(lane_on ? ss : 0.0f);
-                const float r = __builtin_amdgcn_rsqf(ss / (float)a.dh + a.eps);
+                const float r = __builtin_amdgcn_rsqf(ss * inv_width(a.dh) + a.eps);
                 const bool isk = kind[h] == 1;
 #pragma unroll
                 for (int e = 0; e < kVec; ++e) {
@@ -320,7 +320,7 @@ __global__ __launch_bounds__(1024) void rope_token_kernel(const RopeArgs a) {
 #pragma unroll
         for (int e = 0; e < kVec; ++e) ss += f1[e] * f1[e] + f2[e] * f2[e];
         ss = group_sum<LPU>(ss);
-        const float rs = __builtin_amdgcn_rsqf(ss / (float)dh + a.eps);
+        const float rs = __builtin_amdgcn_rsqf(ss * inv_width(dh) + a.eps);
 #pragma unroll
         for (int e = 0; e < kVec; ++e) {
             f1[e] = f1[e] * rs * w1[e];
