@@ -252,25 +252,27 @@ __global__ __launch_bounds__(kFlowThreads) void decode_chain_kernel(const ChainA
                 // instruction issue)
                 float xs[2][2][kVec];
                 float ss[4];
+                // Every wave does the adds, also one that owns no vector of the
+                // row (its lanes sit on vector 0 and add zero to the sums): a
+                // branch around them cost the other waves register moves at
+                // the merge, about a tenth of the loop's instructions.
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     ss[2 * j] = 0.0f;
                     ss[2 * j + 1] = 0.0f;
-                    if (won[0]) {
 #pragma unroll
-                        for (int nn = 0; nn < 2; ++nn) {
-                            float df[kVec];
-                            unpack<T>(nn == 0 ? s[base + j].dA[0] : s[base + j].dM[0], df);
+                    for (int nn = 0; nn < 2; ++nn) {
+                        float df[kVec];
+                        unpack<T>(nn == 0 ? s[base + j].dA[0] : s[base + j].dM[0], df);
 #pragma unroll
-                            for (int e = 0; e < kVec; ++e) hf[0][e] += df[e];
-                            unpack<T>(pack<T>(hf[0]), hf[0]);
+                        for (int e = 0; e < kVec; ++e) hf[0][e] += df[e];
+                        unpack<T>(pack<T>(hf[0]), hf[0]);
 #pragma unroll
-                            for (int e = 0; e < kVec; ++e) xs[j][nn][e] = hf[0][e];
-                            float sk = 0.0f;
+                        for (int e = 0; e < kVec; ++e) xs[j][nn][e] = hf[0][e];
+                        float sk = 0.0f;
 #pragma unroll
-                            for (int e = 0; e < kVec; ++e) sk = __builtin_fmaf(hf[0][e], hf[0][e], sk);
-                            ss[2 * j + nn] = own[0] ? sk : 0.0f;
-                        }
+                        for (int e = 0; e < kVec; ++e) sk = __builtin_fmaf(hf[0][e], hf[0][e], sk);
+                        ss[2 * j + nn] = own[0] ? sk : 0.0f;
                     }
                 }
                 const float4 w4 = make_float4(wave_total_lane63(ss[0]), wave_total_lane63(ss[1]),
