@@ -80,7 +80,8 @@ enum kcr_status {
  * kcr_rmsnorm -- row-wise RMSNorm with fp32 accumulation.
  *
  *   for each row r < rows:
- *     ms   = sum_{j<d} x[r,j]^2 / d          (fp32 sum of the d real columns)
+ *     ms   = sum_{j<d} x[r,j]^2 / d          (fp32 sum of the d real columns,
+ *                                             times 1/d rounded once to fp32)
  *     y[r,j] = x[r,j] * (ms + eps)^(-1/2) * w[j]
  *
  * Defined in the koas-w.github.io 2026-03-31 post, section 3 ("Triton

@@ -16,8 +16,9 @@
 //    LDS exchange of the wave partial sums when WPR > 1. A row group may
 //    take RPG rows, all read before any is written: longer read-only then
 //    write-only phases per wave stream HBM better on MI355X.
-//  * The sum of squares is reduced in-wave with DPP and v_readlane (no LDS,
-//    no barrier when WPR = 1).
+//  * The sum of squares is reduced in-wave with DPP, ending in lane 63 (no
+//    LDS, no barrier when WPR = 1), and the mean square is that sum times
+//    the width's reciprocal.
 //  * Ragged widths (1536, 2176, primes) need no power-of-two padding: only
 //    the vector that straddles the end of a row is read element by element.
 //    Vectors need only dword alignment, so rows of e.g. 8196 bf16 still move
