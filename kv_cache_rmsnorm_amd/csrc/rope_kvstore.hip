@@ -288,9 +288,13 @@ __global__ __launch_bounds__(1024) void rope_token_kernel(const RopeArgs a) {
     const int64_t p = a.pos[t], slot = a.slots[t];
     const int c0 = c * kVec;
     const u32x4 x1 = ld16_nt<T>(src, c0), x2 = ld16_nt<T>(src, half + c0);
-    // Compiler-only barrier: the head loads stay ahead of everything that
-    // waits for the position.
+    // The head loads stay ahead of everything that waits for the position:
+    // no memory access moves across (the compiler barrier) and no
+    // instruction either (the scheduling barrier; without it the scheduler
+    // hoisted the position checks above the head loads, which then waited
+    // for the position's scalar load).
     asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
     float w1[kVec], w2[kVec];
     if constexpr (QKN) {
         const void* wp = kind == 1 ? a.k_w : a.q_w;
