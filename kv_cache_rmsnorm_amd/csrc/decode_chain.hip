@@ -243,7 +243,10 @@ __global__ __launch_bounds__(kFlowThreads) void decode_chain_kernel(const ChainA
             // pair earlier. One pair: layers l0 and l0 + 1 from sets base and
             // base + 1. The last n % 4 layers go one at a time, as below (a
             // pair with a run-time layer count made the compiler copy the
-            // whole argument block to scratch memory).
+            // whole argument block to scratch memory: LLVM folds away its
+            // private copy of a by-value kernel argument only while that
+            // copy has at most a few hundred users, and the larger unrolled
+            // forms pass that count).
             static_assert(PD == 4, "two pairs of layers in flight");
             auto pair = [&](auto base_c, int l0, int slot) {
                 constexpr int base = decltype(base_c)::value;
