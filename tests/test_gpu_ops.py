@@ -226,6 +226,43 @@ def test_rmsnorm_outlier_rows_fp32(kcr):
     assert_close(y[rows], ref[rows], torch.float32, "outlier rows")
 
 
+# fp32 accumulation (the pages' norm computes in fp32) bounds the rows a norm can
+# take: once a row's sum of squares overflows fp32 (|x| around 2e19 and
+# up, which bf16 and fp32 hold), the sum is inf, the scale 1/sqrt(inf) = 0
+# and y is a signed zero, where the fp64 oracle stays finite. The other rows
+# of the same call are unaffected, and the add variant's residual stays
+# bit-exact. No other test feeds such rows.
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32], ids=DT_ID.get)
+@pytest.mark.parametrize("rows,d", [(8, 1536), (300, 2176), (4, 40000)])
+@pytest.mark.parametrize("add", [False, True], ids=["plain", "add"])
+def test_norm_fp32_sum_overflow(kcr, dt, rows, d, add):
+    say(f"norm overflow dt={dt} rows={rows} d={d} add={add}")
+    g = torch.Generator().manual_seed(rows + d)
+    x = torch.randn((rows, d), generator=g).to(dt)
+    delta = torch.randn((rows, d), generator=g).to(dt)
+    w = (torch.rand(d, generator=g) + 0.5).to(dt)
+    huge = [1, rows - 1]
+    sign = torch.where(torch.rand((2, d), generator=g) < 0.5, -1.0, 1.0)
+    x[huge] = (3e19 * sign).to(dt)
+    eps = 1e-6
+    xd = dev(x)
+    if add:
+        delta[huge] = 0
+        y = kcr.add_rmsnorm(xd, dev(delta), dev(w), eps).cpu()
+        x_ref, ref = oracle.add_rmsnorm(np_bits(x), np_bits(delta), np_bits(w), float(np.float32(eps)))
+        assert np.array_equal(np_bits(xd.cpu()).view(np.uint8), x_ref.view(np.uint8)), "residual"
+    else:
+        y = kcr.rmsnorm(xd, dev(w), eps).cpu()
+        ref = oracle.rmsnorm(np_bits(x), np_bits(w), float(np.float32(eps)))
+    yd = y.double().numpy()
+    assert np.all(np.isfinite(ref[huge])) and np.all(ref[huge] != 0), "the oracle stays finite"
+    assert np.all(yd[huge] == 0), "rows whose fp32 sum of squares overflows give zeros"
+    want_sign = np.signbit(x[huge].double().numpy()) ^ np.signbit(w.double().numpy())[None, :]
+    assert np.array_equal(np.signbit(yd[huge]), want_sign), "the zeros carry the sign of x * w"
+    keep = [r for r in range(rows) if r not in huge]
+    assert_close(yd[keep], ref[keep], dt, "the other rows")
+
+
 def test_rmsnorm_empty_and_stream(kcr):
     x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
     w = torch.ones(64, dtype=torch.bfloat16, device="cuda")
