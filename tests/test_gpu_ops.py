@@ -263,6 +263,32 @@ def test_norm_fp32_sum_overflow(kcr, dt, rows, d, add):
     assert_close(yd[keep], ref[keep], dt, "the other rows")
 
 
+# The method's degenerate rows, among ordinary ones, against the oracle: a
+# zero row (y exactly zero), a constant row (y = c / sqrt(c^2 + eps) * w), a
+# row with one nonzero element, and a row so small that its squares
+# underflow in fp32 (the sum is 0, so y = x * eps^(-1/2) * w, which is also
+# the fp64 result to within the tolerance since eps dominates).
+@pytest.mark.parametrize("dt", DTS, ids=DT_ID.get)
+@pytest.mark.parametrize("rows,d", [(8, 1536), (300, 2176), (4, 40000)])
+def test_norm_degenerate_rows(kcr, dt, rows, d):
+    say(f"norm degenerate rows dt={dt} rows={rows} d={d}")
+    g = torch.Generator().manual_seed(7 * rows + d)
+    x = torch.randn((rows, d), generator=g).to(dt)
+    w = (torch.rand(d, generator=g) + 0.5).to(dt)
+    tiny = 1e-4 if dt == torch.float16 else 1e-30
+    x[0] = 0
+    x[1] = 0.75
+    x[2] = 0
+    x[2, d // 3] = -2.5
+    x[rows - 1] = (tiny * torch.randn(d, generator=g)).to(dt)
+    eps = 1e-6
+    y = kcr.rmsnorm(dev(x), dev(w), eps).cpu().double().numpy()
+    ref = oracle.rmsnorm(np_bits(x), np_bits(w), float(np.float32(eps)))
+    assert np.all(y[0] == 0), "a zero row gives zeros"
+    assert np.all(ref[0] == 0)
+    assert_close(y, ref, dt, "degenerate rows")
+
+
 def test_rmsnorm_empty_and_stream(kcr):
     x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
     w = torch.ones(64, dtype=torch.bfloat16, device="cuda")
