@@ -302,6 +302,23 @@ def test_decode_chain_b1_dtypes_and_shapes(kcr, dt):
     check_chain(wl, chain)
 
 
+@pytest.mark.parametrize("batch", [1, 3, 70])
+def test_decode_chain_max_layers(kcr, batch):
+    """The one-launch chain at the most layers its argument block holds (32):
+    at batch 1 (b1 entry point), 3 (four-deep rings, pairs of layers per
+    exchange) and 70 (two-deep rings, one exchange per layer); 32 layers are
+    whole groups of either ring. Small shapes, bf16, every output against the
+    oracle."""
+    from kv_cache_rmsnorm_amd.chain import DecodeChain
+    say(f"decode chain, 32 layers, batch {batch}")
+    wl = workloads.decode_chain(layers=32, batch=batch, ctx=40, seed=90 + batch, hidden=256, inter=512,
+                                hq=4, hkv=2, dh=64, block_size=16)
+    chain = DecodeChain(wl, "cuda", sentinel_cache=True)
+    chain.step_b1() if batch == 1 else chain.step_one_launch()
+    torch.cuda.synchronize()
+    check_chain(wl, chain)
+
+
 def bits_to_tensor(bits: np.ndarray, dt) -> torch.Tensor:
     """Inverse of np_bits: storage-convention numpy array -> CPU tensor."""
     if dt == torch.bfloat16:
