@@ -335,9 +335,9 @@ int kcr_paged_kv_gather(const void* kv_cache, int64_t num_blocks, int block_size
  *
  * Each op is the one defined above (the koas-w.github.io 2026-03-31 post,
  * sections 1, 2 and 4) and its results are those of the separate calls made
- * in this order (the residual and the cache's V rows bit for bit; the other
- * outputs up to the order in which a row's squares are summed, within the
- * same tolerances): the launch-overhead elimination (one launch instead of four
+ * in this order (the residual and the cache's V rows bit for bit; the
+ * norms' outputs up to the order in which a row's squares are summed, within
+ * the same tolerances): the launch-overhead elimination (one launch instead of four
  * per layer) that m.lsln.cn/news/61269 section 4 seeks with CUDA Graph. Only
  * the residual passes from op to op, so inside the launch one workgroup runs
  * the token's residual chain (h in registers) while other workgroups run
