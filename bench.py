@@ -12,11 +12,13 @@ Prints ONE JSON line:
   value        algorithmic bytes of a step / step time (GB/s), whole job
   ms_per_step  decode-step fused-op latency (graph replay)
   roofline     the step's dominant kernel: the chain op with the largest
-               summed kernel time per step (durations from events stamped
-               at each kernel's start and end, hipExtLaunchKernel, in whole
-               steps that run back to back behind graph replays); its
-               algorithmic bytes per launch / its mean duration, with every
-               chain op's share and fraction beside it
+               kernel time per step (its per-launch time inside a captured
+               graph of that op's 28 launches on the chain's buffers, from
+               HIP events on the launch stream around graph replays, times
+               its launches per step); its algorithmic bytes per launch /
+               that time, the counter-measured traffic, a graph of plain
+               copies of the same size, and every chain op's share and
+               fraction beside it
   cpu_baseline the CPU fp64 oracle on a bounded sample of the same workload;
                per_config: the oracle at each parity-shape config, with
                every oracle thread and with one
