@@ -4,7 +4,10 @@ tiers (small calls, measured per-width shapes, unaligned rows, the
 two-pass wide kernel), the strided views and the padding / permuted-block
 cache layouts are crossed in combinations the hand-picked tests do not
 list. Each case prints its parameters before it runs; the comparison rules
-are the same as everywhere else (helpers.py)."""
+are the same as everywhere else (helpers.py). KCR_FUZZ_SCALE=k runs k times
+as many cases of each kind (the first ones are the default cases)."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -16,6 +19,7 @@ from helpers import assert_close, check_rope, assert_rope_close, np_bits
 pytestmark = pytest.mark.gpu
 
 DTS = [torch.bfloat16, torch.float16, torch.float32]
+SCALE = max(1, int(os.environ.get("KCR_FUZZ_SCALE", "1")))
 
 
 @pytest.fixture(scope="module")
@@ -81,7 +85,7 @@ def norm_case(case: int):
     return tier, dt, d, rows, add, d + x_pad, d + y_pad, x_off, y_off, rng
 
 
-@pytest.mark.parametrize("case", range(72))
+@pytest.mark.parametrize("case", range(72 * SCALE))
 def test_fuzz_norms(kcr, case):
     tier, dt, d, rows, add, x_stride, y_stride, x_off, y_off, rng = norm_case(case)
     say(f"norm case {case} ({tier}): dt={dt} d={d} rows={rows} add={add} strides x={x_stride} "
@@ -105,7 +109,7 @@ def test_fuzz_norms(kcr, case):
     assert_close(y.cpu().double().numpy(), y_ref, dt, f"norm case {case}")
 
 
-@pytest.mark.parametrize("case", range(48))
+@pytest.mark.parametrize("case", range(48 * SCALE))
 def test_fuzz_norm_wave_rows(kcr, case):
     """Small calls whose rows are exactly 64 * VPT 16-byte vectors (VPT 1..8)
     take the one-wave-per-row kernel: every VPT in every dtype, plain and
@@ -141,7 +145,7 @@ def test_fuzz_norm_wave_rows(kcr, case):
     assert_close(y.cpu().double().numpy(), y_ref, dt, f"wave-row case {case}")
 
 
-@pytest.mark.parametrize("case", range(36))
+@pytest.mark.parametrize("case", range(36 * SCALE))
 def test_fuzz_gated(kcr, case):
     rng = np.random.default_rng(3000 + case)
     dt = DTS[case % 3]
@@ -164,7 +168,7 @@ def test_fuzz_gated(kcr, case):
     assert_close(out.cpu().double().numpy(), ref, dt, f"gated case {case}")
 
 
-@pytest.mark.parametrize("case", range(36))
+@pytest.mark.parametrize("case", range(36 * SCALE))
 def test_fuzz_rope(kcr, case):
     rng = np.random.default_rng(5000 + case)
     dt = DTS[case % 3]
@@ -213,7 +217,7 @@ def test_fuzz_rope(kcr, case):
     assert_rope_close(kg.view(dt).double().numpy(), k_rot[tok], dt, f"rope case {case}: K rows")
 
 
-@pytest.mark.parametrize("case", range(16))
+@pytest.mark.parametrize("case", range(16 * SCALE))
 def test_fuzz_gather(kcr, case):
     rng = np.random.default_rng(8000 + case)
     dt = DTS[case % 3]
@@ -242,7 +246,7 @@ def test_fuzz_gather(kcr, case):
             assert not got[L:].any(), f"seq {b}: rows past the length were written"
 
 
-@pytest.mark.parametrize("case", range(12))
+@pytest.mark.parametrize("case", range(12 * SCALE))
 def test_fuzz_chain_one_launch(kcr, case):
     """The one-launch decode chain (kcr_decode_chain_batch) at random
     batches, layer counts, widths, head layouts and block sizes in every
