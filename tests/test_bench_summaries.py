@@ -165,3 +165,29 @@ def test_bench_refuses_several_gpus():
         assert r.returncode == 2, r.stderr
         assert "one GPU only" in r.stderr
         assert r.stdout == ""
+
+
+def test_chain_roofline_picks_the_op_with_most_time(monkeypatch):
+    """The roofline object names the chain op with the largest kernel time
+    per step (per-launch time in a graph x launches per step), whichever op
+    moves the most bytes, and its rate is its bytes per launch over that
+    time."""
+    import types
+    import torch
+    chain = types.SimpleNamespace(h=torch.zeros((256, 1536), dtype=torch.bfloat16), hidden=1536, inter=8960,
+                                  hq=12, hkv=2, dh=128, positions=torch.full((256,), 4096, dtype=torch.int64))
+    monkeypatch.setattr(bench, "counter_traffic", lambda op: (None, None))
+    per_op = dict(add_rmsnorm=[4e-3] * 56 * 2, rope_kvstore=[4e-3] * 28 * 2, swiglu=[4e-3] * 28 * 2)
+    copy_us = dict(add_rmsnorm=2.3, rope_kvstore=2.2, swiglu=4.0)
+    nbytes = bench.chain_op_bytes(chain)
+    # add_rmsnorm: 56 x 2.7 us = 151 us per step; SwiGLU moves 4x the bytes but 28 x 3.8 = 106 us
+    graph = dict(add_rmsnorm=2.7, add_rmsnorm_2=2.7, rope_kvstore=2.6, swiglu=3.8)
+    roof = bench.chain_roofline(chain, graph, per_op, 2, copy_us)
+    assert roof["kernel"] == "add_rmsnorm"
+    assert roof["launches_per_step"] == 56
+    assert roof["achieved"] == pytest.approx(nbytes["add_rmsnorm"] / 2.7e-6 / 1e9, rel=1e-3)
+    assert roof["frac"] == pytest.approx(roof["achieved"] / 8000.0, rel=1e-3)
+    assert sum(o["share_of_kernel_time"] for o in roof["chain_ops"].values()) == pytest.approx(1.0, abs=1e-3)
+    # a slower SwiGLU takes the object over
+    graph["swiglu"] = 6.0
+    assert bench.chain_roofline(chain, graph, per_op, 2, copy_us)["kernel"] == "swiglu"
